@@ -1,0 +1,236 @@
+/*
+ * rpa.h — C ABI of librpa.so: ragged paged attention on MI355X (gfx950).
+ *
+ * Four operations, each an asynchronous launch sequence on the caller's HIP
+ * stream:
+ *   rpa_forward        GQA attention over a packed ragged batch whose K/V live
+ *                      in a shared pool of fixed-size pages
+ *                      [RPA v2 page: ragged_paged_attention, ref_ragged_paged_attention];
+ *   mla_rpa_forward    the MLA latent variant, scatter of the new tokens then
+ *                      attention [MLA v1 page: mla_ragged_paged_attention,
+ *                      update_kv_cache, ref_mla_ragged_paged_attention];
+ *   kv_cache_update    the scatter of new tokens into page/row slots alone
+ *                      [MLA v1 page: update_kv_cache; Sparse page:
+ *                      prefill_write_and_attend self-write];
+ *   sparse_mla_forward attention of each query over its own top-k set of page
+ *                      units of the latent pool [Sparse page:
+ *                      sparse_mla_attention, _sparse_mla_kernel_chunked_hminor].
+ *
+ * Pages are cited by short name: "RPA v2 page" (tpu-inference
+ * ragged_paged_attention v2 kernel), "MLA v1 page" (tpu-inference MLA ragged
+ * paged attention v1 kernel), "Sparse page" (sglang-jax sparse MLA prefill
+ * kernel).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *    never keeps a pointer past the call and never allocates on these paths.
+ *    Scratch space is the caller's `workspace` (size from *_workspace_size).
+ *  - Layouts are dense row-major in the index order written; element types
+ *    are given by rpa_dtype (bf16 = upper half of binary32; fp8 = OCP E4M3FN).
+ *  - Calls are asynchronous on `stream` (NULL = the default stream). Unless
+ *    rpa_opts.debug_validate is set, no call synchronises with the host.
+ *  - On any error the call returns a non-zero rpa_status, launches nothing,
+ *    and rpa_last_error() describes the first problem found (thread-local).
+ *  - Outputs are written in the query dtype for rpa_forward/mla_rpa_forward
+ *    and in fp32 for sparse_mla_forward; results are deterministic (a fixed
+ *    reduction order that does not depend on scheduling).
+ */
+#ifndef RPA_H_
+#define RPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as hipStream_t (HIP declares `typedef struct ihipStream_t* hipStream_t`). */
+struct ihipStream_t;
+typedef struct ihipStream_t* rpa_stream_t;
+
+typedef enum {
+  RPA_OK = 0,
+  RPA_E_INVALID = 1,     /* a value is out of its allowed range */
+  RPA_E_SHAPE = 2,       /* sizes disagree with each other */
+  RPA_E_DTYPE = 3,       /* element type not accepted for this argument */
+  RPA_E_UNSUPPORTED = 4, /* valid input this build does not implement */
+  RPA_E_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  RPA_E_HIP = 6          /* the HIP runtime reported an error */
+} rpa_status;
+
+typedef enum { RPA_F32 = 0, RPA_BF16 = 1, RPA_FP8_E4M3 = 2 } rpa_dtype;
+
+typedef enum {
+  RPA_LAYOUT_COMBINED_GQA = 0, /* [P, ps, 2*Hkv, D]: K of kv head h at 2h, V at 2h+1 */
+  RPA_LAYOUT_MLA_SPLIT = 1,    /* kv_c [P, ps, stride_a] and k_pe [P, ps, stride_b] */
+  RPA_LAYOUT_MLA_FUSED = 2     /* one pool [P, ps, stride_a] holding [kv_c || k_pe || 0] */
+} rpa_cache_layout;
+
+/*
+ * Ragged batch description [RPA v2 page: ragged_paged_attention arguments;
+ * MLA v1 page: kv_lens / page_indices / cu_q_lens]. All four arrays are
+ * device int32. Only the first *num_seqs sequences are read.
+ *   cu_q_lens    [max_num_seqs + 1]  packed query offsets; sequence i owns query
+ *                                    tokens [cu_q_lens[i], cu_q_lens[i+1]).
+ *   kv_lens      [max_num_seqs]      keys of sequence i, INCLUDING this step's
+ *                                    new tokens; query r of sequence i sits at
+ *                                    position kv_lens[i] - q_len_i + r.
+ *   page_indices [max_num_seqs * pages_per_seq]  logical page lp of sequence i
+ *                                    is physical page page_indices[i*pps + lp].
+ *   num_seqs     [1]                 the dynamic sequence count.
+ * max_num_seqs, pages_per_seq and max_num_tokens are host-known capacities
+ * (max_num_tokens = rows of the packed query/output arrays).
+ */
+typedef struct {
+  const int32_t* cu_q_lens;
+  const int32_t* kv_lens;
+  const int32_t* page_indices;
+  const int32_t* num_seqs;
+  int32_t max_num_seqs;
+  int32_t pages_per_seq;
+  int32_t max_num_tokens;
+} rpa_ragged_meta;
+
+/*
+ * Attention options [RPA v2 page: ragged_paged_attention keyword arguments].
+ *   sm_scale       multiplies q.k (default 1.0).
+ *   sliding_window 0 = none; W > 0 masks keys at or before position - W.
+ *   soft_cap       0 = none; otherwise scores become cap * tanh(score / cap)
+ *                  after scaling and before masking.
+ *   k_scale/v_scale multiply stored K and V (1.0 = none); used for fp8 pools.
+ *   debug_validate 1 = copy the metadata to the host (synchronising the stream)
+ *                  and run the value checks the pages run at runtime
+ *                  (0 < q_len <= kv_len, page count <= pages_per_seq, page ids
+ *                  in [0, P), total tokens <= max_num_tokens,
+ *                  num_seqs <= max_num_seqs) before launching.
+ * Masked keys are excluded from the softmax exactly; on valid input this is
+ * what the pages' finite mask value produces, since every query sees at least
+ * its own position.
+ */
+typedef struct {
+  float sm_scale;
+  int32_t sliding_window;
+  float soft_cap;
+  float k_scale;
+  float v_scale;
+  int32_t debug_validate;
+} rpa_opts;
+
+/* Fills *opts with the defaults above. */
+void rpa_opts_init(rpa_opts* opts);
+
+/* Thread-local description of the last error (empty string after success). */
+const char* rpa_last_error(void);
+
+/*
+ * Workspace bytes rpa_forward needs for these capacities (host-only query;
+ * depends only on capacities, never on device values).
+ */
+size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t page_size);
+
+/*
+ * GQA ragged paged attention [RPA v2 page: ragged_paged_attention].
+ *   q         [max_num_tokens, num_q_heads, head_dim], q_dtype (F32 or BF16)
+ *   kv_pages  [total_num_pages, page_size, 2*num_kv_heads, head_dim], kv_dtype
+ *             (F32, BF16 or FP8_E4M3); combined layout, K at 2h, V at 2h+1.
+ *   out       [max_num_tokens, num_q_heads, head_dim], q_dtype. Rows of tokens
+ *             at or past cu_q_lens[num_seqs] are not written.
+ * Requires num_q_heads % num_kv_heads == 0. q head h reads kv head
+ * h / (num_q_heads / num_kv_heads). The pool is read only at rows below each
+ * sequence's kv_len, so unused pages and stale table entries are never read.
+ * New tokens must already be in the pool (call kv_cache_update first).
+ */
+rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
+                       const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
+                       int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
+                       const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
+                       rpa_stream_t stream);
+
+/*
+ * Scatter new tokens into a paged cache, in place [MLA v1 page: update_kv_cache;
+ * Sparse page: prefill_write_and_attend self-write].
+ *   Page-table mode (slot_loc == NULL, meta required): new token j of
+ *     sequence i (packed row cu_q_lens[i] + j) goes to position
+ *     p = kv_lens[i] - q_len_i + j, i.e. page page_indices[i*pps + p/ps],
+ *     row p % ps.
+ *   Slot-list mode (slot_loc != NULL, device int32 [num_tokens]): token t goes
+ *     to flat row slot_loc[t] of the [P*ps] rows; negative slots are skipped.
+ *   layout COMBINED_GQA: new_a = K [T, heads, dim_a], new_b = V [T, heads, dim_a],
+ *     cache_a [P, ps, 2*heads, dim_a]; cache_b unused (may be NULL).
+ *   layout MLA_SPLIT: new_a = kv_c [T, dim_a], new_b = k_pe [T, dim_b];
+ *     cache_a [P, ps, stride_a], cache_b [P, ps, stride_b]; the columns past
+ *     the new data are written with zeros.
+ *   layout MLA_FUSED: cache_a [P, ps, stride_a] receives [kv_c || k_pe || 0].
+ * The copy is bitwise. Two tokens naming one slot is invalid input (rejected
+ * under debug_validate via opts; otherwise which one lands is unspecified).
+ * num_tokens = rows of new_a/new_b (for page-table mode, tokens at or past
+ * cu_q_lens[num_seqs] are ignored).
+ */
+rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const void* new_b,
+                           void* cache_a, void* cache_b, rpa_dtype dtype, int32_t total_num_pages,
+                           int32_t page_size, int32_t heads, int32_t dim_a, int32_t dim_b,
+                           int32_t stride_a, int32_t stride_b, int32_t num_tokens,
+                           const rpa_ragged_meta* meta, const int32_t* slot_loc,
+                           int32_t debug_validate, rpa_stream_t stream);
+
+/* Workspace bytes mla_rpa_forward needs for these capacities. */
+size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, int32_t lkv_dim,
+                              int32_t page_size);
+
+/*
+ * MLA ragged paged attention [MLA v1 page: mla_ragged_paged_attention].
+ *   ql_nope [max_num_tokens, num_heads, lkv_dim], q_pe [.., num_heads, r_dim] (BF16)
+ *   new_kv_c [max_num_tokens, lkv_dim], new_k_pe [max_num_tokens, r_dim]; when
+ *     both are NULL the caches are used as they are (attention only).
+ *   cache_kv_c [total_num_pages, page_size, kvc_stride] and
+ *   cache_k_pe [total_num_pages, page_size, kpe_stride], updated in place
+ *     (k_pe pad columns written as zeros).
+ *   out [max_num_tokens, num_heads, lkv_dim] (BF16).
+ * Every head attends the one latent per token: K_t = [kv_c_t || k_pe_t],
+ * V_t = kv_c_t. Runs the scatter, then the attention, in stream order.
+ * This build implements lkv_dim = 512, r_dim = 64, bf16.
+ */
+rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* new_kv_c,
+                           const void* new_k_pe, void* cache_kv_c, void* cache_k_pe,
+                           rpa_dtype dtype, int32_t num_heads, int32_t lkv_dim, int32_t r_dim,
+                           int32_t kvc_stride, int32_t kpe_stride, int32_t total_num_pages,
+                           int32_t page_size, const rpa_ragged_meta* meta, const rpa_opts* opts,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           rpa_stream_t stream);
+
+/* Workspace bytes sparse_mla_forward needs. */
+size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t top_k,
+                                 int32_t read_block, int32_t kv_lora_rank);
+
+/*
+ * Sparse MLA-latent attention, paged single-sequence mode [Sparse page:
+ * sparse_mla_attention, _sparse_mla_kernel_chunked_hminor].
+ *   q          [num_queries, num_heads, kv_lora_rank + rope_dim] (BF16)
+ *   kv_cache   [total_num_pages, page_size, cache_dim] (BF16); token (page P,
+ *              offset o) is row P*page_size + o; cache_dim >= kv_lora_rank+rope_dim.
+ *   page_table [ptw]: logical page -> physical page.
+ *   indices    [num_queries, top_k] unit ids (one unit = read_block consecutive
+ *              logical tokens); -1 = padding.
+ *   positions  [num_queries] query positions (causal bound).
+ *   out        [num_queries, num_heads, kv_lora_rank] FP32.
+ * Query s attends the multiset of keys u*RB + r (u = indices[s,k] >= 0, r < RB)
+ * with u*RB + r <= positions[s] and < seq_len; a unit listed twice counts twice;
+ * an empty set gives zeros. sm_scale is required (> 0, finite).
+ * Requires read_block % 16 == 0 and page_size % read_block == 0.
+ * Logical pages at or past ptw are clamped to ptw-1 for the address and masked.
+ */
+rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t* page_table,
+                              const int32_t* indices, const int32_t* positions, int32_t seq_len,
+                              int32_t num_queries, int32_t num_heads, int32_t top_k,
+                              int32_t read_block, int32_t page_size, int32_t total_num_pages,
+                              int32_t cache_dim, int32_t ptw, int32_t kv_lora_rank,
+                              int32_t rope_dim, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, rpa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H_ */

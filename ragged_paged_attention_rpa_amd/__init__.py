@@ -1,1 +1,323 @@
-"""MI355X-native ragged paged attention (placeholder while the binding lands)."""
+"""MI355X-native ragged paged attention: Python binding of librpa.so.
+
+Thin ctypes marshalling over the C ABI declared in ``include/rpa.h``; every
+step of the computation runs in the library's HIP kernels. PyTorch supplies
+device memory and the current stream. The functions carry the C names:
+
+* :func:`rpa_forward`        GQA attention over a packed ragged batch and a paged K/V pool
+* :func:`kv_cache_update`    scatter new tokens into page/row slots
+* :func:`mla_rpa_forward`    MLA latent variant (scatter + attention)
+* :func:`sparse_mla_forward` sparse top-k MLA over a fused latent pool
+
+The library is loaded on first use; if it has not been built
+(``python -m ragged_paged_attention_rpa_amd.build``) the call raises
+:class:`RpaLibraryMissing`. There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["rpa_forward", "kv_cache_update", "mla_rpa_forward", "sparse_mla_forward",
+           "rpa_workspace_size", "mla_rpa_workspace_size", "sparse_mla_workspace_size",
+           "RpaError", "RpaLibraryMissing", "library_path", "load_library",
+           "LAYOUT_COMBINED_GQA", "LAYOUT_MLA_SPLIT", "LAYOUT_MLA_FUSED", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librpa.so")
+
+LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
+EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_workspace_size", "rpa_forward",
+                    "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
+                    "sparse_mla_workspace_size", "sparse_mla_forward")
+
+
+class RpaLibraryMissing(RuntimeError):
+    pass
+
+
+class RpaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"rpa status {status}: {message}")
+        self.status = status
+
+
+class _Meta(ctypes.Structure):
+    _fields_ = [("cu_q_lens", ctypes.c_void_p), ("kv_lens", ctypes.c_void_p),
+                ("page_indices", ctypes.c_void_p), ("num_seqs", ctypes.c_void_p),
+                ("max_num_seqs", ctypes.c_int32), ("pages_per_seq", ctypes.c_int32),
+                ("max_num_tokens", ctypes.c_int32)]
+
+
+class _Opts(ctypes.Structure):
+    _fields_ = [("sm_scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
+                ("soft_cap", ctypes.c_float), ("k_scale", ctypes.c_float),
+                ("v_scale", ctypes.c_float), ("debug_validate", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Loads librpa.so (once) and declares the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RpaLibraryMissing(
+            f"{LIB_PATH} is missing; build it with `python -m ragged_paged_attention_rpa_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    MP, OP = ctypes.POINTER(_Meta), ctypes.POINTER(_Opts)
+    lib.rpa_opts_init.argtypes = [OP]
+    lib.rpa_opts_init.restype = None
+    lib.rpa_last_error.argtypes = []
+    lib.rpa_last_error.restype = ctypes.c_char_p
+    lib.rpa_workspace_size.argtypes = [MP, I32, I32, I32, I32]
+    lib.rpa_workspace_size.restype = SZ
+    lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P, SZ, P]
+    lib.rpa_forward.restype = I32
+    lib.kv_cache_update.argtypes = [I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
+                                    MP, P, I32, P]
+    lib.kv_cache_update.restype = I32
+    lib.mla_rpa_workspace_size.argtypes = [MP, I32, I32, I32]
+    lib.mla_rpa_workspace_size.restype = SZ
+    lib.mla_rpa_forward.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, MP,
+                                    OP, P, P, SZ, P]
+    lib.mla_rpa_forward.restype = I32
+    lib.sparse_mla_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.sparse_mla_workspace_size.restype = SZ
+    lib.sparse_mla_forward.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
+                                       I32, I32, F32, P, P, SZ, P]
+    lib.sparse_mla_forward.restype = I32
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return 0
+    if t.dtype == torch.bfloat16:
+        return 1
+    if t.dtype == torch.float8_e4m3fn:
+        return 2
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def _i32(t):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise TypeError("metadata tensors must be int32")
+    return t
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _raise(lib, st):
+    if st != 0:
+        raise RpaError(st, lib.rpa_last_error().decode())
+
+
+def _meta(kv_lens, page_indices, cu_q_lens, num_seqs, max_num_tokens):
+    _i32(kv_lens), _i32(page_indices), _i32(cu_q_lens), _i32(num_seqs)
+    m = _Meta()
+    m.cu_q_lens = cu_q_lens.data_ptr()
+    m.kv_lens = kv_lens.data_ptr()
+    m.page_indices = page_indices.data_ptr()
+    m.num_seqs = num_seqs.data_ptr()
+    m.max_num_seqs = kv_lens.numel()
+    m.pages_per_seq = page_indices.numel() // max(1, kv_lens.numel())
+    m.max_num_tokens = max_num_tokens
+    return m
+
+
+def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate):
+    o = _Opts()
+    lib.rpa_opts_init(ctypes.byref(o))
+    o.sm_scale = float(sm_scale)
+    o.sliding_window = int(sliding_window or 0)
+    o.soft_cap = float(soft_cap or 0.0)
+    o.k_scale = float(1.0 if k_scale is None else k_scale)
+    o.v_scale = float(1.0 if v_scale is None else v_scale)
+    o.debug_validate = 1 if debug_validate else 0
+    return o
+
+
+def rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_q_heads, num_kv_heads,
+                       head_dim, page_size):
+    lib = load_library()
+    m = _Meta()
+    m.max_num_seqs = kv_lens.numel()
+    m.pages_per_seq = page_indices.numel() // max(1, kv_lens.numel())
+    m.max_num_tokens = max_num_tokens
+    return int(lib.rpa_workspace_size(ctypes.byref(m), num_q_heads, num_kv_heads, head_dim,
+                                      page_size))
+
+
+def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0,
+                sliding_window=None, soft_cap=None, k_scale=None, v_scale=None, out=None,
+                workspace=None, debug_validate=False, stream=None):
+    """GQA ragged paged attention (see ``rpa_forward`` in include/rpa.h).
+
+    q [T, Hq, D] (fp32/bf16); kv_pages [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn);
+    kv_lens [S], page_indices [S, pps] or [S*pps], cu_q_lens [S+1], num_seqs [1]
+    (int32, on the GPU). Returns ``out`` [T, Hq, D] in q's dtype.
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out, workspace)
+    T, Hq, D = q.shape
+    P, ps, ch, D2 = kv_pages.shape
+    if D2 != D or ch % 2:
+        raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate)
+    need = int(lib.rpa_workspace_size(ctypes.byref(meta), Hq, ch // 2, D, ps))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.rpa_forward(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages), _dtype_code(kv_pages), P,
+                         ps, ch // 2, ctypes.byref(meta), ctypes.byref(opts), _ptr(out),
+                         _ptr(workspace), workspace.numel(), _stream(stream))
+    _raise(lib, st)
+    return out
+
+
+def kv_cache_update(layout, new_a, new_b, cache_a, cache_b=None, *, kv_lens=None,
+                    page_indices=None, cu_q_lens=None, num_seqs=None, slot_loc=None,
+                    debug_validate=False, stream=None):
+    """Scatter new tokens into a paged cache in place (see include/rpa.h).
+
+    COMBINED_GQA: new_a = K [T, Hkv, D], new_b = V [T, Hkv, D], cache_a [P, ps, 2Hkv, D].
+    MLA_SPLIT: new_a = kv_c [T, Dl], new_b = k_pe [T, Dr], cache_a [P, ps, >=Dl],
+               cache_b [P, ps, >=Dr].
+    MLA_FUSED: cache_a [P, ps, >=Dl+Dr] receives [kv_c || k_pe || 0].
+    Addressing: the ragged metadata (page-table mode) or ``slot_loc`` [T].
+    """
+    lib = load_library()
+    _check_dev(new_a, new_b, cache_a, cache_b, kv_lens, page_indices, cu_q_lens, num_seqs,
+               slot_loc)
+    if new_a.dtype != cache_a.dtype or new_b.dtype != cache_a.dtype:
+        raise TypeError("cache dtype must equal the new tokens' dtype")
+    P, ps = cache_a.shape[0], cache_a.shape[1]
+    T = new_a.shape[0]
+    if layout == LAYOUT_COMBINED_GQA:
+        heads, dim_a, dim_b, stride_a, stride_b = new_a.shape[1], new_a.shape[2], 0, 0, 0
+    else:
+        heads, dim_a, dim_b = 0, new_a.shape[1], new_b.shape[1]
+        stride_a = cache_a.shape[2]
+        stride_b = cache_b.shape[2] if cache_b is not None else 0
+    meta = None
+    if slot_loc is None:
+        meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
+    else:
+        _i32(slot_loc)
+    st = lib.kv_cache_update(layout, _ptr(new_a), _ptr(new_b), _ptr(cache_a), _ptr(cache_b),
+                             _dtype_code(cache_a), P, ps, heads, dim_a, dim_b, stride_a, stride_b,
+                             T, ctypes.byref(meta) if meta is not None else None, _ptr(slot_loc),
+                             1 if debug_validate else 0, _stream(stream))
+    _raise(lib, st)
+
+
+def mla_rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_heads, lkv_dim,
+                           page_size):
+    lib = load_library()
+    m = _Meta()
+    m.max_num_seqs = kv_lens.numel()
+    m.pages_per_seq = page_indices.numel() // max(1, kv_lens.numel())
+    m.max_num_tokens = max_num_tokens
+    return int(lib.mla_rpa_workspace_size(ctypes.byref(m), num_heads, lkv_dim, page_size))
+
+
+def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, kv_lens,
+                    page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0, sliding_window=None,
+                    soft_cap=None, out=None, workspace=None, debug_validate=False, stream=None):
+    """MLA ragged paged attention: scatter (unless new_* are None) then attend.
+
+    ql_nope [T, H, 512], q_pe [T, H, 64], new_kv_c [T, 512], new_k_pe [T, 64],
+    cache_kv_c [P, ps, 512], cache_k_pe [P, ps, 128] (bf16). Returns out [T, H, 512].
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_dev(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, kv_lens, page_indices,
+               cu_q_lens, num_seqs, out, workspace)
+    T, H, Dl = ql_nope.shape
+    Dr = q_pe.shape[2]
+    P, ps, kvc_stride = cache_kv_c.shape
+    kpe_stride = cache_k_pe.shape[2]
+    if out is None:
+        out = torch.empty_like(ql_nope)
+    meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, None, None, debug_validate)
+    need = int(lib.mla_rpa_workspace_size(ctypes.byref(meta), H, Dl, ps))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ql_nope.device)
+    st = lib.mla_rpa_forward(_ptr(ql_nope), _ptr(q_pe), _ptr(new_kv_c), _ptr(new_k_pe),
+                             _ptr(cache_kv_c), _ptr(cache_k_pe), _dtype_code(ql_nope), H, Dl, Dr,
+                             kvc_stride, kpe_stride, P, ps, ctypes.byref(meta), ctypes.byref(opts),
+                             _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _raise(lib, st)
+    return out
+
+
+def sparse_mla_workspace_size(num_queries, num_heads, top_k, read_block, kv_lora_rank=512):
+    return int(load_library().sparse_mla_workspace_size(num_queries, num_heads, top_k,
+                                                        read_block, kv_lora_rank))
+
+
+def sparse_mla_forward(q, kv_cache, page_table, indices, positions, *, seq_len, read_block,
+                       sm_scale, kv_lora_rank=512, rope_dim=64, out=None, workspace=None,
+                       stream=None):
+    """Sparse MLA-latent attention over a fused paged latent pool.
+
+    q [S, H, 576] bf16; kv_cache [P, ps, C] bf16; page_table [PTW]; indices [S, K]
+    (-1 = padding); positions [S] (int32). Returns out [S, H, 512] fp32.
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_dev(q, kv_cache, page_table, indices, positions, out, workspace)
+    S, H, Dk = q.shape
+    if Dk != kv_lora_rank + rope_dim:
+        raise ValueError("q last dim must be kv_lora_rank + rope_dim")
+    P, ps, C = kv_cache.shape
+    K = indices.shape[1]
+    if out is None:
+        out = torch.empty((S, H, kv_lora_rank), dtype=torch.float32, device=q.device)
+    need = int(lib.sparse_mla_workspace_size(S, H, K, read_block, kv_lora_rank))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib.sparse_mla_forward(_ptr(q), _ptr(kv_cache), _ptr(_i32(page_table)),
+                                _ptr(_i32(indices)), _ptr(_i32(positions)), int(seq_len), S, H, K,
+                                int(read_block), ps, P, C, page_table.numel(), kv_lora_rank,
+                                rope_dim, float(sm_scale), _ptr(out), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(stream))
+    _raise(lib, st)
+    return out

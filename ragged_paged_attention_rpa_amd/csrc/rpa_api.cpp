@@ -1,0 +1,471 @@
+// Host side of librpa.so: argument checks, workspace carving and launches.
+//
+// Static checks follow the pages' compile-time validators [RPA v2 page:
+// static_validate_inputs; MLA v1 page: static_validate_inputs; Sparse page:
+// sparse_mla_attention argument checks]; the value checks run only when the
+// caller asks for them (debug_validate), as the pages' runtime validators do
+// [RPA v2 page: dynamic_validate_inputs; MLA v1 page: dynamic_validate_inputs].
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "../../include/rpa.h"
+#include "rpa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rpa_status fail(rpa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rpa_status ok() {
+  g_last_error.clear();
+  return RPA_OK;
+}
+
+rpa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RPA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int dtype_bytes(rpa_dtype d) {
+  switch (d) {
+    case RPA_F32: return 4;
+    case RPA_BF16: return 2;
+    case RPA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+rpa_status check_meta(const rpa_ragged_meta* m, bool need_pages) {
+  if (!m) return fail(RPA_E_INVALID, "meta is NULL");
+  if (!m->cu_q_lens || !m->kv_lens || !m->num_seqs || (need_pages && !m->page_indices))
+    return fail(RPA_E_INVALID, "meta has a NULL array");
+  if (m->max_num_seqs <= 0) return fail(RPA_E_SHAPE, "max_num_seqs=%d must be > 0", m->max_num_seqs);
+  if (need_pages && m->pages_per_seq <= 0)
+    return fail(RPA_E_SHAPE, "pages_per_seq=%d must be > 0", m->pages_per_seq);
+  if (m->max_num_tokens < 0) return fail(RPA_E_SHAPE, "max_num_tokens=%d must be >= 0", m->max_num_tokens);
+  return RPA_OK;
+}
+
+rpa_status check_opts(const rpa_opts* o) {
+  if (!o) return fail(RPA_E_INVALID, "opts is NULL");
+  if (!std::isfinite(o->sm_scale)) return fail(RPA_E_INVALID, "sm_scale must be finite");
+  if (o->sliding_window < 0)
+    return fail(RPA_E_INVALID, "sliding_window=%d must be positive (0 = none)", o->sliding_window);
+  if (!std::isfinite(o->soft_cap)) return fail(RPA_E_INVALID, "soft_cap must be finite (0 = none)");
+  if (!std::isfinite(o->k_scale) || !std::isfinite(o->v_scale))
+    return fail(RPA_E_INVALID, "k_scale and v_scale must be finite");
+  return RPA_OK;
+}
+
+struct HostMeta {
+  std::vector<int32_t> cu, kv, pages;
+  int32_t ns = 0;
+};
+
+rpa_status fetch_meta(const rpa_ragged_meta* m, bool need_pages, hipStream_t stream,
+                      HostMeta* h) {
+  h->cu.resize(m->max_num_seqs + 1);
+  h->kv.resize(m->max_num_seqs);
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "debug_validate sync");
+  e = hipMemcpy(h->cu.data(), m->cu_q_lens, h->cu.size() * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess)
+    e = hipMemcpy(h->kv.data(), m->kv_lens, h->kv.size() * 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemcpy(&h->ns, m->num_seqs, 4, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && need_pages) {
+    h->pages.resize((size_t)m->max_num_seqs * m->pages_per_seq);
+    e = hipMemcpy(h->pages.data(), m->page_indices, h->pages.size() * 4, hipMemcpyDeviceToHost);
+  }
+  if (e != hipSuccess) return hip_status(e, "debug_validate copy");
+  return RPA_OK;
+}
+
+// Runtime value checks [RPA v2 page: dynamic_validate_inputs; MLA v1 page:
+// dynamic_validate_inputs].
+rpa_status validate_values(const rpa_ragged_meta* m, const HostMeta& h, int page_size,
+                           int total_num_pages) {
+  if (h.ns < 0 || h.ns > m->max_num_seqs)
+    return fail(RPA_E_INVALID, "num_seqs=%d must be in [0, max_num_seqs=%d]", h.ns, m->max_num_seqs);
+  if (h.cu[h.ns] > m->max_num_tokens)
+    return fail(RPA_E_INVALID, "total q tokens %d must be <= max_num_tokens=%d", h.cu[h.ns],
+                m->max_num_tokens);
+  for (int i = 0; i < h.ns; ++i) {
+    const int q_len = h.cu[i + 1] - h.cu[i];
+    const int kv_len = h.kv[i];
+    if (q_len < 0 || q_len > kv_len)
+      return fail(RPA_E_INVALID, "sequence %d: require 0 <= q_len=%d <= kv_len=%d", i, q_len, kv_len);
+    const int cnt = (kv_len + page_size - 1) / page_size;
+    if (cnt > m->pages_per_seq)
+      return fail(RPA_E_INVALID, "sequence %d: %d pages needed for kv_len=%d > pages_per_seq=%d", i,
+                  cnt, kv_len, m->pages_per_seq);
+    for (int p = 0; p < cnt; ++p) {
+      const int pg = h.pages[(size_t)i * m->pages_per_seq + p];
+      if (pg < 0 || pg >= total_num_pages)
+        return fail(RPA_E_INVALID, "sequence %d: page id %d at logical page %d not in [0, %d)", i,
+                    pg, p, total_num_pages);
+    }
+  }
+  return RPA_OK;
+}
+
+#define RPA_TRY(x)                 \
+  do {                             \
+    rpa_status _s = (x);           \
+    if (_s != RPA_OK) return _s;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+void rpa_opts_init(rpa_opts* o) {
+  if (!o) return;
+  o->sm_scale = 1.0f;
+  o->sliding_window = 0;
+  o->soft_cap = 0.0f;
+  o->k_scale = 1.0f;
+  o->v_scale = 1.0f;
+  o->debug_validate = 0;
+}
+
+const char* rpa_last_error(void) { return g_last_error.c_str(); }
+
+size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t page_size) {
+  (void)page_size;
+  if (!meta || num_kv_heads <= 0 || num_q_heads <= 0 || meta->max_num_seqs <= 0) return 0;
+  return rpa::gqa_workspace_bytes(meta->max_num_seqs, meta->max_num_tokens, num_q_heads,
+                                  num_kv_heads, head_dim, 0, nullptr);
+}
+
+rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
+                       const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
+                       int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
+                       const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
+                       rpa_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  RPA_TRY(check_meta(meta, true));
+  RPA_TRY(check_opts(opts));
+  if (!q || !kv_pages || !out) return fail(RPA_E_INVALID, "q, kv_pages and out must be non-NULL");
+  if (num_q_heads <= 0 || num_kv_heads <= 0)
+    return fail(RPA_E_SHAPE, "head counts must be positive (q %d, kv %d)", num_q_heads, num_kv_heads);
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(RPA_E_SHAPE, "num_q_heads=%d must be divisible by num_kv_heads=%d", num_q_heads,
+                num_kv_heads);
+  if (head_dim <= 0 || head_dim > 512)
+    return fail(RPA_E_SHAPE, "head_dim=%d must be in [1, 512]", head_dim);
+  if (page_size <= 0 || total_num_pages <= 0)
+    return fail(RPA_E_SHAPE, "page_size=%d and total_num_pages=%d must be positive", page_size,
+                total_num_pages);
+  if (q_dtype != RPA_F32 && q_dtype != RPA_BF16)
+    return fail(RPA_E_DTYPE, "q dtype must be F32 or BF16");
+  if (dtype_bytes(kv_dtype) == 0) return fail(RPA_E_DTYPE, "kv dtype must be F32, BF16 or FP8_E4M3");
+
+  rpa::GqaArgs a{};
+  a.q = q;
+  a.kv = kv_pages;
+  a.out = out;
+  a.cu_q_lens = meta->cu_q_lens;
+  a.kv_lens = meta->kv_lens;
+  a.page_indices = meta->page_indices;
+  a.num_seqs = meta->num_seqs;
+  a.max_num_seqs = meta->max_num_seqs;
+  a.pages_per_seq = meta->pages_per_seq;
+  a.max_num_tokens = meta->max_num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.page_size = page_size;
+  a.total_num_pages = total_num_pages;
+  a.q_dtype = (int)q_dtype;
+  a.kv_dtype = (int)kv_dtype;
+  a.score_scale = opts->sm_scale * opts->k_scale;
+  a.soft_cap = opts->soft_cap;
+  a.v_scale = opts->v_scale;
+  a.geo = rpa::gqa_geometry(num_q_heads, num_kv_heads, opts->sliding_window);
+
+  const bool mfma = rpa::gqa_mfma_supported(a.q_dtype, a.kv_dtype, head_dim,
+                                            num_q_heads / num_kv_heads) &&
+                    is_pow2(page_size) && aligned16(q) && aligned16(kv_pages) && aligned16(out);
+  if (mfma) {
+    const size_t need = rpa_workspace_size(meta, num_q_heads, num_kv_heads, head_dim, page_size);
+    if (!workspace || workspace_bytes < need)
+      return fail(RPA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(RPA_E_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  if (opts->debug_validate) {
+    HostMeta h;
+    RPA_TRY(fetch_meta(meta, true, stream, &h));
+    RPA_TRY(validate_values(meta, h, page_size, total_num_pages));
+  }
+  if (meta->max_num_tokens == 0) return ok();
+  if (mfma) {
+    rpa::gqa_bind_workspace(a, workspace);
+    return hip_status(rpa::launch_gqa(a, stream), "rpa_forward launch");
+  }
+  return hip_status(rpa::launch_gqa_generic(a, stream), "rpa_forward launch");
+}
+
+rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const void* new_b,
+                           void* cache_a, void* cache_b, rpa_dtype dtype, int32_t total_num_pages,
+                           int32_t page_size, int32_t heads, int32_t dim_a, int32_t dim_b,
+                           int32_t stride_a, int32_t stride_b, int32_t num_tokens,
+                           const rpa_ragged_meta* meta, const int32_t* slot_loc,
+                           int32_t debug_validate, rpa_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  const int eb = dtype_bytes(dtype);
+  if (eb == 0) return fail(RPA_E_DTYPE, "unknown dtype %d", (int)dtype);
+  if (layout != RPA_LAYOUT_COMBINED_GQA && layout != RPA_LAYOUT_MLA_SPLIT &&
+      layout != RPA_LAYOUT_MLA_FUSED)
+    return fail(RPA_E_INVALID, "unknown layout %d", (int)layout);
+  if (!new_a || !new_b || !cache_a) return fail(RPA_E_INVALID, "new_a, new_b and cache_a must be non-NULL");
+  if (layout == RPA_LAYOUT_MLA_SPLIT && !cache_b)
+    return fail(RPA_E_INVALID, "MLA split layout needs cache_b");
+  if (total_num_pages <= 0 || page_size <= 0)
+    return fail(RPA_E_SHAPE, "page_size=%d and total_num_pages=%d must be positive", page_size,
+                total_num_pages);
+  if (num_tokens < 0) return fail(RPA_E_SHAPE, "num_tokens=%d must be >= 0", num_tokens);
+  if (dim_a <= 0) return fail(RPA_E_SHAPE, "dim_a=%d must be positive", dim_a);
+  if (layout == RPA_LAYOUT_COMBINED_GQA) {
+    if (heads <= 0) return fail(RPA_E_SHAPE, "heads=%d must be positive", heads);
+  } else {
+    if (dim_b <= 0) return fail(RPA_E_SHAPE, "dim_b=%d must be positive", dim_b);
+    if (layout == RPA_LAYOUT_MLA_SPLIT && (stride_a < dim_a || stride_b < dim_b))
+      return fail(RPA_E_SHAPE, "cache strides (%d, %d) must cover the new rows (%d, %d)", stride_a,
+                  stride_b, dim_a, dim_b);
+    if (layout == RPA_LAYOUT_MLA_FUSED && stride_a < dim_a + dim_b)
+      return fail(RPA_E_SHAPE, "fused cache stride %d must cover %d + %d", stride_a, dim_a, dim_b);
+  }
+  if (!slot_loc) RPA_TRY(check_meta(meta, true));
+  if (debug_validate) {
+    std::set<int64_t> seen;
+    if (slot_loc) {
+      std::vector<int32_t> loc(num_tokens);
+      hipError_t e = hipStreamSynchronize(stream);
+      if (e == hipSuccess && num_tokens)
+        e = hipMemcpy(loc.data(), slot_loc, (size_t)num_tokens * 4, hipMemcpyDeviceToHost);
+      if (e != hipSuccess) return hip_status(e, "debug_validate copy");
+      for (int t = 0; t < num_tokens; ++t) {
+        if (loc[t] < 0) continue;
+        if ((int64_t)loc[t] >= (int64_t)total_num_pages * page_size)
+          return fail(RPA_E_INVALID, "token %d: slot %d out of range", t, loc[t]);
+        if (!seen.insert(loc[t]).second)
+          return fail(RPA_E_INVALID, "token %d: slot %d written twice", t, loc[t]);
+      }
+    } else {
+      HostMeta h;
+      RPA_TRY(fetch_meta(meta, true, stream, &h));
+      RPA_TRY(validate_values(meta, h, page_size, total_num_pages));
+      if (h.cu[h.ns] > num_tokens)
+        return fail(RPA_E_INVALID, "total new tokens %d exceed num_tokens=%d", h.cu[h.ns], num_tokens);
+      for (int i = 0; i < h.ns; ++i) {
+        const int q_len = h.cu[i + 1] - h.cu[i];
+        for (int j = 0; j < q_len; ++j) {
+          const int pos = h.kv[i] - q_len + j;
+          const int64_t slot = (int64_t)h.pages[(size_t)i * meta->pages_per_seq + pos / page_size] *
+                                   page_size + pos % page_size;
+          if (!seen.insert(slot).second)
+            return fail(RPA_E_INVALID, "sequence %d token %d: slot %lld written twice", i, j,
+                        (long long)slot);
+        }
+      }
+    }
+  }
+  rpa::KvUpdateArgs a{};
+  a.layout = (int)layout;
+  a.new_a = new_a;
+  a.new_b = new_b;
+  a.cache_a = cache_a;
+  a.cache_b = cache_b;
+  a.elem_bytes = eb;
+  a.total_num_pages = total_num_pages;
+  a.page_size = page_size;
+  a.heads = heads;
+  a.dim_a = dim_a;
+  a.dim_b = dim_b;
+  a.stride_a = stride_a;
+  a.stride_b = stride_b;
+  a.slot_loc = slot_loc;
+  if (meta) {
+    a.cu_q_lens = meta->cu_q_lens;
+    a.kv_lens = meta->kv_lens;
+    a.page_indices = meta->page_indices;
+    a.num_seqs = meta->num_seqs;
+    a.max_num_seqs = meta->max_num_seqs;
+    a.pages_per_seq = meta->pages_per_seq;
+  }
+  return hip_status(rpa::launch_kv_update(a, num_tokens, stream), "kv_cache_update launch");
+}
+
+size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, int32_t lkv_dim,
+                              int32_t page_size) {
+  (void)page_size;
+  if (!meta || meta->max_num_seqs <= 0 || num_heads <= 0 || lkv_dim <= 0) return 0;
+  return rpa::mla_workspace_bytes(meta->max_num_seqs, meta->max_num_tokens, num_heads, lkv_dim,
+                                  nullptr, nullptr);
+}
+
+rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* new_kv_c,
+                           const void* new_k_pe, void* cache_kv_c, void* cache_k_pe,
+                           rpa_dtype dtype, int32_t num_heads, int32_t lkv_dim, int32_t r_dim,
+                           int32_t kvc_stride, int32_t kpe_stride, int32_t total_num_pages,
+                           int32_t page_size, const rpa_ragged_meta* meta, const rpa_opts* opts,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           rpa_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  RPA_TRY(check_meta(meta, true));
+  RPA_TRY(check_opts(opts));
+  if (!ql_nope || !q_pe || !cache_kv_c || !cache_k_pe || !out)
+    return fail(RPA_E_INVALID, "ql_nope, q_pe, caches and out must be non-NULL");
+  if ((new_kv_c == nullptr) != (new_k_pe == nullptr))
+    return fail(RPA_E_INVALID, "new_kv_c and new_k_pe must be both set or both NULL");
+  if (dtype != RPA_BF16) return fail(RPA_E_UNSUPPORTED, "mla_rpa_forward implements BF16 only");
+  if (num_heads <= 0) return fail(RPA_E_SHAPE, "num_heads=%d must be positive", num_heads);
+  if (lkv_dim != 512 || r_dim != 64)
+    return fail(RPA_E_UNSUPPORTED, "mla_rpa_forward implements lkv_dim=512, r_dim=64 (got %d, %d)",
+                lkv_dim, r_dim);
+  if (kvc_stride < lkv_dim || kpe_stride < r_dim)
+    return fail(RPA_E_SHAPE, "cache strides (%d, %d) must cover (%d, %d)", kvc_stride, kpe_stride,
+                lkv_dim, r_dim);
+  // The page pads both latent parts to multiples of 128 columns.
+  if (kvc_stride % 128 != 0 || kpe_stride % 128 != 0)
+    return fail(RPA_E_SHAPE, "cache strides (%d, %d) must be multiples of 128", kvc_stride, kpe_stride);
+  if (page_size <= 0 || total_num_pages <= 0 || !is_pow2(page_size))
+    return fail(RPA_E_SHAPE, "page_size=%d must be a positive power of two; total_num_pages=%d > 0",
+                page_size, total_num_pages);
+  if (opts->k_scale != 1.0f || opts->v_scale != 1.0f)
+    return fail(RPA_E_UNSUPPORTED, "k_scale/v_scale are not applied by the MLA path");
+  if (!aligned16(ql_nope) || !aligned16(q_pe) || !aligned16(cache_kv_c) || !aligned16(cache_k_pe) ||
+      !aligned16(out))
+    return fail(RPA_E_INVALID, "MLA tensors must be 16-byte aligned");
+  const size_t need = mla_rpa_workspace_size(meta, num_heads, lkv_dim, page_size);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace))
+    return fail(RPA_E_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (opts->debug_validate) {
+    HostMeta h;
+    RPA_TRY(fetch_meta(meta, true, stream, &h));
+    RPA_TRY(validate_values(meta, h, page_size, total_num_pages));
+  }
+  if (new_kv_c) {
+    rpa_status st = kv_cache_update(RPA_LAYOUT_MLA_SPLIT, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe,
+                                    dtype, total_num_pages, page_size, 0, lkv_dim, r_dim,
+                                    kvc_stride, kpe_stride, meta->max_num_tokens, meta, nullptr, 0,
+                                    stream_);
+    if (st != RPA_OK) return st;
+  }
+  if (meta->max_num_tokens == 0) return ok();
+  rpa::MlaArgs a{};
+  a.ql_nope = ql_nope;
+  a.q_pe = q_pe;
+  a.cache_kv_c = cache_kv_c;
+  a.cache_k_pe = cache_k_pe;
+  a.out = out;
+  a.cu_q_lens = meta->cu_q_lens;
+  a.kv_lens = meta->kv_lens;
+  a.page_indices = meta->page_indices;
+  a.num_seqs = meta->num_seqs;
+  a.max_num_seqs = meta->max_num_seqs;
+  a.pages_per_seq = meta->pages_per_seq;
+  a.max_num_tokens = meta->max_num_tokens;
+  a.num_heads = num_heads;
+  a.lkv_dim = lkv_dim;
+  a.r_dim = r_dim;
+  a.kvc_stride = kvc_stride;
+  a.kpe_stride = kpe_stride;
+  a.page_size = page_size;
+  a.total_num_pages = total_num_pages;
+  a.score_scale = opts->sm_scale;
+  a.soft_cap = opts->soft_cap;
+  a.window = opts->sliding_window;
+  rpa::mla_bind_workspace(a, workspace);
+  return hip_status(rpa::launch_mla(a, stream), "mla_rpa_forward launch");
+}
+
+size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t top_k,
+                                 int32_t read_block, int32_t kv_lora_rank) {
+  (void)num_queries;
+  (void)num_heads;
+  (void)top_k;
+  (void)read_block;
+  (void)kv_lora_rank;
+  return 0;
+}
+
+rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t* page_table,
+                              const int32_t* indices, const int32_t* positions, int32_t seq_len,
+                              int32_t num_queries, int32_t num_heads, int32_t top_k,
+                              int32_t read_block, int32_t page_size, int32_t total_num_pages,
+                              int32_t cache_dim, int32_t ptw, int32_t kv_lora_rank,
+                              int32_t rope_dim, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, rpa_stream_t stream_) {
+  (void)workspace;
+  (void)workspace_bytes;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  if (!q || !kv_cache || !page_table || !indices || !positions || !out)
+    return fail(RPA_E_INVALID, "q, kv_cache, page_table, indices, positions and out must be non-NULL");
+  // sm_scale has no safe default [Sparse page: sparse_mla_attention].
+  if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
+    return fail(RPA_E_INVALID, "sm_scale is required and must be finite and > 0");
+  if (num_queries < 0 || num_heads <= 0 || top_k <= 0)
+    return fail(RPA_E_SHAPE, "num_queries=%d >= 0, num_heads=%d > 0, top_k=%d > 0 required",
+                num_queries, num_heads, top_k);
+  if (read_block <= 0 || read_block % 16 != 0)
+    return fail(RPA_E_INVALID, "read_block=%d must be a positive multiple of 16", read_block);
+  if (page_size <= 0 || page_size % read_block != 0)
+    return fail(RPA_E_INVALID, "page_size=%d must be a multiple of read_block=%d", page_size, read_block);
+  if (kv_lora_rank != 512 || rope_dim != 64)
+    return fail(RPA_E_UNSUPPORTED, "sparse_mla_forward implements kv_lora_rank=512, rope_dim=64");
+  const int dk = kv_lora_rank + rope_dim;
+  if (cache_dim < dk || cache_dim % 8 != 0)
+    return fail(RPA_E_SHAPE, "cache_dim=%d must be >= %d and a multiple of 8", cache_dim, dk);
+  if (total_num_pages <= 0 || ptw <= 0)
+    return fail(RPA_E_SHAPE, "total_num_pages=%d and ptw=%d must be positive", total_num_pages, ptw);
+  if (seq_len < 0) return fail(RPA_E_INVALID, "seq_len=%d must be >= 0", seq_len);
+  if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out))
+    return fail(RPA_E_INVALID, "q, kv_cache and out must be 16-byte aligned");
+  if (num_queries == 0) return ok();
+  rpa::SparseArgs a{};
+  a.q = q;
+  a.kv = kv_cache;
+  a.page_table = page_table;
+  a.indices = indices;
+  a.positions = positions;
+  a.out = out;
+  a.seq_len = seq_len;
+  a.num_queries = num_queries;
+  a.num_heads = num_heads;
+  a.top_k = top_k;
+  a.read_block = read_block;
+  a.page_size = page_size;
+  a.total_num_pages = total_num_pages;
+  a.cache_dim = cache_dim;
+  a.ptw = ptw;
+  a.dv = kv_lora_rank;
+  a.dk = dk;
+  a.score_scale = sm_scale;
+  return hip_status(rpa::launch_sparse_mla(a, stream), "sparse_mla_forward launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side helpers shared by the gfx950 kernels of librpa.
+//
+// Everything here is wave64 / CDNA4 specific: MFMA builtins, the hardware
+// exp2, OCP-fp8 conversions and lane shuffles. Nothing here is used by the
+// CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rpa {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float floatx4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float floatx2 __attribute__((__vector_size__(2 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) {
+  return __uint_as_float(h16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> packed pair of bf16 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// Four OCP E4M3FN bytes of `w` -> four fp32 (exact; the hardware converter
+// of gfx950 uses the OCP encoding).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = lo[0];
+  o[1] = lo[1];
+  o[2] = hi[0];
+  o[3] = hi[1];
+}
+
+// Four OCP E4M3FN bytes -> two dwords of packed bf16 (exact: every E4M3FN
+// value is a bf16 value, so the bf16 pattern is the fp32 pattern's top half).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  floatx2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  floatx2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2 r;
+  r[0] = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+  r[1] = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh from its definition, tanh(x) = 1 - 2 / (exp(2x) + 1), evaluated with
+// the hardware exp2; saturates cleanly to +-1 for large |x|.
+__device__ __forceinline__ float tanh_def(float x) {
+  const float e = fast_exp2(2.0f * kLog2e * x);
+  return 1.0f - 2.0f / (e + 1.0f);
+}
+
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16) on one wave.
+// Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16], and
+// D[4*(l/16) + i][l%16] for i = 0..3.
+__device__ __forceinline__ floatx4 mfma_16x16x32(const bf16x8& a, const bf16x8& b,
+                                                 const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+__device__ __forceinline__ float wave_sum_xor(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ int cdiv_i(int a, int b) { return (a + b - 1) / b; }
+
+// Largest i in [0, n) with cu[i] <= t (the sequence owning packed token t),
+// or -1 when t is past cu[n].
+__device__ __forceinline__ int find_seq(const int32_t* cu, int n, int t) {
+  if (n <= 0 || t >= cu[n] || t < cu[0]) return -1;
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace rpa

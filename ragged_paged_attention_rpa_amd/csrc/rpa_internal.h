@@ -1,0 +1,123 @@
+// Internal interface between the host API (rpa_api.cpp) and the kernel
+// launchers (*.hip). Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rpa {
+
+// ---------------------------------------------------------------- update ----
+struct KvUpdateArgs {
+  int layout;  // 0 combined GQA, 1 MLA split, 2 MLA fused
+  const void* new_a;
+  const void* new_b;
+  void* cache_a;
+  void* cache_b;
+  int elem_bytes;
+  int total_num_pages, page_size, heads, dim_a, dim_b, stride_a, stride_b;
+  const int32_t* cu_q_lens;
+  const int32_t* kv_lens;
+  const int32_t* page_indices;
+  const int32_t* num_seqs;
+  int max_num_seqs, pages_per_seq;
+  const int32_t* slot_loc;
+};
+hipError_t launch_kv_update(const KvUpdateArgs& a, int num_tokens, hipStream_t stream);
+
+// ------------------------------------------------------------------- GQA ----
+// Work-list tile: one (sequence, kv head, query block, kv split) unit.
+struct Tile {
+  int32_t seq;
+  int32_t qtok0;  // first query token of the block, relative to the sequence
+  int32_t kvh;
+  int32_t split;  // >= 0: split index of a decode-class tile; -1: whole key range
+};
+
+// Geometry shared by the planner, the attention kernel and the merge kernel.
+struct GqaGeometry {
+  int group;        // Hq / Hkv
+  int qdec;         // sequences with q_len <= qdec are decode-class (q_len*group <= 16)
+  int bq;           // query tokens per prefill-class tile (bq*group <= 64)
+  int split_keys;   // target keys per decode split
+  int max_splits;   // cap on splits per decode sequence
+  int window;       // sliding window (0 = none)
+};
+
+struct GqaArgs {
+  const void* q;
+  const void* kv;
+  void* out;
+  const int32_t* cu_q_lens;
+  const int32_t* kv_lens;
+  const int32_t* page_indices;
+  const int32_t* num_seqs;
+  int max_num_seqs, pages_per_seq, max_num_tokens;
+  int num_q_heads, num_kv_heads, head_dim, page_size, total_num_pages;
+  int q_dtype, kv_dtype;
+  float score_scale;  // sm_scale * k_scale
+  float soft_cap;     // 0 = none
+  float v_scale;
+  GqaGeometry geo;
+  // workspace
+  Tile* tiles;
+  int32_t* counters;  // [0] tile count, [1] work cursor
+  float* part_acc;    // [max_num_seqs*Hkv*max_splits][16][D]
+  float* part_ml;     // [max_num_seqs*Hkv*max_splits][16][2]
+  int tile_capacity;
+};
+
+GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window);
+size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads,
+                           int num_kv_heads, int head_dim, int window, int* tile_capacity);
+// Carves the workspace into tiles/counters/partials of GqaArgs.
+void gqa_bind_workspace(GqaArgs& a, void* ws);
+bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group);
+hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream);
+hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------- MLA ----
+struct MlaArgs {
+  const void* ql_nope;
+  const void* q_pe;
+  const void* cache_kv_c;
+  const void* cache_k_pe;
+  void* out;
+  const int32_t* cu_q_lens;
+  const int32_t* kv_lens;
+  const int32_t* page_indices;
+  const int32_t* num_seqs;
+  int max_num_seqs, pages_per_seq, max_num_tokens;
+  int num_heads, lkv_dim, r_dim, kvc_stride, kpe_stride, page_size, total_num_pages;
+  float score_scale;
+  float soft_cap;
+  int window;
+  int split_keys, max_splits;
+  // workspace
+  int32_t* tiles;     // [capacity][4]
+  int32_t* counters;  // [0] count, [1] cursor
+  float* part_acc;    // [capacity][num_heads][lkv_dim]
+  float* part_ml;     // [capacity][num_heads][2]
+  int tile_capacity;
+};
+size_t mla_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_heads, int lkv_dim,
+                           int* tile_capacity, int* max_splits);
+void mla_bind_workspace(MlaArgs& a, void* ws);
+hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- sparse ----
+struct SparseArgs {
+  const void* q;
+  const void* kv;
+  const int32_t* page_table;
+  const int32_t* indices;
+  const int32_t* positions;
+  float* out;
+  int seq_len, num_queries, num_heads, top_k, read_block, page_size, total_num_pages,
+      cache_dim, ptw, dv, dk;
+  float score_scale;
+};
+hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t stream);
+
+}  // namespace rpa

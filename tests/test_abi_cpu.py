@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library builds and loads, exports every
+function include/rpa.h declares, and rejects invalid static arguments with
+the documented status before touching device memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ragged_paged_attention_rpa_amd as rpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rpa.h")
+
+RPA_E_INVALID, RPA_E_SHAPE, RPA_E_DTYPE, RPA_E_UNSUPPORTED, RPA_E_WORKSPACE = 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rpa.library_path()):
+        from ragged_paged_attention_rpa_amd import build
+        build.build()
+    return rpa.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_operations():
+    names = _declared_functions()
+    for op in ("rpa_forward", "kv_cache_update", "mla_rpa_forward", "sparse_mla_forward"):
+        assert op in names
+    assert set(names) == set(rpa.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"{name} not exported by librpa.so"
+
+
+def _meta(S=4, pps=8, T=16):
+    m = rpa._Meta()
+    fake = 0x10000
+    m.cu_q_lens = m.kv_lens = m.page_indices = m.num_seqs = fake
+    m.max_num_seqs, m.pages_per_seq, m.max_num_tokens = S, pps, T
+    return m
+
+
+def _opts(lib, **kw):
+    o = rpa._Opts()
+    lib.rpa_opts_init(ctypes.byref(o))
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def test_opts_defaults(lib):
+    o = _opts(lib)
+    assert (o.sm_scale, o.sliding_window, o.soft_cap, o.k_scale, o.v_scale, o.debug_validate) == \
+        (1.0, 0, 0.0, 1.0, 1.0, 0)
+
+
+FAKE = ctypes.c_void_p(0x10000)
+
+
+def _fwd(lib, Hq=8, D=128, Hkv=2, ps=16, P=32, qd=1, kvd=1, meta=None, opts=None, ws=None,
+         ws_bytes=0):
+    meta = meta or _meta()
+    opts = opts or _opts(lib)
+    return lib.rpa_forward(FAKE, qd, Hq, D, FAKE, kvd, P, ps, Hkv, ctypes.byref(meta),
+                           ctypes.byref(opts), FAKE, ws, ws_bytes, None)
+
+
+def test_rpa_forward_static_rejections(lib):
+    assert _fwd(lib, Hq=6, Hkv=4) == RPA_E_SHAPE
+    assert "divisible" in lib.rpa_last_error().decode()
+    assert _fwd(lib, D=0) == RPA_E_SHAPE
+    assert _fwd(lib, ps=0) == RPA_E_SHAPE
+    assert _fwd(lib, qd=2) == RPA_E_DTYPE            # fp8 queries are not accepted
+    assert _fwd(lib, kvd=7) == RPA_E_DTYPE
+    assert _fwd(lib, opts=_opts(lib, sliding_window=-1)) == RPA_E_INVALID
+    assert _fwd(lib, opts=_opts(lib, soft_cap=float("inf"))) == RPA_E_INVALID
+    assert _fwd(lib, opts=_opts(lib, sm_scale=float("nan"))) == RPA_E_INVALID
+    assert _fwd(lib, meta=_meta(S=0)) == RPA_E_SHAPE
+    # bf16 MFMA path without workspace
+    assert _fwd(lib) == RPA_E_WORKSPACE
+    assert "workspace" in lib.rpa_last_error().decode()
+
+
+def test_workspace_size_depends_only_on_capacities(lib):
+    a = lib.rpa_workspace_size(ctypes.byref(_meta(S=128, pps=512, T=128)), 32, 8, 128, 16)
+    b = lib.rpa_workspace_size(ctypes.byref(_meta(S=128, pps=512, T=128)), 32, 8, 128, 16)
+    c = lib.rpa_workspace_size(ctypes.byref(_meta(S=256, pps=512, T=128)), 32, 8, 128, 16)
+    assert a == b > 0 and c > a
+
+
+def test_kv_update_static_rejections(lib):
+    m = _meta()
+    f = lib.kv_cache_update
+    assert f(9, FAKE, FAKE, FAKE, None, 1, 4, 16, 2, 128, 0, 0, 0, 4, ctypes.byref(m), None, 0,
+             None) == RPA_E_INVALID
+    assert f(1, FAKE, FAKE, FAKE, None, 1, 4, 16, 0, 512, 64, 512, 128, 4, ctypes.byref(m), None,
+             0, None) == RPA_E_INVALID    # split layout without cache_b
+    assert f(1, FAKE, FAKE, FAKE, FAKE, 1, 4, 16, 0, 512, 64, 512, 32, 4, ctypes.byref(m), None,
+             0, None) == RPA_E_SHAPE      # stride_b < dim_b
+    assert f(2, FAKE, FAKE, FAKE, None, 1, 4, 16, 0, 512, 64, 512, 0, 4, None, FAKE, 0,
+             None) == RPA_E_SHAPE         # fused stride < 576
+    assert f(0, FAKE, FAKE, FAKE, None, 5, 4, 16, 2, 128, 0, 0, 0, 4, ctypes.byref(m), None, 0,
+             None) != 0                   # unknown dtype
+
+
+def test_mla_static_rejections(lib):
+    m = _meta()
+    o = _opts(lib)
+    f = lib.mla_rpa_forward
+    args = lambda **k: [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k.get("dt", 1), 128, k.get("dl", 512),
+                        64, 512, 128, 64, 64, ctypes.byref(m), ctypes.byref(o), FAKE, None, 0, None]
+    assert f(*args(dt=0)) == RPA_E_UNSUPPORTED
+    assert f(*args(dl=256)) == RPA_E_UNSUPPORTED
+    assert f(*args()) == RPA_E_WORKSPACE
+
+
+def test_sparse_static_rejections(lib):
+    f = lib.sparse_mla_forward
+    base = dict(seq_len=100, S=4, H=16, K=8, RB=64, ps=64, P=4, C=640, ptw=4, kl=512, rd=64, sc=0.07)
+
+    def call(**k):
+        a = {**base, **k}
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, a["seq_len"], a["S"], a["H"], a["K"], a["RB"],
+                 a["ps"], a["P"], a["C"], a["ptw"], a["kl"], a["rd"], a["sc"], FAKE, None, 0, None)
+
+    assert call(sc=0.0) == RPA_E_INVALID       # sm_scale is required
+    assert call(RB=24) == RPA_E_INVALID        # read_block % 16
+    assert call(ps=96) == RPA_E_INVALID        # page_size % read_block
+    assert call(C=512) == RPA_E_SHAPE          # cache narrower than the latent
+    assert call(kl=256) == RPA_E_UNSUPPORTED

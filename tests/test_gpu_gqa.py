@@ -1,0 +1,283 @@
+"""GPU parity of rpa_forward and kv_cache_update against the CPU oracle.
+
+Each case prints its name before the GPU call so a failure names its case.
+Tolerances (max-abs / mean-abs over the compared outputs): fp32 1e-4 / -,
+bf16 2e-2 / 2e-3, fp8 KV 5e-2 / 5e-3; kv_cache_update is bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ragged_paged_attention_rpa_amd as rpa
+from ragged_paged_attention_rpa_amd import workloads as wl
+from tests.helpers import as_f64, assert_close, storage
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": (1e-4, None), "bf16": (2e-2, 2e-3), "fp8": (5e-2, 5e-3)}
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _dev_meta(c):
+    dev = "cuda"
+    return (torch.from_numpy(c.kv_lens).to(dev), torch.from_numpy(c.page_indices).to(dev),
+            torch.from_numpy(c.cu_q_lens).to(dev),
+            torch.tensor([c.num_seqs], dtype=torch.int32, device=dev))
+
+
+def _run_gpu(c, **kw):
+    kl, pi, cu, ns = _dev_meta(c)
+    out = rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, sm_scale=c.sm_scale,
+                          sliding_window=c.sliding_window, soft_cap=c.soft_cap,
+                          k_scale=c.k_scale, v_scale=c.v_scale, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _run_oracle(c, tokens=None, kv_pages=None):
+    q, qd = storage(c.q)
+    kv, kd = storage(c.kv_pages if kv_pages is None else kv_pages)
+    return oracle.rpa(q, qd, kv, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
+                      sm_scale=c.sm_scale, sliding_window=c.sliding_window, soft_cap=c.soft_cap,
+                      k_scale=c.k_scale, v_scale=c.v_scale, tokens=tokens)
+
+
+def _check(c, got, want, tol, tokens=None):
+    rows = np.arange(int(c.cu_q_lens[c.num_seqs])) if tokens is None else np.asarray(tokens)
+    return assert_close(as_f64(got)[rows], want[rows], *TOL[tol], what=c.name)
+
+
+def test_tiny_gqa_fp32():
+    _say("tiny_gqa fp32")
+    c = wl.tiny_gqa(device="cuda")
+    _check(c, _run_gpu(c), _run_oracle(c), "f32")
+
+
+RAGGED = [
+    # (seqs, Hq, Hkv, ps, window, cap, name)
+    ([(1, 1), (1, 63), (1, 64), (1, 65), (3, 200), (1, 1000)], 32, 8, 16, None, None, "decode-ish"),
+    ([(17, 17), (64, 100), (5, 300), (1, 77), (130, 700)], 32, 8, 16, None, None, "prefill-mix"),
+    ([(1, 300), (40, 1200), (2, 129), (70, 70)], 16, 16, 32, 100, None, "mha-window"),
+    ([(9, 200), (1, 5000), (33, 513)], 8, 1, 64, None, 30.0, "mqa-cap"),
+    ([(4, 4), (2, 1025), (24, 900)], 16, 2, 16, 257, 20.0, "g8-window-cap"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(RAGGED)), ids=[r[-1] for r in RAGGED])
+def test_ragged_bf16(idx):
+    seqs, Hq, Hkv, ps, window, cap, name = RAGGED[idx]
+    _say(f"ragged bf16 {name}")
+    c = wl.make_gqa(seqs, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=ps,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=100 + idx,
+                    device="cuda", sliding_window=window, soft_cap=cap, name=name)
+    _check(c, _run_gpu(c), _run_oracle(c), "bf16")
+
+
+@pytest.mark.parametrize("cap,qscale", [(None, 1.0), (50.0, 1.0), (50.0, 16.0)])
+def test_ragged_fp8_scales(cap, qscale):
+    _say(f"ragged fp8 cap={cap} qscale={qscale}")
+    seqs = [(1, 700), (1, 33), (150, 900), (2, 2), (64, 64)]
+    c = wl.make_gqa(seqs, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn, seed=31, device="cuda",
+                    kv_value_scale=2.0, q_value_scale=qscale, sliding_window=300, soft_cap=cap,
+                    k_scale=0.5, v_scale=0.5, name="fp8")
+    _check(c, _run_gpu(c), _run_oracle(c), "fp8")
+
+
+def test_nan_pages_and_tails_are_never_read():
+    _say("nan hygiene")
+    seqs = [(1, 37), (20, 90), (1, 16)]
+    c = wl.make_gqa(seqs, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=5, device="cuda",
+                    spare_pages=4)
+    clean = _run_gpu(c).clone()
+    kv = c.kv_pages.clone()
+    used = {}
+    for i, (ql, L) in enumerate(seqs):
+        for lp in range(wl.cdiv(L, 16)):
+            used[int(c.page_indices[i, lp])] = (i, lp)
+    for pg in range(kv.shape[0]):
+        if pg not in used:
+            kv[pg] = float("nan")
+        else:
+            i, lp = used[pg]
+            tail = seqs[i][1] - lp * 16
+            if tail < 16:
+                kv[pg, tail:] = float("nan")
+    c.kv_pages = kv
+    dirty = _run_gpu(c)
+    n = int(c.cu_q_lens[c.num_seqs])
+    assert torch.isfinite(dirty[:n].float()).all()
+    assert torch.equal(dirty[:n], clean[:n])
+
+
+def test_deterministic_and_page_permutation_invariant():
+    _say("determinism + permutation")
+    seqs = [(1, 500), (30, 400), (1, 2000)]
+    c = wl.make_gqa(seqs, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=6, device="cuda")
+    a = _run_gpu(c).clone()
+    b = _run_gpu(c).clone()
+    n = int(c.cu_q_lens[c.num_seqs])
+    assert torch.equal(a[:n], b[:n])
+    perm = torch.randperm(c.kv_pages.shape[0], generator=torch.Generator().manual_seed(1))
+    kv2 = torch.empty_like(c.kv_pages)
+    kv2[perm.cuda()] = c.kv_pages
+    c.kv_pages = kv2
+    c.page_indices = perm.numpy().astype(np.int32)[c.page_indices]
+    d = _run_gpu(c)
+    assert torch.equal(a[:n], d[:n])
+
+
+def test_kv_len_one_and_equal_scores():
+    _say("kv_len=1 and Q=0")
+    c = wl.make_gqa([(1, 1), (1, 50)], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=7,
+                    device="cuda")
+    c.q[0].zero_()
+    c.q[1].zero_()
+    out = _run_gpu(c).float().cpu()
+    kv = c.kv_pages.float().cpu()
+    pg = int(c.page_indices[0, 0])
+    for h in range(8):
+        assert torch.equal(out[0, h], kv[pg, 0, 2 * (h // 4) + 1].bfloat16().float())
+    # Q = 0: the mean of the 50 visible values.
+    rows = [kv[int(c.page_indices[1, t // 16]), t % 16] for t in range(50)]
+    mean = torch.stack(rows).double().mean(0)
+    for h in range(8):
+        want = mean[2 * (h // 4) + 1]
+        assert (out[1, h].double() - want).abs().max() < 1e-2
+
+
+def test_empty_batch_and_padding_rows_untouched():
+    _say("num_seqs=0 and padding rows")
+    c = wl.make_gqa([(3, 40), (1, 20)], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=8,
+                    device="cuda", extra_tokens=5)
+    kl, pi, cu, ns = _dev_meta(c)
+    sentinel = torch.full_like(c.q, 7.0)
+    out = rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, torch.zeros_like(ns), out=sentinel.clone(),
+                          sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sentinel)
+    out = rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, out=sentinel.clone(), sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out[4:], sentinel[4:])
+    want = _run_oracle(c)
+    assert_close(as_f64(out)[:4], want[:4], *TOL["bf16"])
+
+
+def test_debug_validate_rejects_bad_metadata():
+    _say("debug_validate")
+    c = wl.make_gqa([(3, 40), (1, 20)], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=9,
+                    device="cuda")
+    kl, pi, cu, ns = _dev_meta(c)
+    bad_kl = kl.clone()
+    bad_kl[0] = 2   # q_len 3 > kv_len 2
+    with pytest.raises(rpa.RpaError, match="q_len"):
+        rpa.rpa_forward(c.q, c.kv_pages, bad_kl, pi, cu, ns, debug_validate=True)
+    bad_pi = pi.clone()
+    bad_pi[1, 0] = c.kv_pages.shape[0]
+    with pytest.raises(rpa.RpaError, match="page id"):
+        rpa.rpa_forward(c.q, c.kv_pages, kl, bad_pi, cu, ns, debug_validate=True)
+    with pytest.raises(rpa.RpaError, match="num_seqs"):
+        rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns + 5, debug_validate=True)
+    out = rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, debug_validate=True, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    assert_close(as_f64(out), _run_oracle(c), *TOL["bf16"])
+
+
+# --------------------------------------------------------- full workloads --
+
+def test_decode_gqa_full_size_sampled():
+    _say("decode_gqa full size (128 seqs, kv 512..8192), sampled rows")
+    c = wl.decode_gqa(device="cuda")
+    got = _run_gpu(c)
+    tokens = np.arange(0, 128, 5)
+    want = _run_oracle(c, tokens=tokens)
+    _check(c, got, want, "bf16", tokens=tokens)
+
+
+def test_mixed_gqa_full_size_sampled():
+    _say("mixed_gqa full size (120 decodes + 8 prefill chunks), sampled rows")
+    c = wl.mixed_gqa(device="cuda")
+    got = _run_gpu(c)
+    rng = np.random.default_rng(0)
+    T = int(c.cu_q_lens[c.num_seqs])
+    tokens = np.unique(np.concatenate([np.arange(0, 120, 7), rng.integers(120, T, 24),
+                                       c.cu_q_lens[121:129] - 1]))
+    want = _run_oracle(c, tokens=tokens)
+    _check(c, got, want, "fp8", tokens=tokens)
+
+
+# ------------------------------------------------------------- kv update --
+
+def test_kv_update_combined_bit_exact():
+    _say("kv_cache_update combined")
+    seqs = [(1, 37), (20, 90), (3, 3)]
+    c = wl.make_gqa(seqs, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=10, device="cuda",
+                    spare_pages=2)
+    T = int(c.cu_q_lens[-1])
+    g = torch.Generator(device="cuda").manual_seed(3)
+    newk = torch.randn((T, 2, 128), generator=g, device="cuda").bfloat16()
+    newv = torch.randn((T, 2, 128), generator=g, device="cuda").bfloat16()
+    host = storage(c.kv_pages)[0].copy()
+    kl, pi, cu, ns = _dev_meta(c)
+    rpa.kv_cache_update(rpa.LAYOUT_COMBINED_GQA, newk, newv, c.kv_pages, kv_lens=kl,
+                        page_indices=pi, cu_q_lens=cu, num_seqs=ns, debug_validate=True)
+    torch.cuda.synchronize()
+    oracle.kv_update(oracle.LAYOUT_COMBINED_GQA, storage(newk)[0], storage(newv)[0], host, None,
+                     oracle.BF16, kv_lens=c.kv_lens, page_indices=c.page_indices,
+                     cu_q_lens=c.cu_q_lens, num_seqs=c.num_seqs)
+    assert np.array_equal(storage(c.kv_pages)[0], host)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_kv_update_mla_bit_exact(fused):
+    _say(f"kv_cache_update mla fused={fused}")
+    c = wl.make_mla([(1, 100), (5, 64), (2, 200)], num_heads=4, page_size=64, seed=11,
+                    device="cuda", spare_pages=2)
+    if fused:
+        P, ps = c.cache_kv_c.shape[:2]
+        cache = torch.randn((P, ps, 640), device="cuda").bfloat16()
+        host = storage(cache)[0].copy()
+        loc = torch.tensor([5, -1, 70, 3, 129, -1, 64, 200], dtype=torch.int32, device="cuda")
+        rpa.kv_cache_update(rpa.LAYOUT_MLA_FUSED, c.new_kv_c, c.new_k_pe, cache, slot_loc=loc,
+                            debug_validate=True)
+        torch.cuda.synchronize()
+        oracle.kv_update(oracle.LAYOUT_MLA_FUSED, storage(c.new_kv_c)[0], storage(c.new_k_pe)[0],
+                         host, None, oracle.BF16, slot_loc=loc.cpu().numpy())
+        assert np.array_equal(storage(cache)[0], host)
+        return
+    ha = storage(c.cache_kv_c)[0].copy()
+    hb = storage(c.cache_k_pe)[0].copy()
+    kl, pi, cu, ns = _dev_meta(c)
+    rpa.kv_cache_update(rpa.LAYOUT_MLA_SPLIT, c.new_kv_c, c.new_k_pe, c.cache_kv_c, c.cache_k_pe,
+                        kv_lens=kl, page_indices=pi, cu_q_lens=cu, num_seqs=ns)
+    torch.cuda.synchronize()
+    oracle.kv_update(oracle.LAYOUT_MLA_SPLIT, storage(c.new_kv_c)[0], storage(c.new_k_pe)[0], ha,
+                     hb, oracle.BF16, kv_lens=c.kv_lens, page_indices=c.page_indices,
+                     cu_q_lens=c.cu_q_lens, num_seqs=c.num_seqs)
+    assert np.array_equal(storage(c.cache_kv_c)[0], ha)
+    assert np.array_equal(storage(c.cache_k_pe)[0], hb)
+
+
+def test_kv_update_rejects_aliased_slots():
+    _say("kv_cache_update aliasing")
+    c = wl.make_mla([(1, 100)], num_heads=4, page_size=64, seed=12, device="cuda")
+    P, ps = c.cache_kv_c.shape[:2]
+    cache = torch.zeros((P, ps, 640), device="cuda", dtype=torch.bfloat16)
+    loc = torch.tensor([7], dtype=torch.int32, device="cuda")
+    two_kvc = torch.cat([c.new_kv_c, c.new_kv_c])
+    two_kpe = torch.cat([c.new_k_pe, c.new_k_pe])
+    with pytest.raises(rpa.RpaError, match="twice"):
+        rpa.kv_cache_update(rpa.LAYOUT_MLA_FUSED, two_kvc, two_kpe, cache,
+                            slot_loc=torch.cat([loc, loc]), debug_validate=True)
