@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark of the ragged paged attention hot path on one MI355X.
+
+A "step" is one full call of the entry point over one synthetic batch (all
+launches: work-list plan, attention tiles, split merge). Inputs are resident
+in HBM before timing starts. Prints ONE JSON line.
+
+Workloads (--config):
+  decode_gqa  (default) 128 decodes, kv_len U[512,8192], 32/8 heads, d128,
+              page 16, bf16 — metric: decode KV GB/s (algorithmic KV bytes)
+  mixed_gqa   120 decodes + 8 prefill chunks, fp8 KV, window 4096, cap 50
+  mla_decode  64 MLA decodes, kv_len U[4096,32768], 128 heads, page 64
+  sparse_mla  4096 queries x 32 page units of 64 tokens, 16 heads
+  tiny_gqa    3 sequences, fp32
+
+The roofline object refers to the dominant kernel, timed with HIP events that
+the library records on its own stream right around that kernel. `traffic`
+comes from the committed rocprofv3 PMC summary for the same workload when it
+was taken on the current kernel source, else null. `cpu_baseline` times the
+CPU oracle on a bounded sample of the same workload (rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode KV GB/s (% HBM peak) + prefill TFLOPS (% MFMA peak), tokens/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+KERNEL_SOURCES = {
+    "decode_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
+    "mixed_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
+    "tiny_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
+    "mla_decode": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
+    "sparse_mla": "ragged_paged_attention_rpa_amd/csrc/sparse_mla.hip",
+}
+KERNEL_NAMES = {
+    "decode_gqa": "gqa_tile_kernel",
+    "mixed_gqa": "gqa_tile_kernel",
+    "tiny_gqa": "gqa_generic_kernel",
+    "mla_decode": "mla_tile_kernel",
+    "sparse_mla": "sparse_mla_kernel",
+}
+
+
+def source_sha(config):
+    """Hash of the dominant kernel's source plus the shared device header."""
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[config], "ragged_paged_attention_rpa_amd/csrc/rpa_device.h"):
+        p = os.path.join(ROOT, rel)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------ work counts --
+
+def gqa_work(case):
+    """Algorithmic work of one GQA call: visible (query, key) pairs and the
+    bytes of the distinct visible K/V rows each sequence must read."""
+    W = case.sliding_window or 0
+    Hq, Hkv, D = case.num_q_heads, case.num_kv_heads, case.head_dim
+    eb = case.kv_pages.element_size()
+    pairs = 0
+    kv_rows = 0
+    dec_rows = pre_pairs = 0
+    dec_bytes = pre_bytes = 0
+    for i in range(case.num_seqs):
+        ql = int(case.cu_q_lens[i + 1] - case.cu_q_lens[i])
+        L = int(case.kv_lens[i])
+        pos = np.arange(L - ql, L, dtype=np.int64)
+        vis = pos + 1 if W == 0 else np.minimum(pos + 1, W)
+        p = int(vis.sum())
+        lo = 0 if W == 0 else max(0, L - ql - W + 1)
+        rows = L - lo
+        pairs += p
+        kv_rows += rows
+        if ql == 1:
+            dec_rows += rows
+            dec_bytes += rows * 2 * Hkv * D * eb
+        else:
+            pre_pairs += p
+            pre_bytes += rows * 2 * Hkv * D * eb
+    return {
+        "kv_bytes": kv_rows * 2 * Hkv * D * eb,
+        "flops": pairs * Hq * 4 * D,
+        "q_tokens": int(case.cu_q_lens[case.num_seqs]),
+        "decode_kv_bytes": dec_bytes,
+        "prefill_flops": pre_pairs * Hq * 4 * D,
+        "prefill_kv_bytes": pre_bytes,
+    }
+
+
+def mla_work(case, heads, dl=512, dr=64):
+    """Visible (query, key) pairs x heads x (2*(dl+dr) for QK + 2*dl for PV);
+    bytes of the distinct latent rows read (dl + dr bf16 per key, pad excluded)."""
+    pairs = rows = 0
+    for i in range(case.num_seqs):
+        ql = int(case.cu_q_lens[i + 1] - case.cu_q_lens[i])
+        L = int(case.kv_lens[i])
+        pairs += int((np.arange(L - ql, L) + 1).sum())
+        rows += L
+    return {"kv_bytes": rows * (dl + dr) * 2, "flops": pairs * heads * (2 * (dl + dr) + 2 * dl),
+            "q_tokens": int(case.cu_q_lens[case.num_seqs])}
+
+
+def sparse_work(case):
+    S, H = case.q.shape[0], case.q.shape[1]
+    dk = case.kv_lora_rank + case.rope_dim
+    keys = 0
+    rb = case.read_block
+    for s in range(S):
+        u = case.indices[s]
+        u = u[u >= 0]
+        kp = (u[:, None] * rb + np.arange(rb)[None, :]).ravel()
+        keys += int(((kp <= case.positions[s]) & (kp < case.seq_len)).sum())
+    return {"gathered_bytes": keys * dk * 2, "flops": keys * H * 2 * (dk + case.kv_lora_rank),
+            "q_tokens": S}
+
+
+# --------------------------------------------------------------- runners --
+
+def _storage(t):
+    """(numpy storage array, oracle dtype code) of a torch tensor."""
+    import torch
+    import oracle
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.float32:
+        return t.numpy(), oracle.F32
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16), oracle.BF16
+    return t.view(torch.uint8).numpy(), oracle.FP8_E4M3
+
+
+class HipEvents:
+    """hipEvent_t pairs created through the HIP runtime (torch creates its
+    events lazily, so their handles are not usable before torch records them)."""
+
+    def __init__(self, n):
+        import ctypes
+        self._ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0
+            assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+
+    def elapsed_ms(self, k):
+        ms = self._ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self._ct.byref(ms), self.pairs[k][0], self.pairs[k][1])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+        self.pairs = []
+
+
+def timed_loop(torch, rpa, fn, steps, warmup):
+    """Runs `warmup` untimed steps, then exactly `steps` steps between two
+    device synchronisations; returns (wall ms/step, mean and median duration
+    of the dominant kernel in ms from the library's event hook)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = HipEvents(steps)
+    lib = rpa.load_library()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        lib.rpa_set_profile_events(ev.pairs[k][0], ev.pairs[k][1])
+        fn()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    lib.rpa_set_profile_events(None, None)
+    kern = [ev.elapsed_ms(k) for k in range(steps)]
+    ev.close()
+    return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), float(np.median(kern))
+
+
+def setup_gqa(torch, rpa, wl, config):
+    case = {"decode_gqa": wl.decode_gqa, "mixed_gqa": wl.mixed_gqa,
+            "tiny_gqa": wl.tiny_gqa}[config](device="cuda")
+    dev = "cuda"
+    kl = torch.from_numpy(case.kv_lens).to(dev)
+    pi = torch.from_numpy(case.page_indices).to(dev)
+    cu = torch.from_numpy(case.cu_q_lens).to(dev)
+    ns = torch.tensor([case.num_seqs], dtype=torch.int32, device=dev)
+    out = torch.empty_like(case.q)
+    need = rpa.rpa_workspace_size(kl, pi, case.q.shape[0], case.num_q_heads, case.num_kv_heads,
+                                  case.head_dim, case.page_size)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def fn():
+        rpa.rpa_forward(case.q, case.kv_pages, kl, pi, cu, ns, sm_scale=case.sm_scale,
+                        sliding_window=case.sliding_window, soft_cap=case.soft_cap,
+                        k_scale=case.k_scale, v_scale=case.v_scale, out=out, workspace=ws)
+    return case, fn
+
+
+def cpu_baseline_gqa(case, work, budget_s=15.0):
+    """Times the CPU oracle on a bounded sample of the workload's query tokens."""
+    import oracle
+    q, qd = _storage(case.q)
+    kv, kd = _storage(case.kv_pages)
+    T = int(case.cu_q_lens[case.num_seqs])
+    rng = np.random.default_rng(0)
+    order = rng.permutation(T)
+
+    def run(tokens):
+        t0 = time.perf_counter()
+        oracle.rpa(q, qd, kv, kd, case.kv_lens, case.page_indices, case.cu_q_lens, case.num_seqs,
+                   sm_scale=case.sm_scale, sliding_window=case.sliding_window,
+                   soft_cap=case.soft_cap, k_scale=case.k_scale, v_scale=case.v_scale,
+                   tokens=tokens)
+        return time.perf_counter() - t0
+
+    probe = np.sort(order[:max(1, min(T, 8))])
+    dt = run(probe)
+    n = int(min(T, max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
+    tokens = np.sort(order[:n])
+    dt = run(tokens)
+    # Work of the sampled tokens: their visible keys (bytes of K/V rows read,
+    # counted once per token) and their flops.
+    W = case.sliding_window or 0
+    seq_of = np.searchsorted(case.cu_q_lens[1:case.num_seqs + 1], tokens, side="right")
+    rows = 0
+    for t, i in zip(tokens, seq_of):
+        ql = int(case.cu_q_lens[i + 1] - case.cu_q_lens[i])
+        L = int(case.kv_lens[i])
+        pos = L - ql + (int(t) - int(case.cu_q_lens[i]))
+        rows += pos + 1 if W == 0 else min(pos + 1, W)
+    eb = case.kv_pages.element_size()
+    kv_bytes = rows * 2 * case.num_kv_heads * case.head_dim * eb
+    flops = rows * case.num_q_heads * 4 * case.head_dim
+    return {"seconds": dt, "tokens": len(tokens), "kv_bytes": kv_bytes, "flops": flops,
+            "cores": oracle.num_threads(),
+            "sample": f"{len(tokens)} of {T} query tokens (all q heads), drawn with seed 0"}
+
+
+def load_traffic(config):
+    """Per-launch HBM bytes of the dominant kernel from the committed PMC
+    summary, if it was measured on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha") != source_sha(config):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def bench_gqa(args, torch, rpa, wl):
+    case, fn = setup_gqa(torch, rpa, wl, args.config)
+    work = gqa_work(case)
+    ms, kern_mean, kern_med = timed_loop(torch, rpa, fn, args.steps, args.warmup)
+    step_s = ms / 1e3
+    kern_s = kern_mean / 1e3
+    res = {"ms_per_step": ms, "kernel_ms_mean": kern_mean, "kernel_ms_median": kern_med,
+           "q_tokens": work["q_tokens"], "tokens_per_s": work["q_tokens"] / step_s}
+    traffic = load_traffic(args.config)
+    if args.config == "decode_gqa" or args.config == "tiny_gqa":
+        gbs = work["kv_bytes"] / step_s / 1e9
+        res.update(value=gbs, unit="GB/s", pct_hbm_peak=100 * gbs / HBM_PEAK_GBS)
+        ach = work["kv_bytes"] / kern_s / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                           "algorithmic_bytes_per_launch": work["kv_bytes"]}
+    else:  # mixed: report against the combined roof of the whole launch
+        tf = work["flops"] / step_s / 1e12
+        res.update(value=tf, unit="TFLOP/s", pct_mfma_peak=100 * tf / BF16_PEAK_TFLOPS,
+                   kv_gbs=work["kv_bytes"] / step_s / 1e9)
+        roof_s = max(work["flops"] / (BF16_PEAK_TFLOPS * 1e12), work["kv_bytes"] / (HBM_PEAK_GBS * 1e9))
+        ach = work["flops"] / kern_s / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": traffic,
+                           "algorithmic_flops_per_launch": work["flops"],
+                           "combined_roof_us": roof_s * 1e6,
+                           "frac_of_combined_roof": roof_s / kern_s}
+    res["work"] = work
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline_gqa(case, work, args.cpu_budget)
+        if res["unit"] == "GB/s":
+            v, unit = cb["kv_bytes"] / cb["seconds"] / 1e9, "GB/s"
+        else:
+            v, unit = cb["flops"] / cb["seconds"] / 1e12, "TFLOP/s"
+        res["cpu_baseline"] = {"value": v, "unit": unit, "cores": cb["cores"], "kind": "oracle",
+                               "sample": cb["sample"], "seconds": cb["seconds"],
+                               "tokens_per_s": cb["tokens"] / cb["seconds"]}
+    cfg = {"decode_gqa": {"workload": "decode_gqa", "num_seqs": 128, "q_len": 1,
+                          "kv_len": "U[512,8192]", "q_heads": 32, "kv_heads": 8, "head_dim": 128,
+                          "page_size": 16, "kv_dtype": "bf16"},
+           "mixed_gqa": {"workload": "mixed_gqa", "decodes": 120, "prefill_chunks": 8,
+                         "q_heads": 32, "kv_heads": 8, "head_dim": 128, "page_size": 16,
+                         "kv_dtype": "fp8_e4m3fn", "sliding_window": 4096, "soft_cap": 50},
+           "tiny_gqa": {"workload": "tiny_gqa", "num_seqs": 3, "dtype": "fp32"}}[args.config]
+    return res, cfg
+
+
+def bench_latent(args, torch, rpa, wl):
+    raise SystemExit(f"--config {args.config}: not wired yet")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode_gqa",
+                    choices=["decode_gqa", "mixed_gqa", "tiny_gqa", "mla_decode", "sparse_mla"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="target seconds of oracle CPU work for cpu_baseline")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many bytes "
+                         "(calibration run for the PMC byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the path has no multi-GPU part; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import ragged_paged_attention_rpa_amd as rpa
+    from ragged_paged_attention_rpa_amd import workloads as wl
+    rpa.load_library()
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4}))
+        return
+    if args.config in ("decode_gqa", "mixed_gqa", "tiny_gqa"):
+        res, cfg = bench_gqa(args, torch, rpa, wl)
+    else:
+        res, cfg = bench_latent(args, torch, rpa, wl)
+    line = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if args.config != "tiny_gqa" else "f32", "data": "synthetic",
+            "config": cfg}
+    line.update(res)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -124,6 +124,16 @@ void rpa_opts_init(rpa_opts* opts);
 const char* rpa_last_error(void);
 
 /*
+ * Profiling hook for benchmarks. `start` and `stop` are hipEvent_t handles
+ * created by the caller (NULL, NULL turns the hook off). While set, each
+ * rpa_forward / mla_rpa_forward / sparse_mla_forward call on this host thread
+ * records `start` on its stream right before its main attention kernel and
+ * `stop` right after it, so hipEventElapsedTime(start, stop) is that kernel's
+ * duration. The library does not own or destroy the events.
+ */
+void rpa_set_profile_events(void* start, void* stop);
+
+/*
  * Workspace bytes rpa_forward needs for these capacities (host-only query;
  * depends only on capacities, never on device values).
  */

@@ -71,6 +71,8 @@ def _load():
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                          c_void_p, c_void_p, c_int, c_void_p, c_int,
                                          c_void_p, c_int]
+        lib.oracle_num_threads.restype = c_int
+        lib.oracle_num_threads.argtypes = []
         lib.oracle_decode_bf16.restype = c_double
         lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
         lib.oracle_decode_e4m3fn.restype = c_double
@@ -239,6 +241,11 @@ def kv_update(layout, new_a, new_b, cache_a, cache_b, dtype, *, kv_lens=None,
         dim_a, dim_b, stride_a, stride_b, _ptr(kv_lens), _ptr(pi), pps, _ptr(cu_q_lens),
         int(num_seqs), _ptr(sl), T)
     _check(rc, "kv_update")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 def decode_bf16(bits: int) -> float:

@@ -36,6 +36,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2 };
 enum { OR_LAYOUT_COMBINED_GQA = 0, OR_LAYOUT_MLA_SPLIT = 1, OR_LAYOUT_MLA_FUSED = 2 };
@@ -428,6 +431,15 @@ int oracle_kv_update(int layout, const void* new_a, const void* new_b, void* cac
     }
   }
   return 0;
+}
+
+/* Threads an OpenMP region of this library uses (for reporting). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
 }
 
 /* Decoders exported for the pins (tests check them against the format

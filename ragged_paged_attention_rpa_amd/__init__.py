@@ -27,7 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librpa.so")
 
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
-EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_workspace_size", "rpa_forward",
+EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_set_profile_events",
+                    "rpa_workspace_size", "rpa_forward",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
                     "sparse_mla_workspace_size", "sparse_mla_forward")
 
@@ -77,6 +78,8 @@ def load_library():
     lib.rpa_opts_init.restype = None
     lib.rpa_last_error.argtypes = []
     lib.rpa_last_error.restype = ctypes.c_char_p
+    lib.rpa_set_profile_events.argtypes = [P, P]
+    lib.rpa_set_profile_events.restype = None
     lib.rpa_workspace_size.argtypes = [MP, I32, I32, I32, I32]
     lib.rpa_workspace_size.restype = SZ
     lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P, SZ, P]
@@ -168,6 +171,18 @@ def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_valid
     o.v_scale = float(1.0 if v_scale is None else v_scale)
     o.debug_validate = 1 if debug_validate else 0
     return o
+
+
+def set_profile_events(start, stop):
+    """Records the hipEvent_t handles ``start``/``stop`` (ints or c_void_p, created
+    with hipEventCreate) around the main kernel of the following calls on this
+    thread; ``None, None`` turns the hook off."""
+    lib = load_library()
+    if start is None or stop is None:
+        lib.rpa_set_profile_events(None, None)
+    else:
+        lib.rpa_set_profile_events(ctypes.c_void_p(int(getattr(start, "value", start))),
+                                   ctypes.c_void_p(int(getattr(stop, "value", stop))))
 
 
 def rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_q_heads, num_kv_heads,

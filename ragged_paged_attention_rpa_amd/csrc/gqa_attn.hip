@@ -698,12 +698,14 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   while ((1 << ps_log2) < a.page_size) ++ps_log2;
   hipLaunchKernelGGL(gqa_plan_kernel, dim3(1), dim3(kThreads), 0, stream, a);
   const int grid = max(1, min(a.tile_capacity, num_cus() * 4));
+  prof_begin(stream);
   if (a.kv_dtype == DT_BF16)
     hipLaunchKernelGGL(gqa_tile_kernel<DT_BF16>, dim3(grid), dim3(kThreads), 0, stream, a,
                        ps_log2);
   else
     hipLaunchKernelGGL(gqa_tile_kernel<DT_FP8>, dim3(grid), dim3(kThreads), 0, stream, a,
                        ps_log2);
+  prof_end(stream);
   if (a.geo.qdec > 0)
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(a.max_num_seqs * a.num_kv_heads), dim3(kThreads),
                        0, stream, a);
@@ -712,8 +714,10 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
 
 hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream) {
   if (a.max_num_tokens <= 0) return hipSuccess;
+  prof_begin(stream);
   hipLaunchKernelGGL(gqa_generic_kernel, dim3(a.max_num_tokens, a.num_q_heads), dim3(64), 0,
                      stream, a);
+  prof_end(stream);
   return hipGetLastError();
 }
 

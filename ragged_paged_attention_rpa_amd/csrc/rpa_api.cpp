@@ -21,6 +21,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
 
 rpa_status fail(rpa_status st, const char* fmt, ...) {
   char buf[512];
@@ -136,7 +138,26 @@ rpa_status validate_values(const rpa_ragged_meta* m, const HostMeta& h, int page
 
 }  // namespace
 
+namespace rpa {
+void prof_begin(hipStream_t stream) {
+  if (g_prof_start) (void)hipEventRecord(g_prof_start, stream);
+}
+void prof_end(hipStream_t stream) {
+  if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
+}
+}  // namespace rpa
+
 extern "C" {
+
+void rpa_set_profile_events(void* start, void* stop) {
+  if (start && stop) {
+    g_prof_start = reinterpret_cast<hipEvent_t>(start);
+    g_prof_stop = reinterpret_cast<hipEvent_t>(stop);
+  } else {
+    g_prof_start = nullptr;
+    g_prof_stop = nullptr;
+  }
+}
 
 void rpa_opts_init(rpa_opts* o) {
   if (!o) return;

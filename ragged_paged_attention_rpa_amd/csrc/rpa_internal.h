@@ -8,6 +8,11 @@
 
 namespace rpa {
 
+// Records the caller's profiling events (rpa_set_profile_events) around the
+// main kernel of an entry point; no-ops when the hook is off.
+void prof_begin(hipStream_t stream);
+void prof_end(hipStream_t stream);
+
 // ---------------------------------------------------------------- update ----
 struct KvUpdateArgs {
   int layout;  // 0 combined GQA, 1 MLA split, 2 MLA fused
