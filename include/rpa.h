@@ -228,7 +228,8 @@ size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t
  * Query s attends the multiset of keys u*RB + r (u = indices[s,k] >= 0, r < RB)
  * with u*RB + r <= positions[s] and < seq_len; a unit listed twice counts twice;
  * an empty set gives zeros. sm_scale is required (> 0, finite).
- * Requires read_block % 16 == 0 and page_size % read_block == 0.
+ * Requires read_block % 16 == 0 and page_size % read_block == 0; this build
+ * handles top_k <= 256 units per query (RPA_E_UNSUPPORTED above).
  * Logical pages at or past ptw are clamped to ptw-1 for the address and masked.
  */
 rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t* page_table,

@@ -454,6 +454,9 @@ rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t
                 num_queries, num_heads, top_k);
   if (read_block <= 0 || read_block % 16 != 0)
     return fail(RPA_E_INVALID, "read_block=%d must be a positive multiple of 16", read_block);
+  if (top_k > 256)
+    return fail(RPA_E_UNSUPPORTED, "top_k=%d selected units per query; this build handles up to 256",
+                top_k);
   if (page_size <= 0 || page_size % read_block != 0)
     return fail(RPA_E_INVALID, "page_size=%d must be a multiple of read_block=%d", page_size, read_block);
   if (kv_lora_rank != 512 || rope_dim != 64)

@@ -32,9 +32,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return u >> 16;
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a).
+typedef __bf16 bf16x2_t __attribute__((__vector_size__(2 * sizeof(__bf16))));
+
+// Two fp32 -> packed pair of bf16 (low half = a), round to nearest even, with
+// gfx950's v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+  const floatx2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Four OCP E4M3FN bytes of `w` -> four fp32 (exact; the hardware converter
@@ -89,6 +93,70 @@ __device__ __forceinline__ float wave_sum_xor(float v, int mask) {
 }
 
 __device__ __forceinline__ int cdiv_i(int a, int b) { return (a + b - 1) / b; }
+
+// Online softmax with a lazily moved reference max (log2 domain). Weights are
+// p = 2^(s - m_ref); the reference only moves (and the accumulators are
+// rescaled by 2^(m_ref_old - m_ref_new)) when a block's row max exceeds it by
+// more than kLazyTau, so p <= 2^kLazyTau and most blocks skip the rescale.
+constexpr float kLazyTau = 8.0f;
+
+__device__ __forceinline__ bool wave_any(bool v) {
+  return __builtin_amdgcn_ballot_w64(v) != 0;
+}
+
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
+
+// D(16x16 f32) += A(16x16 bf16) * B(16x16 bf16); lane l holds A[l%16][4*(l/16)+i],
+// B[4*(l/16)+i][l%16] (i = 0..3) and D as for mfma_16x16x32.
+__device__ __forceinline__ floatx4 mfma_16x16x16(const u32x2& a, const u32x2& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                    __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+}
+
+// ---- LDS direct loads and explicit synchronisation -------------------------
+// One global_load_lds_dwordx4: lane L's 16 bytes at `gaddr` land in LDS at
+// lds_base + 16*L, where lds_base (a byte address, wave-uniform) goes in M0.
+// Issued through inline asm so the compiler's wait-count pass does not treat
+// it as an LDS store and add waits before unrelated LDS reads; callers wait
+// with wait_vmcnt<N>() (vector-memory ops complete in issue order).
+__device__ __forceinline__ void dma_b128(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gaddr)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Compiler-only fence: memory accesses are not moved across it. Used to keep
+// the scheduler from hoisting a whole unrolled loop's LDS loads at once.
+__device__ __forceinline__ void sched_fence() { asm volatile("" : : : "memory"); }
+
+// Workgroup barrier without the fence __syncthreads() carries (that fence
+// would drain outstanding LDS DMA); also a compiler barrier for memory.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+      (__attribute__((address_space(3))) char*)(uintptr_t)addr);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group the four lanes 4r..4r+3 name
+// row r (4 consecutive b16 each); lane j of the group receives column j of the
+// 4x16 block, i.e. element j of rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
+  shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
 
 // Largest i in [0, n) with cu[i] <= t (the sequence owning packed token t),
 // or -1 when t is past cu[n].

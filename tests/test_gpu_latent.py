@@ -1,0 +1,174 @@
+"""GPU parity of mla_rpa_forward (scatter + attention) and sparse_mla_forward
+against the CPU oracle. bf16 tolerances: max-abs 2e-2, mean-abs 2e-3."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ragged_paged_attention_rpa_amd as rpa
+from ragged_paged_attention_rpa_amd import workloads as wl
+from tests.helpers import as_f64, assert_close, storage
+
+pytestmark = pytest.mark.gpu
+TOL = (2e-2, 2e-3)
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _meta(c):
+    d = "cuda"
+    return (torch.from_numpy(c.kv_lens).to(d), torch.from_numpy(c.page_indices).to(d),
+            torch.from_numpy(c.cu_q_lens).to(d),
+            torch.tensor([c.num_seqs], dtype=torch.int32, device=d))
+
+
+def _mla_gpu(c, update=True):
+    kl, pi, cu, ns = _meta(c)
+    out = rpa.mla_rpa_forward(c.ql_nope, c.q_pe, c.new_kv_c if update else None,
+                              c.new_k_pe if update else None, c.cache_kv_c, c.cache_k_pe, kl, pi,
+                              cu, ns, sm_scale=c.sm_scale, sliding_window=c.sliding_window,
+                              soft_cap=c.soft_cap)
+    torch.cuda.synchronize()
+    return out
+
+
+def _mla_oracle(c, ckv, ckp, tokens=None):
+    return oracle.mla(storage(c.ql_nope)[0], storage(c.q_pe)[0], oracle.BF16, ckv, ckp, c.kv_lens,
+                      c.page_indices, c.cu_q_lens, c.num_seqs, sm_scale=c.sm_scale,
+                      sliding_window=c.sliding_window, soft_cap=c.soft_cap, tokens=tokens)
+
+
+def _host_caches_after_update(c):
+    ckv = storage(c.cache_kv_c)[0].copy()
+    ckp = storage(c.cache_k_pe)[0].copy()
+    oracle.kv_update(oracle.LAYOUT_MLA_SPLIT, storage(c.new_kv_c)[0], storage(c.new_k_pe)[0], ckv,
+                     ckp, oracle.BF16, kv_lens=c.kv_lens, page_indices=c.page_indices,
+                     cu_q_lens=c.cu_q_lens, num_seqs=c.num_seqs)
+    return ckv, ckp
+
+
+MLA_CASES = [
+    # (seqs, heads, page_size, window, cap, name)
+    ([(1, 100), (1, 2000), (1, 1), (1, 64), (1, 65)], 128, 64, None, None, "decode-h128"),
+    ([(3, 300), (1, 777), (5, 64), (2, 2)], 16, 64, None, None, "ragged-h16"),
+    ([(1, 5000), (4, 1300), (1, 129)], 128, 16, 700, None, "page16-window"),
+    ([(2, 400), (1, 3000)], 40, 32, None, 30.0, "h40-cap"),
+    ([(1, 900), (2, 150)], 130, 64, None, None, "h130-two-groups"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MLA_CASES)), ids=[c[-1] for c in MLA_CASES])
+def test_mla_update_and_attention(idx):
+    seqs, H, ps, window, cap, name = MLA_CASES[idx]
+    _say(f"mla {name}")
+    c = wl.make_mla(seqs, num_heads=H, page_size=ps, seed=200 + idx, device="cuda",
+                    sliding_window=window, soft_cap=cap, name=name)
+    ckv, ckp = _host_caches_after_update(c)
+    got = _mla_gpu(c)
+    # The scatter must land bit-exactly in both caches.
+    assert np.array_equal(storage(c.cache_kv_c)[0], ckv)
+    assert np.array_equal(storage(c.cache_k_pe)[0], ckp)
+    want = _mla_oracle(c, ckv, ckp)
+    n = int(c.cu_q_lens[c.num_seqs])
+    assert_close(as_f64(got)[:n], want[:n], *TOL, what=name)
+
+
+def test_mla_attention_only_and_determinism():
+    _say("mla attention only")
+    c = wl.make_mla([(1, 3000), (1, 17), (2, 600)], num_heads=128, page_size=64, seed=210,
+                    device="cuda")
+    a = _mla_gpu(c, update=False).clone()
+    b = _mla_gpu(c, update=False)
+    assert torch.equal(a, b)
+    want = _mla_oracle(c, storage(c.cache_kv_c)[0], storage(c.cache_k_pe)[0])
+    assert_close(as_f64(a)[:4], want[:4], *TOL)
+
+
+def test_mla_decode_full_size_sampled():
+    _say("mla_decode full size (64 seqs, kv 4096..32768, 128 heads), sampled tokens")
+    c = wl.mla_decode(device="cuda")
+    ckv, ckp = _host_caches_after_update(c)
+    got = _mla_gpu(c)
+    tokens = np.arange(0, 64, 6)
+    want = _mla_oracle(c, ckv, ckp, tokens=tokens)
+    assert_close(as_f64(got)[tokens], want[tokens], *TOL, what="mla_decode")
+
+
+# ------------------------------------------------------------------ sparse --
+
+def _sparse_gpu(c, indices=None):
+    d = "cuda"
+    idx = torch.from_numpy(c.indices if indices is None else indices).to(d)
+    out = rpa.sparse_mla_forward(c.q, c.kv_cache, torch.from_numpy(c.page_table).to(d), idx,
+                                 torch.from_numpy(c.positions).to(d), seq_len=c.seq_len,
+                                 read_block=c.read_block, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _sparse_oracle(c, indices=None, queries=None):
+    return oracle.sparse_mla(storage(c.q)[0], oracle.BF16, storage(c.kv_cache)[0], c.page_table,
+                             c.indices if indices is None else indices, c.positions,
+                             seq_len=c.seq_len, read_block=c.read_block, sm_scale=c.sm_scale,
+                             queries=queries)
+
+
+SPARSE_CASES = [
+    # (T, S, H, K, ps, RB, seq_len_cut, name)
+    (2048, 48, 16, 8, 64, 64, 0, "page-units"),
+    (2048, 40, 20, 12, 64, 32, 0, "h20-rb32"),
+    (1500, 30, 8, 40, 128, 64, 300, "seq-len-cut"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SPARSE_CASES)), ids=[c[-1] for c in SPARSE_CASES])
+def test_sparse_small(idx):
+    T, S, H, K, ps, RB, cut, name = SPARSE_CASES[idx]
+    _say(f"sparse {name}")
+    rng = np.random.default_rng(300 + idx)
+    pos = np.sort(rng.integers(0, T, S)).astype(np.int32)
+    c = wl.make_sparse(T=T, S=S, H=H, K=K, page_size=ps, read_block=RB, seed=300 + idx,
+                       device="cuda", positions=pos, pad_frac=0.3, name=name)
+    if cut:
+        c.seq_len = T - cut
+    idx_arr = c.indices.copy()
+    idx_arr[0, -1] = idx_arr[0, 0]     # a repeated unit counts twice
+    idx_arr[1, :] = -1                 # empty selection -> zeros
+    got = as_f64(_sparse_gpu(c, idx_arr))
+    want = _sparse_oracle(c, idx_arr)
+    assert np.all(got[1] == 0.0)
+    assert_close(got, want, *TOL, what=name)
+
+
+def test_sparse_nan_outside_selection_is_never_read():
+    _say("sparse nan hygiene")
+    c = wl.make_sparse(T=1024, S=16, H=16, K=4, seed=320, device="cuda")
+    clean = _sparse_gpu(c).clone()
+    # Poison every page row that no selected, causal key of any query reads.
+    used = np.zeros(c.kv_cache.shape[0] * 64, dtype=bool)
+    for s in range(16):
+        for u in c.indices[s]:
+            if u < 0:
+                continue
+            for r in range(64):
+                kp = u * 64 + r
+                if kp <= c.positions[s] and kp < c.seq_len:
+                    used[c.page_table[kp // 64] * 64 + kp % 64] = True
+    flat = c.kv_cache.view(-1, c.kv_cache.shape[2])
+    flat[torch.from_numpy(~used).cuda()] = float("nan")
+    dirty = _sparse_gpu(c)
+    assert torch.isfinite(dirty).all()
+    assert torch.equal(dirty, clean)
+
+
+def test_sparse_full_size_sampled():
+    _say("sparse_mla full size (4096 queries x 32 units x 64 tokens), sampled queries")
+    c = wl.sparse_mla(device="cuda")
+    got = as_f64(_sparse_gpu(c))
+    qs = np.arange(0, 4096, 97)
+    want = _sparse_oracle(c, queries=qs)
+    assert_close(got[qs], want[qs], *TOL, what="sparse_mla")
