@@ -320,8 +320,115 @@ def bench_gqa(args, torch, rpa, wl):
     return res, cfg
 
 
+def _budgeted(run, order, budget_s, probe_n=2):
+    """Runs run(sample) on a probe, then on a sample sized for ~budget_s."""
+    probe = np.sort(order[:max(1, min(len(order), probe_n))])
+    dt = run(probe)
+    n = int(min(len(order), max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
+    sample = np.sort(order[:n])
+    return sample, run(sample)
+
+
 def bench_latent(args, torch, rpa, wl):
-    raise SystemExit(f"--config {args.config}: not wired yet")
+    import oracle
+    dev = "cuda"
+    if args.config == "mla_decode":
+        case = wl.mla_decode(device=dev)
+        kl = torch.from_numpy(case.kv_lens).to(dev)
+        pi = torch.from_numpy(case.page_indices).to(dev)
+        cu = torch.from_numpy(case.cu_q_lens).to(dev)
+        ns = torch.tensor([case.num_seqs], dtype=torch.int32, device=dev)
+        out = torch.empty_like(case.ql_nope)
+        H = case.ql_nope.shape[1]
+        need = rpa.mla_rpa_workspace_size(kl, pi, case.ql_nope.shape[0], H, 512, case.page_size)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def fn(update=True):
+            rpa.mla_rpa_forward(case.ql_nope, case.q_pe, case.new_kv_c if update else None,
+                                case.new_k_pe if update else None, case.cache_kv_c,
+                                case.cache_k_pe, kl, pi, cu, ns, sm_scale=case.sm_scale, out=out,
+                                workspace=ws)
+        work = mla_work(case, H)
+        ms, kmean, kmed = timed_loop(torch, rpa, fn, args.steps, args.warmup)
+        ms_attn, _, _ = timed_loop(torch, rpa, lambda: fn(False), args.steps, args.warmup)
+        gbs = work["kv_bytes"] / (ms / 1e3) / 1e9
+        ach = work["kv_bytes"] / (kmean / 1e3) / 1e9
+        res = {"value": gbs, "unit": "GB/s", "ms_per_step": ms, "kernel_ms_mean": kmean,
+               "kernel_ms_median": kmed, "ms_per_step_attention_only": ms_attn,
+               "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
+               "tokens_per_s": work["q_tokens"] / (ms / 1e3),
+               "mfma_tflops_in_kernel": work["flops"] / (kmean / 1e3) / 1e12,
+               "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic(args.config),
+                            "algorithmic_bytes_per_launch": work["kv_bytes"]},
+               "work": work}
+        if not args.no_cpu_baseline:
+            ckv, _ = _storage(case.cache_kv_c)
+            ckp, _ = _storage(case.cache_k_pe)
+            ql, d = _storage(case.ql_nope)
+            qp, _ = _storage(case.q_pe)
+
+            def run(tokens):
+                t0 = time.perf_counter()
+                oracle.mla(ql, qp, d, ckv, ckp, case.kv_lens, case.page_indices, case.cu_q_lens,
+                           case.num_seqs, sm_scale=case.sm_scale, tokens=tokens)
+                return time.perf_counter() - t0
+            order = np.random.default_rng(0).permutation(work["q_tokens"])
+            toks, dt = _budgeted(run, order, args.cpu_budget, 1)
+            kvb = int(sum(int(case.kv_lens[t]) for t in toks)) * 1152
+            res["cpu_baseline"] = {"value": kvb / dt / 1e9, "unit": "GB/s",
+                                   "cores": oracle.num_threads(), "kind": "oracle",
+                                   "sample": f"{len(toks)} of {work['q_tokens']} decode tokens "
+                                             "(all 128 heads), drawn with seed 0",
+                                   "seconds": dt, "tokens_per_s": len(toks) / dt}
+        cfg = {"workload": "mla_decode", "num_seqs": 64, "q_len": 1, "kv_len": "U[4096,32768]",
+               "heads": 128, "kv_lora_rank": 512, "rope_dim": 64, "page_size": 64,
+               "dtype": "bf16", "includes_kv_cache_update": True}
+        return res, cfg
+    # sparse_mla
+    case = wl.sparse_mla(device=dev)
+    pt = torch.from_numpy(case.page_table).to(dev)
+    idx = torch.from_numpy(case.indices).to(dev)
+    pos = torch.from_numpy(case.positions).to(dev)
+    out = torch.empty((case.q.shape[0], case.q.shape[1], 512), dtype=torch.float32, device=dev)
+
+    def fn():
+        rpa.sparse_mla_forward(case.q, case.kv_cache, pt, idx, pos, seq_len=case.seq_len,
+                               read_block=case.read_block, sm_scale=case.sm_scale, out=out)
+    work = sparse_work(case)
+    ms, kmean, kmed = timed_loop(torch, rpa, fn, args.steps, args.warmup)
+    tf = work["flops"] / (ms / 1e3) / 1e12
+    ach = work["flops"] / (kmean / 1e3) / 1e12
+    res = {"value": tf, "unit": "TFLOP/s", "ms_per_step": ms, "kernel_ms_mean": kmean,
+           "kernel_ms_median": kmed, "pct_mfma_peak": 100 * tf / BF16_PEAK_TFLOPS,
+           "gathered_gbs_in_kernel": work["gathered_bytes"] / (kmean / 1e3) / 1e9,
+           "tokens_per_s": work["q_tokens"] / (ms / 1e3),
+           "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                        "traffic": load_traffic(args.config),
+                        "algorithmic_flops_per_launch": work["flops"]},
+           "work": work}
+    if not args.no_cpu_baseline:
+        q, d = _storage(case.q)
+        kv, _ = _storage(case.kv_cache)
+
+        def run(qs):
+            t0 = time.perf_counter()
+            oracle.sparse_mla(q, d, kv, case.page_table, case.indices, case.positions,
+                              seq_len=case.seq_len, read_block=case.read_block,
+                              sm_scale=case.sm_scale, queries=qs)
+            return time.perf_counter() - t0
+        order = np.random.default_rng(0).permutation(q.shape[0])
+        qs, dt = _budgeted(run, order, args.cpu_budget, 2)
+        flops = work["flops"] * len(qs) / q.shape[0]
+        res["cpu_baseline"] = {"value": flops / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": f"{len(qs)} of {q.shape[0]} queries (all 16 heads), "
+                                         "drawn with seed 0; flops scaled by the sample share",
+                               "seconds": dt, "tokens_per_s": len(qs) / dt}
+    cfg = {"workload": "sparse_mla", "seq_tokens": 65536, "queries": 4096, "heads": 16,
+           "top_k_units": 32, "read_block": 64, "page_size": 64, "dtype": "bf16"}
+    return res, cfg
 
 
 def main():

@@ -28,12 +28,9 @@ namespace {
 constexpr int kD = 128;                   // head dim of the MFMA path
 constexpr int kBN = 64;                   // keys per LDS block
 constexpr int kThreads = 256;             // 4 waves
-constexpr int kKStride = kD * 2 + 16;     // LDS bytes per key row of K (padded)
-constexpr int kVStride = kBN * 2 + 8;     // LDS bytes per dim row of V^T (padded)
-constexpr int kKBytes = kBN * kKStride;   // 17408
-constexpr int kVBytes = kD * kVStride;    // 17408
 constexpr int kPartRows = 16;             // rows of a decode-class tile
 constexpr int kNegBig = -1000000000;
+constexpr int kMaxSplits = 16;            // cap on splits of one decode sequence
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
@@ -164,27 +161,43 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
   __syncthreads();
   const int total = min(run_pre + run_dec, a.tile_capacity);
   const int H = a.num_kv_heads;
-  for (int t = tid; t < total; t += kThreads) {
-    Tile tl;
-    if (t < run_pre) {
-      const int seq = upper_bound_seq(pre_off, ns, t);
-      const int q_len = a.cu_q_lens[seq + 1] - a.cu_q_lens[seq];
-      const int nqb = cdiv_i(q_len, a.geo.bq);
-      const int local = t - pre_off[seq];
-      tl.seq = seq;
-      tl.kvh = local / nqb;
-      tl.qtok0 = (local % nqb) * a.geo.bq;
-      tl.split = -1;
-    } else {
-      const int u = t - run_pre;
-      const int seq = upper_bound_seq(dec_off, ns, u);
-      const int local = u - dec_off[seq];
-      tl.seq = seq;
-      tl.kvh = local % H;
-      tl.qtok0 = 0;
-      tl.split = local / H;
+  // Each thread writes one contiguous range of tiles: one search for its
+  // first tile, then the owning sequence advances as the offsets are passed.
+  const int per = (total + kThreads - 1) / kThreads;
+  const int t0 = min(total, tid * per);
+  const int t1 = min(total, t0 + per);
+  if (t0 < t1) {
+    int seq = -1, seq_begin = 0, seq_end = 0, nqb = 1;
+    for (int t = t0; t < t1; ++t) {
+      Tile tl;
+      if (t < run_pre) {
+        if (seq < 0 || t >= seq_end) {
+          seq = upper_bound_seq(pre_off, ns, t);
+          seq_begin = pre_off[seq];
+          seq_end = pre_off[seq + 1];
+          const int q_len = a.cu_q_lens[seq + 1] - a.cu_q_lens[seq];
+          nqb = cdiv_i(q_len, a.geo.bq);
+        }
+        const int local = t - seq_begin;
+        tl.seq = seq;
+        tl.kvh = local / nqb;
+        tl.qtok0 = (local % nqb) * a.geo.bq;
+        tl.split = -1;
+      } else {
+        const int u = t - run_pre;
+        if (seq < 0 || t == run_pre || u >= seq_end) {  // first decode tile or next sequence
+          seq = upper_bound_seq(dec_off, ns, u);
+          seq_begin = dec_off[seq];
+          seq_end = dec_off[seq + 1];
+        }
+        const int local = u - seq_begin;
+        tl.seq = seq;
+        tl.kvh = local % H;
+        tl.qtok0 = 0;
+        tl.split = local / H;
+      }
+      a.tiles[t] = tl;
     }
-    a.tiles[t] = tl;
   }
   if (tid == 0) {
     a.counters[0] = total;
@@ -193,147 +206,129 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
 }
 
 // ------------------------------------------------------------ tile kernel --
+//
+// Keys move through LDS in blocks of 64, one key per lane of a DMA
+// instruction (global_load_lds_dwordx4), so a block is stored chunk-major:
+// column c holds 16 bytes of every key. bf16 pools give 32 columns per key
+// (K dims 8c..8c+7 in columns 0..15, V dims in 16..31); fp8 pools give 16 raw
+// columns that a conversion pass widens into the same bf16 layout. Odd
+// columns rotate the keys by four slots and columns are padded to 1088 bytes,
+// which keeps both MFMA operand reads free of LDS bank conflicts.
+//
+// Two compute modes share the block pipeline:
+//  * rows <= 16 (decode): every wave takes the same rows and one 16-key tile
+//    of each block, keeping its own softmax state; the four states are merged
+//    in LDS at the end;
+//  * rows > 16 (prefill): wave w takes rows 16w .. 16w+15 against all 64 keys.
 
-// Register staging of one 64-key block of K and V rows of one kv head.
-// bf16: 32 lanes per key (16 B each, 512 B = K row then V row), 8 steps.
-// fp8:  16 lanes per key (16 B each, 256 B), 4 steps.
+constexpr int kCols = 32;                     // bf16 columns per key (K + V)
+constexpr int kRawCols = 16;                  // fp8 columns per key (K + V)
+constexpr int kColStride = kBN * 16 + 64;     // 1088 bytes per column
+constexpr int kStageBytes = kCols * kColStride;       // 34816
+constexpr int kRawStageBytes = kRawCols * kColStride; // 17408
+constexpr int kPageWin = 512;                 // page ids of the tile cached in LDS
+
+__device__ __attribute__((aligned(16))) const uint8_t kZeroKV[512] = {0};
+
 template <int KV_DT>
-struct KvStage {
-  static constexpr int kLanesPerKey = KV_DT == DT_BF16 ? 32 : 16;
-  static constexpr int kKeysPerStep = kThreads / kLanesPerKey;
-  static constexpr int kSteps = kBN / kKeysPerStep;
-  u32x4 buf[kSteps];
+struct TileSmem {
+  // bf16: two DMA stages. fp8: two raw DMA stages plus one converted stage.
+  char stage[KV_DT == DT_BF16 ? 2 * kStageBytes : 2 * kRawStageBytes + kStageBytes];
+  int pages[kPageWin];
+  int tile;
 };
 
-template <int KV_DT>
-__device__ __forceinline__ void stage_load(KvStage<KV_DT>& st, const GqaArgs& a, int seq, int kvh,
-                                           int kb, int lo, int hi, int ps_log2) {
-  constexpr int LPK = KvStage<KV_DT>::kLanesPerKey;
-  constexpr int KPS = KvStage<KV_DT>::kKeysPerStep;
-  const int tid = threadIdx.x;
-  const int kk = tid / LPK;
-  const int c = tid % LPK;
-  const int eb = KV_DT == DT_BF16 ? 2 : 1;
-  const int64_t token_stride = (int64_t)2 * a.num_kv_heads * kD * eb;  // bytes per token row
-  const char* kv = (const char*)a.kv;
-  const int32_t* table = a.page_indices + (int64_t)seq * a.pages_per_seq;
-#pragma unroll
-  for (int s = 0; s < KvStage<KV_DT>::kSteps; ++s) {
-    const int key = kb + s * KPS + kk;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (key >= lo && key < hi) {
-      const int page = table[key >> ps_log2];
-      if (page >= 0 && page < a.total_num_pages) {
-        const int64_t row = ((int64_t)page << ps_log2) + (key & ((1 << ps_log2) - 1));
-        const char* p = kv + row * token_stride + (int64_t)(2 * kvh) * kD * eb + c * 16;
-        v = *reinterpret_cast<const u32x4*>(p);
-      }
-    }
-    st.buf[s] = v;
-  }
+__device__ __forceinline__ uint32_t col_slot(int key, int c) {
+  return (uint32_t)(c * kColStride + (((key + 4 * (c & 1)) & (kBN - 1)) << 4));
 }
 
-template <int KV_DT>
-__device__ __forceinline__ void stage_store(const KvStage<KV_DT>& st, char* k_lds, char* v_lds) {
-  constexpr int LPK = KvStage<KV_DT>::kLanesPerKey;
-  constexpr int KPS = KvStage<KV_DT>::kKeysPerStep;
-  const int tid = threadIdx.x;
-  const int kk = tid / LPK;
-  const int c = tid % LPK;
-#pragma unroll
-  for (int s = 0; s < KvStage<KV_DT>::kSteps; ++s) {
-    const int key = s * KPS + kk;
-    const u32x4 v = st.buf[s];
-    if (KV_DT == DT_BF16) {
-      if (c < 16) {
-        *reinterpret_cast<u32x4*>(k_lds + key * kKStride + c * 16) = v;
-      } else {
-        const int d0 = (c - 16) * 8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<uint16_t*>(v_lds + (d0 + 2 * i) * kVStride + key * 2) =
-              (uint16_t)(v[i] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(v_lds + (d0 + 2 * i + 1) * kVStride + key * 2) =
-              (uint16_t)(v[i] >> 16);
-        }
-      }
-    } else {
-      if (c < 8) {
-        const u32x2 b0 = fp8x4_to_bf16x4(v[0]);
-        const u32x2 b1 = fp8x4_to_bf16x4(v[1]);
-        const u32x2 b2 = fp8x4_to_bf16x4(v[2]);
-        const u32x2 b3 = fp8x4_to_bf16x4(v[3]);
-        const u32x4 w0 = {b0[0], b0[1], b1[0], b1[1]};
-        const u32x4 w1 = {b2[0], b2[1], b3[0], b3[1]};
-        *reinterpret_cast<u32x4*>(k_lds + key * kKStride + c * 32) = w0;
-        *reinterpret_cast<u32x4*>(k_lds + key * kKStride + c * 32 + 16) = w1;
-      } else {
-        const int d0 = (c - 8) * 16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x2 b = fp8x4_to_bf16x4(v[i]);
-          *reinterpret_cast<uint16_t*>(v_lds + (d0 + 4 * i + 0) * kVStride + key * 2) =
-              (uint16_t)(b[0] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(v_lds + (d0 + 4 * i + 1) * kVStride + key * 2) =
-              (uint16_t)(b[0] >> 16);
-          *reinterpret_cast<uint16_t*>(v_lds + (d0 + 4 * i + 2) * kVStride + key * 2) =
-              (uint16_t)(b[1] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(v_lds + (d0 + 4 * i + 3) * kVStride + key * 2) =
-              (uint16_t)(b[1] >> 16);
-        }
-      }
-    }
-  }
+// Lane bases (the block-independent part of each operand address).
+__device__ __forceinline__ uint32_t k_base(int key0) {
+  const int lane = threadIdx.x & 63;
+  return col_slot(key0 + (lane & 15), lane >> 4);
+}
+__device__ __forceinline__ uint32_t v_base(int k0) {
+  const int lane = threadIdx.x & 63;
+  const int jj = lane & 15;
+  return col_slot(k0 + 4 * (lane >> 4) + (jj >> 2), 16 + ((jj & 3) >> 1)) + 8 * (jj & 1);
 }
 
-template <int KV_DT>
-__device__ void process_tile(const GqaArgs& a, const Tile& tile, char* k_lds, char* v_lds,
-                             int ps_log2) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int G = a.geo.group;
-  const int seq = tile.seq;
-  const int kvh = tile.kvh;
-  const SeqInfo s = seq_info(a, seq);
+// S^T for one 16-key tile over head_dim 128 (4 k-steps); column 4j + lane/16.
+__device__ __forceinline__ floatx4 score16(uint32_t stage, uint32_t kb, const u32x4* qv) {
+  u32x4 kf[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kf[j] = lds_read_b128(stage + kb + 4 * j * kColStride);
+  floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = mfma_16x16x32(as_bf16x8(kf[j]), as_bf16x8(qv[j]), c);
+  return c;
+}
 
-  int qtok0, ntok, lo, hi;
-  int nsplit = 1;
+// V^T operand of dims 16dt .. 16dt+15 for 4 keys per lane group.
+__device__ __forceinline__ u32x2 vtr(uint32_t stage, uint32_t vb, int dt) {
+  return lds_read_tr16(stage + vb + 2 * dt * kColStride);
+}
+
+struct TileCtx {
+  int seq, kvh, qtok0, ntok, lo, hi, nsplit, first_pos, nrows;
+};
+
+__device__ __forceinline__ TileCtx tile_ctx(const GqaArgs& a, const Tile& tile, const SeqInfo& s) {
+  TileCtx t;
+  t.seq = tile.seq;
+  t.kvh = tile.kvh;
+  t.nsplit = 1;
   if (tile.split >= 0) {
     int lo_all, hi_all, chunk;
     decode_range(a, s, &lo_all, &hi_all);
-    split_plan(hi_all - lo_all, a.geo.split_keys, a.geo.max_splits, &nsplit, &chunk);
-    qtok0 = 0;
-    ntok = s.q_len;
-    lo = lo_all + tile.split * chunk;
-    hi = min(hi_all, lo + chunk);
+    split_plan(hi_all - lo_all, a.geo.split_keys, a.geo.max_splits, &t.nsplit, &chunk);
+    t.qtok0 = 0;
+    t.ntok = s.q_len;
+    t.lo = lo_all + tile.split * chunk;
+    t.hi = min(hi_all, t.lo + chunk);
   } else {
-    qtok0 = tile.qtok0;
-    ntok = min(a.geo.bq, s.q_len - qtok0);
-    const int first = s.kv_len - s.q_len + qtok0;
-    lo = a.geo.window > 0 ? max(0, first - a.geo.window + 1) : 0;
-    hi = min(first + ntok, s.kv_cap);
+    t.qtok0 = tile.qtok0;
+    t.ntok = min(a.geo.bq, s.q_len - t.qtok0);
+    const int first = s.kv_len - s.q_len + t.qtok0;
+    t.lo = a.geo.window > 0 ? max(0, first - a.geo.window + 1) : 0;
+    t.hi = min(first + t.ntok, s.kv_cap);
   }
-  const int first_pos = s.kv_len - s.q_len + qtok0;
-  const int nrows = ntok * G;
-  const bool wave_active = wave * 16 < nrows;
+  t.first_pos = s.kv_len - s.q_len + t.qtok0;
+  t.nrows = t.ntok * a.geo.group;
+  return t;
+}
 
-  // This lane's row (for the S^T columns and the O^T columns).
-  const int r = wave * 16 + (lane & 15);
-  const bool row_ok = r < nrows;
-  const int qpos = row_ok ? first_pos + r / G : kNegBig;
+template <int KV_DT>
+__device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>& sm,
+                             int ps_log2) {
+  constexpr int kDmaCols = KV_DT == DT_BF16 ? kCols : kRawCols;
+  constexpr int kIPW = kDmaCols / 4;  // DMA instructions per wave per block
+  constexpr int kEB = KV_DT == DT_BF16 ? 2 : 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;
+  const int G = a.geo.group;
+  const SeqInfo s = seq_info(a, tile.seq);
+  const TileCtx t = tile_ctx(a, tile, s);
+  const bool keysplit = t.nrows <= 16;
   const int W = a.geo.window;
 
-  // Q^T operand: row r, dims 32j + 8*(lane/16) .. +7.
+  // This lane's row: in key-split mode all waves hold rows 0..15.
+  const int r = (keysplit ? 0 : wave * 16) + (lane & 15);
+  const bool row_ok = r < t.nrows;
+  const bool wave_active = keysplit || wave * 16 < t.nrows;
+  const int qpos = row_ok ? t.first_pos + r / G : kNegBig;
+
   u32x4 qv[4];
   {
-    const int tok = s.cu0 + qtok0 + (row_ok ? r / G : 0);
-    const int head = kvh * G + (row_ok ? r % G : 0);
+    const int tok = s.cu0 + t.qtok0 + (row_ok ? r / G : 0);
+    const int head = t.kvh * G + (row_ok ? r % G : 0);
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.num_q_heads + head) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * j + 8 * (lane >> 4));
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * j + 8 * g);
       qv[j] = v;
     }
   }
@@ -341,127 +336,277 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, char* k_lds, ch
   floatx4 acc[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
 
-  const float cap = a.soft_cap;
-  const float sc = cap != 0.f ? a.score_scale : a.score_scale * kLog2e;
-
-  const int kb0 = lo > 0 ? (lo / kBN) * kBN : 0;
-  const int nblk = hi > kb0 ? cdiv_i(hi - kb0, kBN) : 0;
-
-  KvStage<KV_DT> st;
-  if (nblk > 0) {
-    stage_load<KV_DT>(st, a, seq, kvh, kb0, lo, hi, ps_log2);
-    stage_store<KV_DT>(st, k_lds, v_lds);
+  const int kb0 = (t.lo / kBN) * kBN;
+  const int nblk = t.hi > kb0 ? cdiv_i(t.hi - kb0, kBN) : 0;
+  const int32_t* table = a.page_indices + (int64_t)t.seq * a.pages_per_seq;
+  const int ps_mask = (1 << ps_log2) - 1;
+  int pwin = kb0 >> ps_log2;
+  for (int i = tid; i < kPageWin; i += kThreads) {
+    const int lp = pwin + i;
+    sm.pages[i] = lp < a.pages_per_seq ? table[lp] : -1;
   }
   __syncthreads();
 
-  for (int b = 0; b < nblk; ++b) {
-    const int kb = kb0 + b * kBN;
-    if (b + 1 < nblk) stage_load<KV_DT>(st, a, seq, kvh, kb + kBN, lo, hi, ps_log2);
+  const int64_t token_bytes = (int64_t)2 * a.num_kv_heads * kD * kEB;
+  const char* kv_head = (const char*)a.kv + (int64_t)(2 * t.kvh) * kD * kEB;
+  const uint32_t sbase = lds_addr(sm.stage);
+  const uint32_t dma_stride = KV_DT == DT_BF16 ? kStageBytes : kRawStageBytes;
+  const uint32_t conv = sbase + 2 * kRawStageBytes;  // fp8: converted stage
 
-    if (wave_active) {
-      // S^T[key, row] for the 4 key tiles of the block.
-      floatx4 sv[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        floatx4 c = {0.f, 0.f, 0.f, 0.f};
-        const char* krow = k_lds + (16 * kt + (lane & 15)) * kKStride + 16 * (lane >> 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 kf = *reinterpret_cast<const u32x4*>(krow + 64 * j);
-          c = mfma_16x16x32(as_bf16x8(kf), as_bf16x8(qv[j]), c);
-        }
-        sv[kt] = c;
+  auto issue = [&](int b) {
+    const int kb = kb0 + b * kBN;
+    if (((kb + kBN - 1) >> ps_log2) - pwin >= kPageWin) {
+      wg_barrier();
+      pwin = kb >> ps_log2;
+      for (int i = tid; i < kPageWin; i += kThreads) {
+        const int lp = pwin + i;
+        sm.pages[i] = lp < a.pages_per_seq ? table[lp] : -1;
       }
-      // Scale, soft cap, mask (log2 domain).
+      __syncthreads();
+    }
+    const char* p[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int key = kb + ((lane - 4 * par) & (kBN - 1));
+      p[par] = (const char*)kZeroKV;
+      if (key >= t.lo && key < t.hi) {
+        const int page = sm.pages[(key >> ps_log2) - pwin];
+        if (page >= 0 && page < a.total_num_pages)
+          p[par] = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+      }
+    }
+    const uint32_t st = sbase + (uint32_t)(b & 1) * dma_stride;
+#pragma unroll
+    for (int ii = 0; ii < kIPW; ++ii) {
+      const int c = __builtin_amdgcn_readfirstlane(wave * kIPW + ii);
+      dma_b128(p[c & 1] + c * 16, __builtin_amdgcn_readfirstlane(st + (uint32_t)c * kColStride));
+    }
+  };
+
+  const float cap = a.soft_cap;
+  const float sc = cap != 0.f ? a.score_scale : a.score_scale * kLog2e;
+  uint32_t kbs[4], vbs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    kbs[i] = k_base(16 * i);
+    vbs[i] = v_base(16 * i);
+  }
+  const uint32_t kbw = k_base(16 * wave);  // key-split mode: this wave's key tile
+  const uint32_t vbw = v_base(16 * wave);
+
+  drain_vmem_before_loop();
+  if (nblk > 0) issue(0);
+  for (int b = 0; b < nblk; ++b) {
+    if (b + 1 < nblk) {
+      issue(b + 1);
+      wait_vmcnt<kIPW>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    wg_barrier();
+    uint32_t cur = sbase + (uint32_t)(b & 1) * dma_stride;
+    if (KV_DT == DT_FP8) {
+      // Widen the raw block: thread handles raw column (tid / 64 + 4i), key slot lane.
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rc = wave + 4 * i;                 // raw column: 16 fp8 values
+        const int slot = lane;                       // raw slot of this lane
+        const int key = (slot - 4 * (rc & 1)) & (kBN - 1);
+        const u32x4 w = lds_read_b128(cur + rc * kColStride + slot * 16);
+        const u32x2 b0 = fp8x4_to_bf16x4(w[0]);
+        const u32x2 b1 = fp8x4_to_bf16x4(w[1]);
+        const u32x2 b2 = fp8x4_to_bf16x4(w[2]);
+        const u32x2 b3 = fp8x4_to_bf16x4(w[3]);
+        const int c0 = 2 * rc;  // bf16 columns 2rc (dims 0..7) and 2rc + 1 (dims 8..15)
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+            (__attribute__((address_space(3))) char*)(uintptr_t)(conv + col_slot(key, c0))) =
+            u32x4{b0[0], b0[1], b1[0], b1[1]};
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+            (__attribute__((address_space(3))) char*)(uintptr_t)(conv + col_slot(key, c0 + 1))) =
+            u32x4{b2[0], b2[1], b3[0], b3[1]};
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+      wg_barrier();
+      cur = conv;
+    }
+    const int kb = kb0 + b * kBN;
+    if (keysplit) {
+      // One 16-key tile per wave; PV on v_mfma_f32_16x16x16_bf16.
+      floatx4 sv = score16(cur, kbw, qv);
       float mblk = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 16 * kt + 4 * (lane >> 4) + i;
-          float x = sv[kt][i] * sc;
-          if (cap != 0.f) x = cap * tanh_def(x / cap) * kLog2e;
-          const bool vis = key >= lo && key < hi && key <= qpos && (W <= 0 || key > qpos - W);
-          x = vis ? x : -INFINITY;
-          sv[kt][i] = x;
-          mblk = fmaxf(mblk, x);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + 16 * wave + 4 * g + i;
+        float x = sv[i] * sc;
+        if (cap != 0.f) x = cap * tanh_def(x / cap) * kLog2e;
+        const bool vis = key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
+        sv[i] = vis ? x : -INFINITY;
+        mblk = fmaxf(mblk, sv[i]);
       }
       mblk = wave_max_xor(mblk, 16);
       mblk = wave_max_xor(mblk, 32);
-      const float m_new = fmaxf(m_run, mblk);
-      float alpha = 1.f;
-      u32x4 pb[2];
-      if (m_new == -INFINITY) {
-        pb[0] = u32x4{0u, 0u, 0u, 0u};
-        pb[1] = u32x4{0u, 0u, 0u, 0u};
-      } else {
-        alpha = fast_exp2(m_run - m_new);
+      const bool need = mblk > m_run + kLazyTau;
+      if (wave_any(need)) {
+        const float m_new = need ? mblk : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;  // rows not moving keep scale 1
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          acc[dt][0] *= alpha;
+          acc[dt][1] *= alpha;
+          acc[dt][2] *= alpha;
+          acc[dt][3] *= alpha;
+        }
+        m_run = m_new;
+      }
+      u32x2 pb = {0u, 0u};
+      if (m_run != -INFINITY) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sv[i] - m_run);
+        l_run += p[0] + p[1] + p[2] + p[3];
+        pb[0] = pack_bf16x2(p[0], p[1]);
+        pb[1] = pack_bf16x2(p[2], p[3]);
+      }
+      u32x2 vt[8];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vt[dt] = vtr(cur, vbw, dt);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[dt] = mfma_16x16x16(vt[dt], pb, acc[dt]);
+    } else if (wave_active) {
+      floatx4 sv[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sv[kt] = score16(cur, kbs[kt], qv);
+      float mblk = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 16 * kt + 4 * g + i;
+          float x = sv[kt][i] * sc;
+          if (cap != 0.f) x = cap * tanh_def(x / cap) * kLog2e;
+          const bool vis =
+              key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
+          sv[kt][i] = vis ? x : -INFINITY;
+          mblk = fmaxf(mblk, sv[kt][i]);
+        }
+      mblk = wave_max_xor(mblk, 16);
+      mblk = wave_max_xor(mblk, 32);
+      const bool need = mblk > m_run + kLazyTau;
+      if (wave_any(need)) {
+        const float m_new = need ? mblk : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;  // rows not moving keep scale 1
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          acc[dt][0] *= alpha;
+          acc[dt][1] *= alpha;
+          acc[dt][2] *= alpha;
+          acc[dt][3] *= alpha;
+        }
+        m_run = m_new;
+      }
+      u32x4 pb[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+      if (m_run != -INFINITY) {
         float psum = 0.f;
-        float p[4][4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[kt][i] = fast_exp2(sv[kt][i] - m_new);
-            psum += p[kt][i];
+            sv[kt][i] = fast_exp2(sv[kt][i] - m_run);
+            psum += sv[kt][i];
           }
-        l_run = l_run * alpha + psum;
+        l_run += psum;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          pb[ks][0] = pack_bf16x2(p[2 * ks][0], p[2 * ks][1]);
-          pb[ks][1] = pack_bf16x2(p[2 * ks][2], p[2 * ks][3]);
-          pb[ks][2] = pack_bf16x2(p[2 * ks + 1][0], p[2 * ks + 1][1]);
-          pb[ks][3] = pack_bf16x2(p[2 * ks + 1][2], p[2 * ks + 1][3]);
+          pb[ks][0] = pack_bf16x2(sv[2 * ks][0], sv[2 * ks][1]);
+          pb[ks][1] = pack_bf16x2(sv[2 * ks][2], sv[2 * ks][3]);
+          pb[ks][2] = pack_bf16x2(sv[2 * ks + 1][0], sv[2 * ks + 1][1]);
+          pb[ks][3] = pack_bf16x2(sv[2 * ks + 1][2], sv[2 * ks + 1][3]);
         }
       }
-      m_run = m_new;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        acc[dt][0] *= alpha;
-        acc[dt][1] *= alpha;
-        acc[dt][2] *= alpha;
-        acc[dt][3] *= alpha;
-      }
-      // O^T[d, row] += V^T[d, key] P^T[key, row].
+      for (int dt0 = 0; dt0 < 8; dt0 += 4) {
+        u32x4 vf[4][2];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const char* vrow = v_lds + (16 * dt + (lane & 15)) * kVStride + 8 * (lane >> 4);
+        for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vrow + 64 * ks);
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vrow + 64 * ks + 32);
-          const u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
-          acc[dt] = mfma_16x16x32(as_bf16x8(vf), as_bf16x8(pb[ks]), acc[dt]);
-        }
+          for (int ks = 0; ks < 2; ++ks) {
+            const u32x2 v0 = vtr(cur, vbs[2 * ks], dt0 + d);
+            const u32x2 v1 = vtr(cur, vbs[2 * ks + 1], dt0 + d);
+            vf[d][ks] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          }
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            acc[dt0 + d] = mfma_16x16x32(as_bf16x8(vf[d][ks]), as_bf16x8(pb[ks]), acc[dt0 + d]);
+        sched_fence();
       }
     }
-    __syncthreads();
-    if (b + 1 < nblk) {
-      stage_store<KV_DT>(st, k_lds, v_lds);
-      __syncthreads();
-    }
+    wg_barrier();
   }
 
-  if (!wave_active) return;
-  // Row normaliser: the four lanes holding a row each summed a quarter of it.
+  // Row normaliser of this wave: the four lanes of a row each summed a quarter.
   float l_row = wave_sum_xor(l_run, 16);
   l_row = wave_sum_xor(l_row, 32);
+  float m_row = m_run;
+  if (keysplit) {
+    // Merge the four waves' states (disjoint key tiles) through LDS.
+    float* accs = reinterpret_cast<float*>(sm.stage);       // [4][16][128]
+    float* mls = accs + 4 * 16 * kD;                         // [4][16][2]
+    const int hl = lane & 15;
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<floatx4*>(accs + (wave * 16 + hl) * kD + 16 * dt + 4 * g) = acc[dt];
+    if (g == 0) {
+      mls[(wave * 16 + hl) * 2] = m_run;
+      mls[(wave * 16 + hl) * 2 + 1] = l_row;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * 16 + hl) * 2]);
+    float wt[4];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wt[w] = M == -INFINITY ? 0.f : fast_exp2(mls[(w * 16 + hl) * 2] - M);
+      L += wt[w] * mls[(w * 16 + hl) * 2 + 1];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const floatx4 x = *reinterpret_cast<const floatx4*>(accs + (w * 16 + hl) * kD + 16 * dt + 4 * g);
+        o[0] += wt[w] * x[0];
+        o[1] += wt[w] * x[1];
+        o[2] += wt[w] * x[2];
+        o[3] += wt[w] * x[3];
+      }
+      acc[dt] = o;
+    }
+    m_row = M;
+    l_row = L;
+  } else if (!wave_active) {
+    return;
+  }
 
-  if (tile.split >= 0 && nsplit > 1) {
-    // Partial (m, l, unnormalised acc) for the merge kernel.
-    const int64_t pidx = ((int64_t)seq * a.num_kv_heads + kvh) * a.geo.max_splits + tile.split;
+  if (tile.split >= 0 && t.nsplit > 1) {
+    const int64_t pidx = ((int64_t)t.seq * a.num_kv_heads + t.kvh) * a.geo.max_splits + tile.split;
     if (row_ok) {
       float* pa = a.part_acc + (pidx * kPartRows + r) * kD;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<floatx4*>(pa + 16 * dt + 4 * (lane >> 4)) = acc[dt];
-      if (lane < 16) {
+        *reinterpret_cast<floatx4*>(pa + 16 * dt + 4 * g) = acc[dt];
+      if (g == 0) {
         float* pm = a.part_ml + (pidx * kPartRows + r) * 2;
-        pm[0] = m_run;
+        pm[0] = m_row;
         pm[1] = l_row;
       }
     }
@@ -469,31 +614,30 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, char* k_lds, ch
   }
   if (!row_ok) return;
   const float inv = l_row > 0.f ? a.v_scale / l_row : 0.f;
-  const int tok = s.cu0 + qtok0 + r / G;
-  const int head = kvh * G + r % G;
+  const int tok = s.cu0 + t.qtok0 + r / G;
+  const int head = t.kvh * G + r % G;
   uint16_t* op = (uint16_t*)a.out + ((int64_t)tok * a.num_q_heads + head) * kD;
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) {
     u32x2 w;
     w[0] = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
     w[1] = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-    *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * (lane >> 4)) = w;
+    *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = w;
   }
 }
 
 template <int KV_DT>
-__global__ void __launch_bounds__(kThreads, 2) gqa_tile_kernel(GqaArgs a, int ps_log2) {
-  __shared__ __attribute__((aligned(16))) char smem[kKBytes + kVBytes];
-  __shared__ int s_tile;
+__global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_log2) {
+  __shared__ __attribute__((aligned(16))) TileSmem<KV_DT> sm;
   const int count = a.counters[0];
   for (;;) {
-    if (threadIdx.x == 0) s_tile = atomicAdd(&a.counters[1], 1);
+    if (threadIdx.x == 0) sm.tile = atomicAdd(&a.counters[1], 1);
     __syncthreads();
-    const int ti = s_tile;
+    const int ti = sm.tile;
     __syncthreads();
     if (ti >= count) break;
     const Tile tile = a.tiles[ti];
-    process_tile<KV_DT>(a, tile, smem, smem + kKBytes, ps_log2);
+    process_tile<KV_DT>(a, tile, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -514,22 +658,29 @@ __global__ void __launch_bounds__(kThreads) gqa_merge_kernel(GqaArgs a) {
   const int d0 = (threadIdx.x & 15) * 8; // 8 dims per thread
   if (r >= nrows) return;
   const int64_t pbase = ((int64_t)seq * a.num_kv_heads + kvh) * a.geo.max_splits;
+  float mv[kMaxSplits];
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, a.part_ml[((pbase + sp) * kPartRows + r) * 2]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    mv[sp] = sp < nsplit ? a.part_ml[((pbase + sp) * kPartRows + r) * 2] : -INFINITY;
+    M = fmaxf(M, mv[sp]);
+  }
   float L = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* pm = a.part_ml + ((pbase + sp) * kPartRows + r) * 2;
-      const float w = fast_exp2(pm[0] - M);
-      L += w * pm[1];
-      const float* pa = a.part_acc + ((pbase + sp) * kPartRows + r) * kD + d0;
-      const floatx4 x0 = *reinterpret_cast<const floatx4*>(pa);
-      const floatx4 x1 = *reinterpret_cast<const floatx4*>(pa + 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] += w * x0[i];
-        o[4 + i] += w * x1[i];
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      if (sp < nsplit) {
+        const float w = fast_exp2(mv[sp] - M);
+        L += w * a.part_ml[((pbase + sp) * kPartRows + r) * 2 + 1];
+        const float* pa = a.part_acc + ((pbase + sp) * kPartRows + r) * kD + d0;
+        const floatx4 x0 = *reinterpret_cast<const floatx4*>(pa);
+        const floatx4 x1 = *reinterpret_cast<const floatx4*>(pa + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] += w * x0[i];
+          o[4 + i] += w * x1[i];
+        }
       }
     }
   }
@@ -651,7 +802,7 @@ GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window) {
   g.qdec = g.group <= 16 ? 16 / g.group : 0;
   g.bq = g.group <= 64 ? 64 / g.group : 1;
   g.split_keys = 512;
-  g.max_splits = 16;
+  g.max_splits = kMaxSplits;
   g.window = window;
   return g;
 }
@@ -697,7 +848,7 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   int ps_log2 = 0;
   while ((1 << ps_log2) < a.page_size) ++ps_log2;
   hipLaunchKernelGGL(gqa_plan_kernel, dim3(1), dim3(kThreads), 0, stream, a);
-  const int grid = max(1, min(a.tile_capacity, num_cus() * 4));
+  const int grid = max(1, min(a.tile_capacity, num_cus() * 2));
   prof_begin(stream);
   if (a.kv_dtype == DT_BF16)
     hipLaunchKernelGGL(gqa_tile_kernel<DT_BF16>, dim3(grid), dim3(kThreads), 0, stream, a,

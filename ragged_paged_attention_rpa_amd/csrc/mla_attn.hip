@@ -287,18 +287,28 @@ __global__ void __launch_bounds__(256) mla_plan_kernel(MlaArgs a, int tile_targe
   __threadfence();
   __syncthreads();
   const int total = min(run, a.tile_capacity);
-  for (int t = tid; t < total; t += 256) {
-    int lo = 0, hi = ns - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= t)
-        lo = mid;
-      else
-        hi = mid - 1;
+  // Each thread writes one contiguous range of tiles (one search, then the
+  // owning sequence advances as its offsets are passed).
+  const int span = (total + 255) / 256;
+  const int t0 = min(total, tid * span);
+  const int t1 = min(total, t0 + span);
+  int seq = -1, seq_begin = 0, seq_end = 0, q_len = 0;
+  for (int t = t0; t < t1; ++t) {
+    if (seq < 0 || t >= seq_end) {
+      int lo = 0, hi = ns - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= t)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      seq = lo;
+      seq_begin = off[seq];
+      seq_end = off[seq + 1];
+      q_len = a.cu_q_lens[seq + 1] - a.cu_q_lens[seq];
     }
-    const int seq = lo;
-    const int local = t - off[seq];
-    const int q_len = a.cu_q_lens[seq + 1] - a.cu_q_lens[seq];
+    const int local = t - seq_begin;
     int4 tl;
     tl.x = seq;
     tl.w = local % HG;
@@ -423,6 +433,7 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
     kbase[t] = k_base(16 * t);
     vbase[t] = v_base(16 * t);
   }
+  drain_vmem_before_loop();
   if (nblk > 0) issue(0, st0);
   for (int b = 0; b < nblk; ++b) {
     const uint32_t cur = (b & 1) ? st1 : st0;
@@ -463,7 +474,7 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
           const bool need = mblk > m_run[h] + kLazyTau;
           if (wave_any(need)) {
             const float m_new = need ? mblk : m_run[h];
-            const float alpha = fast_exp2(m_run[h] - m_new);
+            const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.f;  // rows not moving keep scale 1
             l_run[h] *= alpha;
 #pragma unroll
             for (int dt = 0; dt < kDvTiles; ++dt) {
@@ -703,6 +714,7 @@ sparse_mla_kernel(SparseArgs a) {
   const float sc = a.score_scale;
   const uint32_t kbase = k_base(16 * wave);
   const uint32_t vbase = v_base(16 * wave);
+  drain_vmem_before_loop();
   if (nblk > 0) issue(0, st0, sm.valid[0]);
   for (int b = 0; b < nblk; ++b) {
     const int cs = b & 1;
@@ -731,7 +743,7 @@ sparse_mla_kernel(SparseArgs a) {
     const bool need = mblk > m_run + kLazyTau;
     if (wave_any(need)) {
       const float m_new = need ? mblk : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;  // rows not moving keep scale 1
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < kDvTiles; ++dt) {

@@ -132,6 +132,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Waits for every outstanding vector-memory op with an s_waitcnt the
+// compiler's wait-count pass can see (vmcnt 0, expcnt and lgkmcnt untouched).
+// Called before a DMA-pipelined loop: the pass then knows the loads issued
+// before the loop (queries, page ids) are complete and does not put a
+// vmcnt(0) inside the loop, which would also drain the in-flight DMA.
+__device__ __forceinline__ void drain_vmem_before_loop() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Compiler-only fence: memory accesses are not moved across it. Used to keep
 // the scheduler from hoisting a whole unrolled loop's LDS loads at once.
 __device__ __forceinline__ void sched_fence() { asm volatile("" : : : "memory"); }

@@ -281,3 +281,16 @@ def test_kv_update_rejects_aliased_slots():
     with pytest.raises(rpa.RpaError, match="twice"):
         rpa.kv_cache_update(rpa.LAYOUT_MLA_FUSED, two_kvc, two_kpe, cache,
                             slot_loc=torch.cat([loc, loc]), debug_validate=True)
+
+
+def test_rows_whose_window_starts_in_a_later_block():
+    """Rows of one tile whose visible keys begin in different key blocks (the
+    first block is fully masked for some rows only): regression test for the
+    per-row rescale when other rows of the wave move their reference max."""
+    _say("window starting in a later block")
+    for Hq, Hkv in [(16, 16), (16, 4), (8, 1)]:
+        c = wl.make_gqa([(40, 1200), (70, 70), (3, 1000)], num_q_heads=Hq, num_kv_heads=Hkv,
+                        head_dim=128, page_size=32, q_dtype=torch.bfloat16,
+                        kv_dtype=torch.bfloat16, seed=102, device="cuda", sliding_window=100,
+                        name=f"late-window-{Hq}-{Hkv}")
+        _check(c, _run_gpu(c), _run_oracle(c), "bf16")
