@@ -54,42 +54,27 @@ struct RowSrc {
   int64_t sa, sb;
 };
 
-// Per-lane source pointers of one block: lane L loads key L in even columns
-// and key (L - 4) mod 64 in odd columns. rows[k] (LDS) is the physical row of
-// block key k, or -1 for a key that must read as zeros.
-struct LanePtrs {
-  const char* a[2];
-  const char* b[2];
-};
-
-__device__ __forceinline__ LanePtrs lane_ptrs(const RowSrc& src, const int* rows) {
-  const int lane = threadIdx.x & 63;
-  LanePtrs lp;
-#pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int key = (lane - 4 * par) & (kBlk - 1);
-    const int row = rows[key];
-    if (row >= 0) {
-      lp.a[par] = src.a + (int64_t)row * src.sa;
-      lp.b[par] = src.b + (int64_t)row * src.sb;
-    } else {
-      lp.a[par] = (const char*)kZeroRow;
-      lp.b[par] = (const char*)kZeroRow + kDl * 2;
-    }
-  }
-  return lp;
-}
-
 // This wave's share of one block: columns [wave*IPW, wave*IPW + IPW), one
-// global_load_lds_dwordx4 each (64 keys x 16 bytes).
+// global_load_lds_dwordx4 each (64 keys x 16 bytes). Lane L loads key L in
+// even columns and key (L - 4) mod 64 in odd columns; rows[k] (LDS) is the
+// physical row of block key k, or -1 for a key that must read as zeros. Both
+// row ids are read from LDS before the first DMA of the block; the
+// addresses are then rebuilt per instruction with VALU arithmetic only.
 template <int IPW>
-__device__ __forceinline__ void issue_block(const LanePtrs& lp, uint32_t stage, int wave) {
+__device__ __forceinline__ void issue_block(const RowSrc& src, uint32_t stage, int wave,
+                                            const int* rows) {
+  const int lane = threadIdx.x & 63;
+  const int row_par[2] = {rows[lane], rows[(lane - 4) & (kBlk - 1)]};
 #pragma unroll
   for (int ii = 0; ii < IPW; ++ii) {
     const int c = __builtin_amdgcn_readfirstlane(wave * IPW + ii);
-    const int par = c & 1;
-    const char* g = c < 64 ? (par ? lp.a[1] : lp.a[0]) + c * 16
-                           : (par ? lp.b[1] : lp.b[0]) + (c - 64) * 16;
+    const int row = (c & 1) ? row_par[1] : row_par[0];
+    const bool in_a = c < 64;
+    const char* base = in_a ? src.a : src.b;
+    const int64_t stride = in_a ? src.sa : src.sb;
+    const int coff = (in_a ? c : c - 64) * 16;
+    const char* g = row >= 0 ? base + (int64_t)row * stride + coff
+                             : (const char*)kZeroRow + c * 16;
     dma_b128(g, __builtin_amdgcn_readfirstlane(stage + (uint32_t)c * kColStride));
   }
 }
@@ -422,7 +407,7 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     wg_barrier();
-    issue_block<kMlaIPW>(lane_ptrs(src, sm.rows), st, wave);
+    issue_block<kMlaIPW>(src, st, wave, sm.rows);
   };
 
   const float sc = a.score_scale;
@@ -708,7 +693,7 @@ sparse_mla_kernel(SparseArgs a) {
     }
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     wg_barrier();
-    issue_block<kSpIPW>(lane_ptrs(src, sm.rows), st, wave);
+    issue_block<kSpIPW>(src, st, wave, sm.rows);
   };
 
   const float sc = a.score_scale;

@@ -120,11 +120,21 @@ __device__ __forceinline__ floatx4 mfma_16x16x16(const u32x2& a, const u32x2& b,
 // Issued through inline asm so the compiler's wait-count pass does not treat
 // it as an LDS store and add waits before unrelated LDS reads; callers wait
 // with wait_vmcnt<N>() (vector-memory ops complete in issue order).
+// Because the compiler cannot see the memory instruction inside the asm, the
+// asm carries its own wait states: one between the M0 write and the LDS-DMA
+// load that reads M0, and five after the load before the compiler may reuse
+// the address registers. Callers also read everything a block's DMA needs
+// from LDS before issuing it: LDS reads interleaved between the LDS-DMA
+// instructions of one wave gave wrong rows on gfx950.
 __device__ __forceinline__ void dma_b128(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(gaddr)
-               : "memory");
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_nop 4"
+      :
+      : "s"(lds_base), "v"(gaddr)
+      : "memory");
 }
 
 template <int N>
