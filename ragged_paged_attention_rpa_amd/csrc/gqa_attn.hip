@@ -2,9 +2,9 @@
 // ref_ragged_paged_attention, flash_attention].
 //
 // Three launches on one stream, no host synchronisation:
-//   1. gqa_plan_kernel   one workgroup turns the ragged metadata into a work
-//                        list of tiles (prefill-class tiles first, then
-//                        decode-class splits) and resets the work cursor;
+//   1. gqa_plan_kernel   turns the ragged metadata into a work list of tiles
+//                        (prefill-class tiles first, then decode-class
+//                        splits) and resets the work cursor;
 //   2. gqa_tile_kernel   a persistent grid pops tiles off the list. A tile is
 //                        (sequence, kv head, block of query tokens, key range);
 //                        its rows are (query token, q head of the kv head's
@@ -27,7 +27,8 @@ namespace {
 
 constexpr int kD = 128;                   // head dim of the MFMA path
 constexpr int kBN = 64;                   // keys per LDS block
-constexpr int kThreads = 256;             // 4 waves
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kPartRows = 16;             // rows of a decode-class tile
 constexpr int kNegBig = -1000000000;
 constexpr int kMaxSplits = 16;            // cap on splits of one decode sequence
@@ -99,21 +100,27 @@ __device__ __forceinline__ void seq_tile_counts(const GqaArgs& a, int seq, int* 
   }
 }
 
-// Block-wide exclusive scan of one int per thread (256 threads).
+// Block-wide exclusive scan of one int per thread: wave scans by shuffles,
+// then the four wave totals through LDS.
 __device__ int block_excl_scan(int v, int* sh, int* total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int x = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += x;
-    __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
-  const int incl = sh[tid];
-  *total = sh[kThreads - 1];
+  if (lane == 63) sh[wave] = x;
   __syncthreads();
-  return incl - v;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    before += w < wave ? sh[w] : 0;
+    all += sh[w];
+  }
+  *total = all;
+  __syncthreads();
+  return before + x - v;
 }
 
 // seq_off layout in the workspace: [0, ns] prefill offsets, then [0, ns] decode offsets.
@@ -132,12 +139,18 @@ __device__ __forceinline__ int upper_bound_seq(const int* off, int n, int t) {
   return lo;
 }
 
+// Batches of up to this many sequences keep the planner's tile offsets in LDS.
+constexpr int kPlanLdsSeqs = 4096;
+constexpr int kPlanWgs = 32;
+
 __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
   __shared__ int sh[kThreads];
+  __shared__ int off_lds[2 * (kPlanLdsSeqs + 1)];
   const int tid = threadIdx.x;
   const int ns = num_seqs_clamped(a);
-  int* pre_off = seq_offsets(a);
-  int* dec_off = pre_off + (a.max_num_seqs + 1);
+  const bool in_lds = ns <= kPlanLdsSeqs;
+  int* pre_off = in_lds ? off_lds : seq_offsets(a);
+  int* dec_off = pre_off + (in_lds ? kPlanLdsSeqs + 1 : a.max_num_seqs + 1);
   int run_pre = 0, run_dec = 0;
   for (int c0 = 0; c0 < ns; c0 += kThreads) {
     const int i = c0 + tid;
@@ -157,15 +170,22 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
     pre_off[ns] = run_pre;
     dec_off[ns] = run_dec;
   }
-  __threadfence();
+  if (!in_lds) __threadfence();
   __syncthreads();
   const int total = min(run_pre + run_dec, a.tile_capacity);
   const int H = a.num_kv_heads;
-  // Each thread writes one contiguous range of tiles: one search for its
-  // first tile, then the owning sequence advances as the offsets are passed.
-  const int per = (total + kThreads - 1) / kThreads;
-  const int t0 = min(total, tid * per);
-  const int t1 = min(total, t0 + per);
+  // With the offsets in LDS every workgroup has computed them and writes its
+  // share of the tiles; otherwise workgroup 0 writes them all. Each thread
+  // writes one contiguous range: one search for its first tile, then the
+  // owning sequence advances as the offsets are passed.
+  const int nwg = in_lds ? (int)gridDim.x : 1;
+  if ((int)blockIdx.x >= nwg) return;
+  const int per_wg = (total + nwg - 1) / nwg;
+  const int w0 = min(total, (int)blockIdx.x * per_wg);
+  const int w1 = min(total, w0 + per_wg);
+  const int per = (w1 - w0 + kThreads - 1) / kThreads;
+  const int t0 = min(w1, w0 + tid * per);
+  const int t1 = min(w1, t0 + per);
   if (t0 < t1) {
     int seq = -1, seq_begin = 0, seq_end = 0, nqb = 1;
     for (int t = t0; t < t1; ++t) {
@@ -199,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
       a.tiles[t] = tl;
     }
   }
-  if (tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     a.counters[0] = total;
     a.counters[1] = 0;
   }
@@ -207,13 +227,18 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
 
 // ------------------------------------------------------------ tile kernel --
 //
-// Keys move through LDS in blocks of 64, one key per lane of a DMA
-// instruction (global_load_lds_dwordx4), so a block is stored chunk-major:
-// column c holds 16 bytes of every key. bf16 pools give 32 columns per key
-// (K dims 8c..8c+7 in columns 0..15, V dims in 16..31); fp8 pools give 16 raw
-// columns that a conversion pass widens into the same bf16 layout. Odd
-// columns rotate the keys by four slots and columns are padded to 1088 bytes,
-// which keeps both MFMA operand reads free of LDS bank conflicts.
+// Keys move through LDS in blocks of 64. A DMA instruction
+// (global_load_lds_dwordx4) moves 1 KB of consecutive global bytes, two keys
+// of a bf16 pool (K then V of one kv head: 512 bytes each) or four keys of an
+// fp8 pool (256 bytes each): wide contiguous requests stream much faster
+// than the 64-keys-by-16-bytes pattern of one column per instruction. A block
+// is stored key-major, 512 bytes per key; inside a key the 16-byte column q
+// (0..15 K dims 8q.., 16..31 V dims 8(q-16)..) sits at q ^ swz(key), which
+// makes the K reads (eight keys, one column) and the transposed V reads
+// (four keys, two columns) hit distinct banks. The DMA applies the swizzle
+// by choosing which global column each lane fetches. fp8 blocks land raw
+// (256 bytes per key, unswizzled) and a conversion pass widens them into
+// the bf16 layout.
 //
 // Two compute modes share the block pipeline:
 //  * rows <= 16 (decode): every wave takes the same rows and one 16-key tile
@@ -221,52 +246,64 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
 //    in LDS at the end;
 //  * rows > 16 (prefill): wave w takes rows 16w .. 16w+15 against all 64 keys.
 
-constexpr int kCols = 32;                     // bf16 columns per key (K + V)
-constexpr int kRawCols = 16;                  // fp8 columns per key (K + V)
-constexpr int kColStride = kBN * 16 + 64;     // 1088 bytes per column
-constexpr int kStageBytes = kCols * kColStride;       // 34816
-constexpr int kRawStageBytes = kRawCols * kColStride; // 17408
-constexpr int kPageWin = 512;                 // page ids of the tile cached in LDS
+constexpr int kKeyBytes = 512;                       // K + V of one key, bf16
+constexpr int kRawKeyBytes = 256;                    // K + V of one key, fp8
+constexpr int kStageBytes = kBN * kKeyBytes;         // 32768
+constexpr int kRawStageBytes = kBN * kRawKeyBytes;   // 16384
+constexpr int kTileBytes = 16 * kKeyBytes;           // one 16-key MFMA tile
+constexpr int kPageWin = 512;                        // page ids of the tile cached in LDS
+constexpr int kStages = 2;                           // DMA stages per workgroup
 
 __device__ __attribute__((aligned(16))) const uint8_t kZeroKV[512] = {0};
 
-template <int KV_DT>
+template <int KV_DT, int NST>
 struct TileSmem {
-  // bf16: two DMA stages. fp8: two raw DMA stages plus one converted stage.
-  char stage[KV_DT == DT_BF16 ? 2 * kStageBytes : 2 * kRawStageBytes + kStageBytes];
+  // bf16: NST DMA stages. fp8: NST raw DMA stages plus one converted stage.
+  char stage[KV_DT == DT_BF16 ? NST * kStageBytes : NST * kRawStageBytes + kStageBytes];
   int pages[kPageWin];
   int tile;
 };
 
-__device__ __forceinline__ uint32_t col_slot(int key, int c) {
-  return (uint32_t)(c * kColStride + (((key + 4 * (c & 1)) & (kBN - 1)) << 4));
+// Column swizzle of a key (only its low four bits matter, so every 16-key
+// tile has the same pattern): eight consecutive keys give distinct low three
+// bits, and the four keys of an aligned quad give distinct bits 1..2.
+__device__ __forceinline__ int swz(int key) {
+  return ((key & 3) << 1) | ((key >> 2) & 1) | (key & 8);
 }
 
-// Lane bases (the block-independent part of each operand address).
-__device__ __forceinline__ uint32_t k_base(int key0) {
-  const int lane = threadIdx.x & 63;
-  return col_slot(key0 + (lane & 15), lane >> 4);
+// Byte offset of logical column q of block key `key`.
+__device__ __forceinline__ uint32_t key_col(int key, int q) {
+  return (uint32_t)(key * kKeyBytes + ((q ^ swz(key)) << 4));
 }
-__device__ __forceinline__ uint32_t v_base(int k0) {
+
+// K operand of tile 0 for k-step 0: key lane%16, column lane/16. Column
+// lane/16 + 4j is at k_base() ^ (j << 6); tile t is kTileBytes * t further.
+__device__ __forceinline__ uint32_t k_base() {
+  const int lane = threadIdx.x & 63;
+  return key_col(lane & 15, lane >> 4);
+}
+// Transposed-V operand of tile 0, dims 0..15: in each 16-lane group g, lanes
+// 4r..4r+3 read 8 bytes each of key 4g + r. Dims 16dt.. are at v_base() ^ (dt << 5).
+__device__ __forceinline__ uint32_t v_base() {
   const int lane = threadIdx.x & 63;
   const int jj = lane & 15;
-  return col_slot(k0 + 4 * (lane >> 4) + (jj >> 2), 16 + ((jj & 3) >> 1)) + 8 * (jj & 1);
+  return key_col(4 * (lane >> 4) + (jj >> 2), 16 + ((jj & 3) >> 1)) + 8 * (jj & 1);
 }
 
-// S^T for one 16-key tile over head_dim 128 (4 k-steps); column 4j + lane/16.
-__device__ __forceinline__ floatx4 score16(uint32_t stage, uint32_t kb, const u32x4* qv) {
+// S^T for one 16-key tile over head_dim 128 (4 k-steps); kx[j] = k_base() ^ (j << 6).
+__device__ __forceinline__ floatx4 score16(uint32_t tile, const uint32_t* kx, const u32x4* qv) {
   u32x4 kf[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kf[j] = lds_read_b128(stage + kb + 4 * j * kColStride);
+  for (int j = 0; j < 4; ++j) kf[j] = lds_read_b128(tile + kx[j]);
   floatx4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < 4; ++j) c = mfma_16x16x32(as_bf16x8(kf[j]), as_bf16x8(qv[j]), c);
   return c;
 }
 
-// V^T operand of dims 16dt .. 16dt+15 for 4 keys per lane group.
-__device__ __forceinline__ u32x2 vtr(uint32_t stage, uint32_t vb, int dt) {
-  return lds_read_tr16(stage + vb + 2 * dt * kColStride);
+// V^T operand of dims 16dt .. 16dt+15 for 4 keys per lane group; vx = v_base() ^ (dt << 5).
+__device__ __forceinline__ u32x2 vtr(uint32_t tile, uint32_t vx) {
+  return lds_read_tr16(tile + vx);
 }
 
 struct TileCtx {
@@ -298,11 +335,25 @@ __device__ __forceinline__ TileCtx tile_ctx(const GqaArgs& a, const Tile& tile, 
   return t;
 }
 
-template <int KV_DT>
-__device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>& sm,
+// Waits until at most `ahead` blocks of this wave's DMA are outstanding
+// (each block is kIPW instructions).
+template <int kIPW>
+__device__ __forceinline__ void wait_blocks_ahead(int ahead) {
+  if (ahead <= 0)
+    wait_vmcnt<0>();
+  else if (ahead == 1)
+    wait_vmcnt<kIPW>();
+  else if (ahead == 2)
+    wait_vmcnt<2 * kIPW>();
+  else
+    wait_vmcnt<3 * kIPW>();
+}
+
+template <int KV_DT, int NST>
+__device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT, NST>& sm,
                              int ps_log2) {
-  constexpr int kDmaCols = KV_DT == DT_BF16 ? kCols : kRawCols;
-  constexpr int kIPW = kDmaCols / 4;  // DMA instructions per wave per block
+  // DMA instructions per wave per block (1 KB each, four waves).
+  constexpr int kIPW = (KV_DT == DT_BF16 ? kStageBytes : kRawStageBytes) / 1024 / kWaves;
   constexpr int kEB = KV_DT == DT_BF16 ? 2 : 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -353,7 +404,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>
   const char* kv_head = (const char*)a.kv + (int64_t)(2 * t.kvh) * kD * kEB;
   const uint32_t sbase = lds_addr(sm.stage);
   const uint32_t dma_stride = KV_DT == DT_BF16 ? kStageBytes : kRawStageBytes;
-  const uint32_t conv = sbase + 2 * kRawStageBytes;  // fp8: converted stage
+  const uint32_t conv = sbase + NST * kRawStageBytes;  // fp8: converted stage
 
   auto issue = [&](int b) {
     const int kb = kb0 + b * kBN;
@@ -366,65 +417,76 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>
       }
       __syncthreads();
     }
-    const char* p[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int key = kb + ((lane - 4 * par) & (kBN - 1));
-      p[par] = (const char*)kZeroKV;
-      if (key >= t.lo && key < t.hi) {
-        const int page = sm.pages[(key >> ps_log2) - pwin];
-        if (page >= 0 && page < a.total_num_pages)
-          p[par] = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
-      }
+    // Row address of block key 16*wave + lane%16 (the same in each 16-lane
+    // group); every DMA instruction below takes its keys' rows by readlane.
+    const int key = kb + 16 * wave + (lane & 15);
+    const char* row = (const char*)kZeroKV;
+    if (key >= t.lo && key < t.hi) {
+      const int page = sm.pages[(key >> ps_log2) - pwin];
+      if (page >= 0 && page < a.total_num_pages)
+        row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
     }
-    const uint32_t st = sbase + (uint32_t)(b & 1) * dma_stride;
+    const uint32_t rlo = (uint32_t)(uintptr_t)row;
+    const uint32_t rhi = (uint32_t)((uintptr_t)row >> 32);
+    const uint32_t st = sbase + (uint32_t)(b % NST) * dma_stride;
+    constexpr int kKeysPerDma = KV_DT == DT_BF16 ? 2 : 4;
+    const int sub = KV_DT == DT_BF16 ? lane >> 5 : lane >> 4;  // key of this lane in the DMA
 #pragma unroll
     for (int ii = 0; ii < kIPW; ++ii) {
-      const int c = __builtin_amdgcn_readfirstlane(wave * kIPW + ii);
-      dma_b128(p[c & 1] + c * 16, __builtin_amdgcn_readfirstlane(st + (uint32_t)c * kColStride));
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int k = 0; k < kKeysPerDma; ++k) {
+        const uint32_t l = __builtin_amdgcn_readlane(rlo, kKeysPerDma * ii + k);
+        const uint32_t h = __builtin_amdgcn_readlane(rhi, kKeysPerDma * ii + k);
+        lo = sub == k ? l : lo;
+        hi = sub == k ? h : hi;
+      }
+      const char* base = (const char*)(((uint64_t)hi << 32) | lo);
+      const char* src = KV_DT == DT_BF16
+                            ? base + (((lane & 31) ^ swz(kKeysPerDma * ii + sub)) << 4)
+                            : base + ((lane & 15) << 4);
+      const int c = wave * kIPW + ii;  // 1 KB slot of the stage
+      dma_b128(src, __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024));
     }
   };
 
   const float cap = a.soft_cap;
   const float sc = cap != 0.f ? a.score_scale : a.score_scale * kLog2e;
-  uint32_t kbs[4], vbs[4];
+  uint32_t kx[4], vx[8];
+  {
+    const uint32_t kb_ = k_base(), vb_ = v_base();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    kbs[i] = k_base(16 * i);
-    vbs[i] = v_base(16 * i);
+    for (int j = 0; j < 4; ++j) kx[j] = kb_ ^ (uint32_t)(j << 6);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) vx[dt] = vb_ ^ (uint32_t)(dt << 5);
   }
-  const uint32_t kbw = k_base(16 * wave);  // key-split mode: this wave's key tile
-  const uint32_t vbw = v_base(16 * wave);
 
   drain_vmem_before_loop();
-  if (nblk > 0) issue(0);
+  // Prologue: the first NST-1 blocks in flight.
+  for (int b = 0; b < NST - 1 && b < nblk; ++b) issue(b);
   for (int b = 0; b < nblk; ++b) {
-    if (b + 1 < nblk) {
-      issue(b + 1);
-      wait_vmcnt<kIPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    if (b + NST - 1 < nblk) issue(b + NST - 1);
+    // Blocks issued after block b: min(NST-1, nblk-1-b).
+    wait_blocks_ahead<kIPW>(min(NST - 1, nblk - 1 - b));
     wg_barrier();
-    uint32_t cur = sbase + (uint32_t)(b & 1) * dma_stride;
+    uint32_t cur = sbase + (uint32_t)(b % NST) * dma_stride;
     if (KV_DT == DT_FP8) {
-      // Widen the raw block: thread handles raw column (tid / 64 + 4i), key slot lane.
+      // Widen the raw block: unit u = tid + 256i is raw column u%16 of key
+      // u/16 (16 fp8 values: bf16 columns 2(u%16) and 2(u%16) + 1).
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rc = wave + 4 * i;                 // raw column: 16 fp8 values
-        const int slot = lane;                       // raw slot of this lane
-        const int key = (slot - 4 * (rc & 1)) & (kBN - 1);
-        const u32x4 w = lds_read_b128(cur + rc * kColStride + slot * 16);
+        const int u = tid + kThreads * i;
+        const int key = u >> 4, rc = u & 15;
+        const u32x4 w = lds_read_b128(cur + key * kRawKeyBytes + rc * 16);
         const u32x2 b0 = fp8x4_to_bf16x4(w[0]);
         const u32x2 b1 = fp8x4_to_bf16x4(w[1]);
         const u32x2 b2 = fp8x4_to_bf16x4(w[2]);
         const u32x2 b3 = fp8x4_to_bf16x4(w[3]);
-        const int c0 = 2 * rc;  // bf16 columns 2rc (dims 0..7) and 2rc + 1 (dims 8..15)
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-            (__attribute__((address_space(3))) char*)(uintptr_t)(conv + col_slot(key, c0))) =
+            (__attribute__((address_space(3))) char*)(uintptr_t)(conv + key_col(key, 2 * rc))) =
             u32x4{b0[0], b0[1], b1[0], b1[1]};
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-            (__attribute__((address_space(3))) char*)(uintptr_t)(conv + col_slot(key, c0 + 1))) =
+            (__attribute__((address_space(3))) char*)(uintptr_t)(conv + key_col(key, 2 * rc + 1))) =
             u32x4{b2[0], b2[1], b3[0], b3[1]};
       }
       asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
@@ -434,7 +496,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>
     const int kb = kb0 + b * kBN;
     if (keysplit) {
       // One 16-key tile per wave; PV on v_mfma_f32_16x16x16_bf16.
-      floatx4 sv = score16(cur, kbw, qv);
+      floatx4 sv = score16(cur + kTileBytes * wave, kx, qv);
       float mblk = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -472,13 +534,13 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>
       }
       u32x2 vt[8];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) vt[dt] = vtr(cur, vbw, dt);
+      for (int dt = 0; dt < 8; ++dt) vt[dt] = vtr(cur + kTileBytes * wave, vx[dt]);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) acc[dt] = mfma_16x16x16(vt[dt], pb, acc[dt]);
     } else if (wave_active) {
       floatx4 sv[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) sv[kt] = score16(cur, kbs[kt], qv);
+      for (int kt = 0; kt < 4; ++kt) sv[kt] = score16(cur + kTileBytes * kt, kx, qv);
       float mblk = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -534,8 +596,8 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>
         for (int d = 0; d < 4; ++d)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const u32x2 v0 = vtr(cur, vbs[2 * ks], dt0 + d);
-            const u32x2 v1 = vtr(cur, vbs[2 * ks + 1], dt0 + d);
+            const u32x2 v0 = vtr(cur + kTileBytes * (2 * ks), vx[dt0 + d]);
+            const u32x2 v1 = vtr(cur + kTileBytes * (2 * ks + 1), vx[dt0 + d]);
             vf[d][ks] = u32x4{v0[0], v0[1], v1[0], v1[1]};
           }
 #pragma unroll
@@ -626,9 +688,9 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT>
   }
 }
 
-template <int KV_DT>
+template <int KV_DT, int NST>
 __global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_log2) {
-  __shared__ __attribute__((aligned(16))) TileSmem<KV_DT> sm;
+  __shared__ __attribute__((aligned(16))) TileSmem<KV_DT, NST> sm;
   const int count = a.counters[0];
   for (;;) {
     if (threadIdx.x == 0) sm.tile = atomicAdd(&a.counters[1], 1);
@@ -637,7 +699,7 @@ __global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_lo
     __syncthreads();
     if (ti >= count) break;
     const Tile tile = a.tiles[ti];
-    process_tile<KV_DT>(a, tile, sm, ps_log2);
+    process_tile<KV_DT, NST>(a, tile, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -801,7 +863,7 @@ GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window) {
   g.group = num_q_heads / num_kv_heads;
   g.qdec = g.group <= 16 ? 16 / g.group : 0;
   g.bq = g.group <= 64 ? 64 / g.group : 1;
-  g.split_keys = 512;
+  g.split_keys = 1024;
   g.max_splits = kMaxSplits;
   g.window = window;
   return g;
@@ -847,15 +909,21 @@ void gqa_bind_workspace(GqaArgs& a, void* ws) {
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   int ps_log2 = 0;
   while ((1 << ps_log2) < a.page_size) ++ps_log2;
-  hipLaunchKernelGGL(gqa_plan_kernel, dim3(1), dim3(kThreads), 0, stream, a);
+  // Up to kPlanLdsSeqs sequences, several planner workgroups share the tile
+  // writes (each computes the offsets itself); beyond that, one workgroup.
+  const int plan_wgs = a.max_num_seqs <= kPlanLdsSeqs ? kPlanWgs : 1;
+  hipLaunchKernelGGL(gqa_plan_kernel, dim3(plan_wgs), dim3(kThreads), 0, stream, a);
+  // Two workgroups per CU, each with two stages: one block computing while
+  // the next streams in (deeper pipelines at one workgroup per CU measured
+  // slower: the compute of a block is then exposed).
   const int grid = max(1, min(a.tile_capacity, num_cus() * 2));
   prof_begin(stream);
   if (a.kv_dtype == DT_BF16)
-    hipLaunchKernelGGL(gqa_tile_kernel<DT_BF16>, dim3(grid), dim3(kThreads), 0, stream, a,
-                       ps_log2);
+    hipLaunchKernelGGL((gqa_tile_kernel<DT_BF16, kStages>), dim3(grid), dim3(kThreads), 0, stream,
+                       a, ps_log2);
   else
-    hipLaunchKernelGGL(gqa_tile_kernel<DT_FP8>, dim3(grid), dim3(kThreads), 0, stream, a,
-                       ps_log2);
+    hipLaunchKernelGGL((gqa_tile_kernel<DT_FP8, kStages>), dim3(grid), dim3(kThreads), 0, stream,
+                       a, ps_log2);
   prof_end(stream);
   if (a.geo.qdec > 0)
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(a.max_num_seqs * a.num_kv_heads), dim3(kThreads),

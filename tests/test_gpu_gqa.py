@@ -66,6 +66,10 @@ RAGGED = [
     ([(1, 300), (40, 1200), (2, 129), (70, 70)], 16, 16, 32, 100, None, "mha-window"),
     ([(9, 200), (1, 5000), (33, 513)], 8, 1, 64, None, 30.0, "mqa-cap"),
     ([(4, 4), (2, 1025), (24, 900)], 16, 2, 16, 257, 20.0, "g8-window-cap"),
+    # decode sequences long enough that the split count hits its cap and the
+    # chunks grow past the target split size
+    ([(1, 20000), (2, 17000), (4, 1500), (1, 16385)], 32, 8, 16, None, None, "long-decode"),
+    ([(1, 18000), (3, 9000)], 16, 4, 16, 5000, 30.0, "long-window"),
 ]
 
 
