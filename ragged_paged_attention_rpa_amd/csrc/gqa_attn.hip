@@ -237,8 +237,8 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
 // makes the K reads (eight keys, one column) and the transposed V reads
 // (four keys, two columns) hit distinct banks. The DMA applies the swizzle
 // by choosing which global column each lane fetches. fp8 blocks land raw
-// (256 bytes per key, unswizzled) and a conversion pass widens them into
-// the bf16 layout.
+// (256 bytes per key, column rc at rc ^ (key & 15)) and a conversion pass
+// widens them into the bf16 layout.
 //
 // Two compute modes share the block pipeline:
 //  * rows <= 16 (decode): every wave takes the same rows and one 16-key tile
@@ -265,10 +265,19 @@ struct TileSmem {
 };
 
 // Column swizzle of a key (only its low four bits matter, so every 16-key
-// tile has the same pattern): eight consecutive keys give distinct low three
-// bits, and the four keys of an aligned quad give distinct bits 1..2.
+// tile has the same pattern). It maps the low four key bits one-to-one, gives
+// eight consecutive keys distinct low three bits (K reads: eight keys, one
+// column) and, for the transposed V reads (four keys of a quad, two columns
+// each), distinct bits 0..2 within a quad and distinct bit 3 between the two
+// quads of an aligned group of eight, so neither read conflicts with 32 or 64
+// LDS banks.
 __device__ __forceinline__ int swz(int key) {
-  return ((key & 3) << 1) | ((key >> 2) & 1) | (key & 8);
+  return ((key & 3) << 1) | ((key >> 2) & 1) | ((((key >> 2) ^ (key >> 3)) & 1) << 3);
+}
+
+// Raw fp8 blocks: column rc (0..15) of key k sits at rc ^ (k & 15).
+__device__ __forceinline__ uint32_t raw_col(int key, int rc) {
+  return (uint32_t)(key * kRawKeyBytes + ((rc ^ (key & 15)) << 4));
 }
 
 // Byte offset of logical column q of block key `key`.
@@ -349,7 +358,7 @@ __device__ __forceinline__ void wait_blocks_ahead(int ahead) {
     wait_vmcnt<3 * kIPW>();
 }
 
-template <int KV_DT, int NST>
+template <int KV_DT, int NST, bool CAP>
 __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT, NST>& sm,
                              int ps_log2) {
   // DMA instructions per wave per block (1 KB each, four waves).
@@ -442,16 +451,31 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
         hi = sub == k ? h : hi;
       }
       const char* base = (const char*)(((uint64_t)hi << 32) | lo);
-      const char* src = KV_DT == DT_BF16
-                            ? base + (((lane & 31) ^ swz(kKeysPerDma * ii + sub)) << 4)
-                            : base + ((lane & 15) << 4);
+      const int kk = kKeysPerDma * ii + sub;  // key within this wave's 16
+      const char* src = KV_DT == DT_BF16 ? base + (((lane & 31) ^ swz(kk)) << 4)
+                                         : base + (((lane & 15) ^ kk) << 4);
       const int c = wave * kIPW + ii;  // 1 KB slot of the stage
       dma_b128(src, __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024));
     }
   };
 
-  const float cap = a.soft_cap;
-  const float sc = cap != 0.f ? a.score_scale : a.score_scale * kLog2e;
+  // Log2-domain logit of a raw score s = q.k: s * scale * log2(e), or with
+  // the soft cap c, c * tanh(s * scale / c) * log2(e). tanh(z) is taken as
+  // 1 - 2 / (e^{2z} + 1) with the hardware exp2 and reciprocal, so the capped
+  // logit is c2 - c3 / (2^{s * c1} + 1).
+  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
+  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
+  auto logit = [&](float sraw) -> float {
+    if (!CAP) return sraw * c1;
+    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
+  };
+  // Keys [klo, khi) of this wave's share of a block are visible to every row
+  // of the wave (rows past the tile's end do not count): the mask can be skipped.
+  auto all_visible = [&](int klo, int khi) -> bool {
+    const bool ok = !row_ok || (klo >= t.lo && khi <= t.hi && khi - 1 <= qpos &&
+                                (W <= 0 || klo > qpos - W));
+    return __builtin_amdgcn_ballot_w64(!ok) == 0;
+  };
   uint32_t kx[4], vx[8];
   {
     const uint32_t kb_ = k_base(), vb_ = v_base();
@@ -471,13 +495,13 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     wg_barrier();
     uint32_t cur = sbase + (uint32_t)(b % NST) * dma_stride;
     if (KV_DT == DT_FP8) {
-      // Widen the raw block: unit u = tid + 256i is raw column u%16 of key
-      // u/16 (16 fp8 values: bf16 columns 2(u%16) and 2(u%16) + 1).
+      // Widen the raw block: thread tid takes raw column tid/16 (16 fp8
+      // values: bf16 columns 2(tid/16) and 2(tid/16) + 1) of keys tid%16 + 16i,
+      // so sixteen consecutive lanes touch sixteen keys.
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int u = tid + kThreads * i;
-        const int key = u >> 4, rc = u & 15;
-        const u32x4 w = lds_read_b128(cur + key * kRawKeyBytes + rc * 16);
+        const int key = (tid & 15) + 16 * i, rc = tid >> 4;
+        const u32x4 w = lds_read_b128(cur + raw_col(key, rc));
         const u32x2 b0 = fp8x4_to_bf16x4(w[0]);
         const u32x2 b1 = fp8x4_to_bf16x4(w[1]);
         const u32x2 b2 = fp8x4_to_bf16x4(w[2]);
@@ -498,14 +522,21 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
       // One 16-key tile per wave; PV on v_mfma_f32_16x16x16_bf16.
       floatx4 sv = score16(cur + kTileBytes * wave, kx, qv);
       float mblk = -INFINITY;
+      if (all_visible(kb + 16 * wave, kb + 16 * wave + 16)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 16 * wave + 4 * g + i;
-        float x = sv[i] * sc;
-        if (cap != 0.f) x = cap * tanh_def(x / cap) * kLog2e;
-        const bool vis = key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
-        sv[i] = vis ? x : -INFINITY;
-        mblk = fmaxf(mblk, sv[i]);
+        for (int i = 0; i < 4; ++i) {
+          sv[i] = logit(sv[i]);
+          mblk = fmaxf(mblk, sv[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 16 * wave + 4 * g + i;
+          const bool vis =
+              key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
+          sv[i] = vis ? logit(sv[i]) : -INFINITY;
+          mblk = fmaxf(mblk, sv[i]);
+        }
       }
       mblk = wave_max_xor(mblk, 16);
       mblk = wave_max_xor(mblk, 32);
@@ -542,18 +573,26 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) sv[kt] = score16(cur + kTileBytes * kt, kx, qv);
       float mblk = -INFINITY;
+      if (all_visible(kb, kb + kBN)) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kb + 16 * kt + 4 * g + i;
-          float x = sv[kt][i] * sc;
-          if (cap != 0.f) x = cap * tanh_def(x / cap) * kLog2e;
-          const bool vis =
-              key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
-          sv[kt][i] = vis ? x : -INFINITY;
-          mblk = fmaxf(mblk, sv[kt][i]);
-        }
+          for (int i = 0; i < 4; ++i) {
+            sv[kt][i] = logit(sv[kt][i]);
+            mblk = fmaxf(mblk, sv[kt][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb + 16 * kt + 4 * g + i;
+            const bool vis =
+                key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
+            sv[kt][i] = vis ? logit(sv[kt][i]) : -INFINITY;
+            mblk = fmaxf(mblk, sv[kt][i]);
+          }
+      }
       mblk = wave_max_xor(mblk, 16);
       mblk = wave_max_xor(mblk, 32);
       const bool need = mblk > m_run + kLazyTau;
@@ -688,7 +727,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
   }
 }
 
-template <int KV_DT, int NST>
+template <int KV_DT, int NST, bool CAP>
 __global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_log2) {
   __shared__ __attribute__((aligned(16))) TileSmem<KV_DT, NST> sm;
   const int count = a.counters[0];
@@ -699,7 +738,7 @@ __global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_lo
     __syncthreads();
     if (ti >= count) break;
     const Tile tile = a.tiles[ti];
-    process_tile<KV_DT, NST>(a, tile, sm, ps_log2);
+    process_tile<KV_DT, NST, CAP>(a, tile, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -918,12 +957,22 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   // slower: the compute of a block is then exposed).
   const int grid = max(1, min(a.tile_capacity, num_cus() * 2));
   prof_begin(stream);
-  if (a.kv_dtype == DT_BF16)
-    hipLaunchKernelGGL((gqa_tile_kernel<DT_BF16, kStages>), dim3(grid), dim3(kThreads), 0, stream,
-                       a, ps_log2);
-  else
-    hipLaunchKernelGGL((gqa_tile_kernel<DT_FP8, kStages>), dim3(grid), dim3(kThreads), 0, stream,
-                       a, ps_log2);
+  const bool cap = a.soft_cap != 0.f;
+#define RPA_TILE_LAUNCH(DT, CAP)                                                         \
+  hipLaunchKernelGGL((gqa_tile_kernel<DT, kStages, CAP>), dim3(grid), dim3(kThreads), 0, \
+                     stream, a, ps_log2)
+  if (a.kv_dtype == DT_BF16) {
+    if (cap)
+      RPA_TILE_LAUNCH(DT_BF16, true);
+    else
+      RPA_TILE_LAUNCH(DT_BF16, false);
+  } else {
+    if (cap)
+      RPA_TILE_LAUNCH(DT_FP8, true);
+    else
+      RPA_TILE_LAUNCH(DT_FP8, false);
+  }
+#undef RPA_TILE_LAUNCH
   prof_end(stream);
   if (a.geo.qdec > 0)
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(a.max_num_seqs * a.num_kv_heads), dim3(kThreads),
