@@ -5,11 +5,15 @@
 // Both attend one 576-wide latent row per key, shared by every head: the key
 // is the whole row [kv_c (512) || k_pe (64)], the value its first 512 columns.
 // Shared core:
-//  * keys stream through LDS in blocks of 64 rows x 1152 bytes, moved by
+//  * keys stream through LDS in blocks of 64 rows, moved by
 //    global_load_lds_dwordx4 (no register staging) into two stages, so the
-//    next block's loads are in flight while the current one is multiplied;
-//  * 16-byte chunks of a row are XOR-swizzled by (row/2 mod 8) so that the
-//    16 rows read by one MFMA operand fall in distinct LDS bank groups;
+//    next block's loads are in flight while the current one is multiplied.
+//    One instruction moves the 1 KB latent part of one row; one more moves
+//    the 128-byte rope parts of eight rows, so every request is a long run
+//    of consecutive bytes;
+//  * a block is stored row-major (latent parts, then rope parts); the 16-byte
+//    chunks of a row are XOR-swizzled by the row, so the rows read by one
+//    MFMA operand fall in distinct LDS banks;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS, Q^T in VGPRs),
 //    V^T for O^T += V^T P^T read straight out of the same rows with
 //    ds_read_b64_tr_b16, so the value needs no second copy.
@@ -29,23 +33,32 @@ namespace {
 
 constexpr int kDl = 512;
 constexpr int kDk = 576;
-constexpr int kRowChunks = kDk * 2 / 16;              // 72 chunks of 16 B per latent row
-constexpr int kBlk = 64;                              // keys per block (one per lane)
-constexpr int kColStride = kBlk * 16 + 64;            // 1088: LDS bytes per chunk column
-constexpr int kStageBytes = kRowChunks * kColStride;  // 78336
-constexpr int kQSteps = kDk / 32;                     // 18 MFMA k-steps
-constexpr int kDvTiles = kDl / 16;                    // 32 output tiles of 16 dims
+constexpr int kBlk = 64;                                     // keys per block
+constexpr int kKvcBytes = kDl * 2;                           // 1024: latent part of a row
+constexpr int kKpeBytes = (kDk - kDl) * 2;                   // 128: rope part of a row
+constexpr int kKpeOff = kBlk * kKvcBytes;                    // rope parts follow the latent parts
+constexpr int kStageBytes = kBlk * (kKvcBytes + kKpeBytes);  // 73728
+constexpr int kTileKvc = 16 * kKvcBytes;                     // latent parts of a 16-key tile
+constexpr int kTileKpe = 16 * kKpeBytes;                     // rope parts of a 16-key tile
+constexpr int kDmaPer8 = 9;                                  // DMA instructions per 8 keys
+constexpr int kQSteps = kDk / 32;                            // 18 MFMA k-steps
+constexpr int kDvTiles = kDl / 16;                           // 32 output tiles of 16 dims
 
 // Zero row read by keys outside the visible range (1152 bytes of bf16 zeros).
-__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kRowChunks * 16] = {0};
+__device__ __attribute__((aligned(16))) const uint8_t kZeroRow[kKvcBytes + kKpeBytes] = {0};
 
-// LDS layout of a block: chunk-major. Column c (16 bytes of every key) starts
-// at c * kColStride; key k sits at slot k in even columns and at slot
-// (k + 4) mod 64 in odd columns. The column padding (64 B) and the rotation
-// keep both operand reads below free of bank conflicts.
-__device__ __forceinline__ uint32_t col_slot(int key, int c) {
-  return (uint32_t)(c * kColStride + (((key + 4 * (c & 1)) & (kBlk - 1)) << 4));
+// Chunk q (0..63) of a row's latent part sits at q ^ swz(row) (row = key
+// within the block; only its low four bits matter): one-to-one on sixteen
+// consecutive rows, distinct low three bits on eight, distinct bits 0..2
+// within an aligned quad and distinct bit 3 between the two quads of an
+// aligned eight, which keeps the K reads (one chunk of 8 or 16 rows) and the
+// transposed V reads (two chunks of 4 rows per lane group) conflict free.
+__device__ __forceinline__ int swz(int key) {
+  return ((key & 3) << 1) | ((key >> 2) & 1) | ((((key >> 2) ^ (key >> 3)) & 1) << 3);
 }
+// Rope chunk q (0..7) sits at q ^ swz_pe(row): one-to-one on eight
+// consecutive rows and on the eight rows of either parity among sixteen.
+__device__ __forceinline__ int swz_pe(int key) { return ((key >> 1) & 7) ^ ((key & 1) << 2); }
 
 // Latent row r: columns [0, 512) at a + r*sa, columns [512, 576) at b + r*sb.
 struct RowSrc {
@@ -54,89 +67,89 @@ struct RowSrc {
   int64_t sa, sb;
 };
 
-// This wave's share of one block: columns [wave*IPW, wave*IPW + IPW), one
-// global_load_lds_dwordx4 each (64 keys x 16 bytes). Lane L loads key L in
-// even columns and key (L - 4) mod 64 in odd columns; rows[k] (LDS) is the
-// physical row of block key k, or -1 for a key that must read as zeros. Both
-// row ids are read from LDS before the first DMA of the block; the
-// addresses are then rebuilt per instruction with VALU arithmetic only.
-template <int IPW>
-__device__ __forceinline__ void issue_block(const RowSrc& src, uint32_t stage, int wave,
-                                            const int* rows) {
+// DMA of block keys [8*grp, 8*grp + 8): their latent parts (one instruction
+// per key, 64 lanes x 16 bytes) and rope parts (one instruction, 8 keys x 8
+// lanes). `row` is the physical row of block key 8*grp + lane/8, or -1 for a
+// key that reads as zeros; the latent instructions take their row by readlane.
+__device__ __forceinline__ void issue_keys8(const RowSrc& src, uint32_t stage, int grp, int row) {
   const int lane = threadIdx.x & 63;
-  const int row_par[2] = {rows[lane], rows[(lane - 4) & (kBlk - 1)]};
 #pragma unroll
-  for (int ii = 0; ii < IPW; ++ii) {
-    const int c = __builtin_amdgcn_readfirstlane(wave * IPW + ii);
-    const int row = (c & 1) ? row_par[1] : row_par[0];
-    const bool in_a = c < 64;
-    const char* base = in_a ? src.a : src.b;
-    const int64_t stride = in_a ? src.sa : src.sb;
-    const int coff = (in_a ? c : c - 64) * 16;
-    const char* g = row >= 0 ? base + (int64_t)row * stride + coff
-                             : (const char*)kZeroRow + c * 16;
-    dma_b128(g, __builtin_amdgcn_readfirstlane(stage + (uint32_t)c * kColStride));
+  for (int ii = 0; ii < 8; ++ii) {
+    const int r = __builtin_amdgcn_readlane(row, 8 * ii);
+    const int key = 8 * grp + ii;
+    const char* base = r >= 0 ? src.a + (int64_t)r * src.sa : (const char*)kZeroRow;
+    dma_b128(base + ((lane ^ swz(key)) << 4),
+             __builtin_amdgcn_readfirstlane(stage + (uint32_t)key * kKvcBytes));
   }
+  const int key = 8 * grp + (lane >> 3);
+  const char* base =
+      row >= 0 ? src.b + (int64_t)row * src.sb : (const char*)kZeroRow + kKvcBytes;
+  dma_b128(base + (((lane & 7) ^ swz_pe(key)) << 4),
+           __builtin_amdgcn_readfirstlane(stage + (uint32_t)(kKpeOff + grp * 1024)));
 }
 
-// Q^T operand of one wave: lane l holds head (l % 16) dims 32j + 8(l/16) .. +7.
+// Q^T operand of one wave, lane l = head l%16. The contraction order is free
+// as long as K uses the same one: k-step j < 16 covers latent chunk
+// 16*(l/16) + j (dims 128(l/16) + 8j ..+7), k-step 16 + m rope chunk
+// 2*(l/16) + m.
 __device__ __forceinline__ void load_q(u32x4* qv, const uint16_t* q_nope, const uint16_t* q_pe,
                                        bool ok) {
   const int g = (threadIdx.x & 63) >> 4;
 #pragma unroll
-  for (int j = 0; j < kQSteps; ++j) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (ok) {
-      const int d = 32 * j + 8 * g;
-      v = d < kDl ? *reinterpret_cast<const u32x4*>(q_nope + d)
-                  : *reinterpret_cast<const u32x4*>(q_pe + (d - kDl));
-    }
-    qv[j] = v;
-  }
+  for (int j = 0; j < 16; ++j)
+    qv[j] = ok ? *reinterpret_cast<const u32x4*>(q_nope + 128 * g + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+    qv[16 + m] = ok ? *reinterpret_cast<const u32x4*>(q_pe + 16 * g + 8 * m) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Lane base for the S^T A operand of key tile key0 (rows key0 + lane%16,
-// columns 4j + lane/16): col_slot(...) minus the j-dependent 4j*kColStride.
-__device__ __forceinline__ uint32_t k_base(int key0) {
+// S^T A operand, key tile 0 (row lane%16): latent k-step j at k_lat() ^ (j << 4),
+// rope k-step 16 + m at k_rope() ^ (m << 4); tile t is t*kTileKvc (t*kTileKpe)
+// further. Stage bases are multiples of 1024, so the XOR may follow the add.
+__device__ __forceinline__ uint32_t k_lat() {
   const int lane = threadIdx.x & 63;
-  return col_slot(key0 + (lane & 15), lane >> 4);
+  const int kk = lane & 15;
+  return (uint32_t)(kk * kKvcBytes + 256 * (lane >> 4) + (swz(kk) << 4));
 }
-
-// Lane base for the V^T A operand read with ds_read_b64_tr_b16 for keys
-// k0 + 4(lane/16) .. +3 and dims 16dt + lane%16 (dt-dependent part removed).
-__device__ __forceinline__ uint32_t v_base(int k0) {
+__device__ __forceinline__ uint32_t k_rope() {
   const int lane = threadIdx.x & 63;
-  const int g = lane >> 4;
+  const int kk = lane & 15;
+  return (uint32_t)(kKpeOff + kk * kKpeBytes + (((2 * (lane >> 4)) ^ swz_pe(kk)) << 4));
+}
+// V^T A operand read with ds_read_b64_tr_b16, key tile 0: in lane group g,
+// lanes 4r..4r+3 read 8 bytes each of row 4g + r; dims 16dt .. are at
+// v_lat() ^ (dt << 5).
+__device__ __forceinline__ uint32_t v_lat() {
+  const int lane = threadIdx.x & 63;
   const int jj = lane & 15;
-  const int h = (jj & 3) >> 1;
-  return col_slot(k0 + 4 * g + (jj >> 2), h) + 8 * (jj & 1);
+  const int key = 4 * (lane >> 4) + (jj >> 2);
+  return (uint32_t)(key * kKvcBytes + ((((jj & 3) >> 1) ^ swz(key)) << 4) + 8 * (jj & 1));
 }
 
-// S^T[key, head] for one 16-key tile and NH head tiles; each K operand read
-// feeds NH MFMAs.
-template <int NH>
-__device__ __forceinline__ void score_tile(floatx4* out, uint32_t stage, uint32_t kb,
-                                           const u32x4 (*qv)[kQSteps]) {
-  const uint32_t base = stage + kb;
+// S^T[key, head] for NT 16-key tiles and NH 16-head tiles; lat/rope are the
+// lane operand addresses of the first tile (stage included). Each K read
+// feeds NH MFMAs; the NT tiles give independent accumulation chains.
+template <int NT, int NH>
+__device__ __forceinline__ void score_tiles(floatx4 (&sv)[NT][NH], uint32_t lat, uint32_t rope,
+                                            const u32x4 (&qv)[NH][kQSteps]) {
 #pragma unroll
-  for (int h = 0; h < NH; ++h) out[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
-  for (int j0 = 0; j0 < kQSteps; j0 += 3) {
-    u32x4 kf[3];
+    for (int h = 0; h < NH; ++h) sv[t][h] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 3; ++j) kf[j] = lds_read_b128(base + 4 * (j0 + j) * kColStride);
+  for (int j = 0; j < kQSteps; ++j) {
+    u32x4 kf[NT];
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+    for (int t = 0; t < NT; ++t)
+      kf[t] = j < 16 ? lds_read_b128((lat ^ (uint32_t)(j << 4)) + t * kTileKvc)
+                     : lds_read_b128((rope ^ (uint32_t)((j - 16) << 4)) + t * kTileKpe);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < NH; ++h)
-        out[h] = mfma_16x16x32(as_bf16x8(kf[j]), as_bf16x8(qv[h][j0 + j]), out[h]);
+        sv[t][h] = mfma_16x16x32(as_bf16x8(kf[t]), as_bf16x8(qv[h][j]), sv[t][h]);
     sched_fence();
   }
-}
-
-// V^T operand for dims of tile dt (4 keys per lane group).
-__device__ __forceinline__ u32x2 v_tr(uint32_t stage, uint32_t vb, int dt) {
-  return lds_read_tr16(stage + vb + 2 * dt * kColStride);
 }
 
 // Score transform in the exp2 domain: scale, optional soft cap.
@@ -169,10 +182,12 @@ constexpr int kMlaWaves = 8;
 constexpr int kMlaThreads = kMlaWaves * 64;
 constexpr int kMlaHT = 1;                             // 16-head tiles per wave
 constexpr int kMlaHeads = kMlaWaves * 16 * kMlaHT;    // heads per workgroup (128)
-constexpr int kMlaIPW = kRowChunks / kMlaWaves;       // 9 columns per wave
+constexpr int kMlaGroups = kBlk / 8 / kMlaWaves;      // 8-key DMA groups per wave
+constexpr int kMlaIPW = kMlaGroups * kDmaPer8;        // DMA instructions per wave per block
 constexpr int kPageWin = 1024;                        // page ids cached in LDS
 constexpr int kMlaMaxSplits = 16;
 constexpr int kMlaMinChunk = 256;
+constexpr int kPvStep = 2;                            // V tiles per PV step
 
 struct MlaSeq {
   int cu0, q_len, kv_len, kv_cap;
@@ -316,7 +331,6 @@ __global__ void __launch_bounds__(256) mla_plan_kernel(MlaArgs a, int tile_targe
 struct MlaShared {
   char stage[2][kStageBytes];
   int pages[kPageWin];
-  int rows[kBlk];
   int tile;
 };
 static_assert(sizeof(MlaShared) <= 160 * 1024, "MLA LDS budget");
@@ -383,7 +397,8 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
   const uint32_t st1 = lds_addr(sm.stage[1]);
   const int P = a.total_num_pages;
 
-  // Rows of block b go to sm.rows (one thread per key), then this wave's DMA.
+  // This wave's DMA groups of block b: each lane resolves the row of its key
+  // (key 8*grp + lane/8) before the group's first DMA instruction.
   auto issue = [&](int b, uint32_t st) {
     const int kb = kb0 + b * kBlk;
     // Refill the page window when this block runs past it.
@@ -396,28 +411,24 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
       }
       __syncthreads();
     }
-    if (tid < kBlk) {
-      const int key = kb + tid;
+    int rows[kMlaGroups];
+#pragma unroll
+    for (int gi = 0; gi < kMlaGroups; ++gi) {
+      const int key = kb + 8 * (wave * kMlaGroups + gi) + (lane >> 3);
       int row = -1;
       if (key >= lo && key < hi) {
         const int page = sm.pages[(key >> ps_log2) - pwin];
         if (page >= 0 && page < P) row = (page << ps_log2) + (key & ps_mask);
       }
-      sm.rows[tid] = row;
+      rows[gi] = row;
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-    wg_barrier();
-    issue_block<kMlaIPW>(src, st, wave, sm.rows);
+#pragma unroll
+    for (int gi = 0; gi < kMlaGroups; ++gi) issue_keys8(src, st, wave * kMlaGroups + gi, rows[gi]);
   };
 
   const float sc = a.score_scale;
   const float cap = a.soft_cap;
-  uint32_t kbase[4], vbase[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    kbase[t] = k_base(16 * t);
-    vbase[t] = v_base(16 * t);
-  }
+  const uint32_t klat = k_lat(), krope = k_rope(), vlat = v_lat();
   drain_vmem_before_loop();
   if (nblk > 0) issue(0, st0);
   for (int b = 0; b < nblk; ++b) {
@@ -430,22 +441,20 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
     }
     wg_barrier();
     if (wave_active) {
-      const int kb = kb0 + b * kBlk;
-      u32x4 pb[kMlaHT][2];
-#pragma unroll
-      for (int h = 0; h < kMlaHT; ++h) {
-        pb[h][0] = u32x4{0u, 0u, 0u, 0u};
-        pb[h][1] = u32x4{0u, 0u, 0u, 0u};
-      }
-      {
-        floatx4 sv[4][kMlaHT];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) score_tile<kMlaHT>(sv[kt], cur, kbase[kt], qv);
+      // The block is taken as two halves of 32 keys, each with its own
+      // softmax step, which keeps the per-step registers small.
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        const int kb = kb0 + b * kBlk + 32 * half;
+        const uint32_t hc = cur + (uint32_t)(2 * half * kTileKvc);
+        u32x4 pb[kMlaHT];
+        floatx4 sv[2][kMlaHT];
+        score_tiles<2, kMlaHT>(sv, hc + klat, cur + (uint32_t)(2 * half * kTileKpe) + krope, qv);
 #pragma unroll
         for (int h = 0; h < kMlaHT; ++h) {
           float mblk = -INFINITY;
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = kb + 16 * kt + 4 * g + i;
@@ -470,41 +479,42 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
             }
             m_run[h] = m_new;
           }
+          pb[h] = u32x4{0u, 0u, 0u, 0u};
           if (m_run[h] != -INFINITY) {
             float psum = 0.f;
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 sv[kt][h][i] = fast_exp2(sv[kt][h][i] - m_run[h]);
                 psum += sv[kt][h][i];
               }
             l_run[h] += psum;
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              pb[h][ks][0] = pack_bf16x2(sv[2 * ks][h][0], sv[2 * ks][h][1]);
-              pb[h][ks][1] = pack_bf16x2(sv[2 * ks][h][2], sv[2 * ks][h][3]);
-              pb[h][ks][2] = pack_bf16x2(sv[2 * ks + 1][h][0], sv[2 * ks + 1][h][1]);
-              pb[h][ks][3] = pack_bf16x2(sv[2 * ks + 1][h][2], sv[2 * ks + 1][h][3]);
-            }
+            pb[h][0] = pack_bf16x2(sv[0][h][0], sv[0][h][1]);
+            pb[h][1] = pack_bf16x2(sv[0][h][2], sv[0][h][3]);
+            pb[h][2] = pack_bf16x2(sv[1][h][0], sv[1][h][1]);
+            pb[h][3] = pack_bf16x2(sv[1][h][2], sv[1][h][3]);
           }
         }
-      }
+        // O^T += V^T P^T over the 32 keys (one k-step: tiles 2*half and 2*half + 1).
+        const uint32_t vcur = hc + vlat;
 #pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt) {
-        u32x4 vf[2];
+        for (int dt0 = 0; dt0 < kDvTiles; dt0 += kPvStep) {
+          u32x4 vf[kPvStep];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const u32x2 v0 = v_tr(cur, vbase[2 * ks], dt);
-          const u32x2 v1 = v_tr(cur, vbase[2 * ks + 1], dt);
-          vf[ks] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          for (int d = 0; d < kPvStep; ++d) {
+            const uint32_t va = vcur ^ (uint32_t)((dt0 + d) << 5);
+            const u32x2 v0 = lds_read_tr16(va);
+            const u32x2 v1 = lds_read_tr16(va + kTileKvc);
+            vf[d] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          }
+#pragma unroll
+          for (int d = 0; d < kPvStep; ++d)
+#pragma unroll
+            for (int h = 0; h < kMlaHT; ++h)
+              acc[h][dt0 + d] = mfma_16x16x32(as_bf16x8(vf[d]), as_bf16x8(pb[h]), acc[h][dt0 + d]);
+          sched_fence();
         }
-#pragma unroll
-        for (int h = 0; h < kMlaHT; ++h)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            acc[h][dt] = mfma_16x16x32(as_bf16x8(vf[ks]), as_bf16x8(pb[h][ks]), acc[h][dt]);
-        sched_fence();
       }
     }
     wg_barrier();
@@ -543,7 +553,7 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
 }
 
 __global__ void __launch_bounds__(kMlaThreads) mla_tile_kernel(MlaArgs a, int ps_log2) {
-  __shared__ __attribute__((aligned(16))) MlaShared sm;
+  __shared__ __attribute__((aligned(1024))) MlaShared sm;
   const int count = a.counters[0];
   const int chunk = a.counters[2];
   for (;;) {
@@ -610,21 +620,20 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
 
 constexpr int kSpWaves = 4;
 constexpr int kSpThreads = kSpWaves * 64;
-constexpr int kSpIPW = kRowChunks / kSpWaves;         // 18 columns per wave
+constexpr int kSpGroups = kBlk / 8 / kSpWaves;         // 8-key DMA groups per wave (2)
+constexpr int kSpIPW = kSpGroups * kDmaPer8;           // DMA instructions per wave per block
 constexpr int kSpMaxUnits = 256;
 
 struct SparseShared {
   char stage[2][kStageBytes];
   int unit_row[kSpMaxUnits];
   int unit_id[kSpMaxUnits];
-  int rows[kBlk];
-  uint8_t valid[2][kBlk];
 };
 static_assert(sizeof(SparseShared) <= 160 * 1024, "sparse LDS budget");
 
 __global__ void __launch_bounds__(kSpThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 sparse_mla_kernel(SparseArgs a) {
-  __shared__ __attribute__((aligned(16))) SparseShared sm;
+  __shared__ __attribute__((aligned(1024))) SparseShared sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -656,10 +665,10 @@ sparse_mla_kernel(SparseArgs a) {
   }
   __syncthreads();
 
-  u32x4 qv[kQSteps];
+  u32x4 qv[1][kQSteps];
   {
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)qi * a.num_heads + head) * kDk;
-    load_q(qv, qp, qp + kDl, head_ok);
+    load_q(qv[0], qp, qp + kDl, head_ok);
   }
   floatx4 acc[kDvTiles];
 #pragma unroll
@@ -676,10 +685,14 @@ sparse_mla_kernel(SparseArgs a) {
   const int total = K * RB;
   const int nblk = cdiv_i(total, kBlk);
 
-  // Rows and validity of block b (one thread per key), then this wave's DMA.
-  auto issue = [&](int b, uint32_t st, uint8_t* valid) {
-    if (tid < kBlk) {
-      const int kk = b * kBlk + tid;
+  // This wave's two DMA groups of block b (keys 16*wave .. +15, the keys it
+  // also multiplies). Each lane resolves the row of key 8*grp + lane/8; the
+  // validity of the group's keys is returned as a lane mask (bit 8i: key i).
+  auto issue = [&](int b, uint32_t st, uint64_t* vmask) {
+    int rows[kSpGroups];
+#pragma unroll
+    for (int gi = 0; gi < kSpGroups; ++gi) {
+      const int kk = b * kBlk + 16 * wave + 8 * gi + (lane >> 3);
       int row = -1;
       if (kk < total) {
         const int unit = kk / RB;
@@ -688,37 +701,41 @@ sparse_mla_kernel(SparseArgs a) {
         const int kp = sm.unit_id[unit] * RB + r;
         if (base >= 0 && kp <= pos && kp < a.seq_len) row = base + r;
       }
-      sm.rows[tid] = row;
-      valid[tid] = row >= 0 ? 1 : 0;
+      rows[gi] = row;
+      vmask[gi] = __builtin_amdgcn_ballot_w64(row >= 0);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-    wg_barrier();
-    issue_block<kSpIPW>(src, st, wave, sm.rows);
+#pragma unroll
+    for (int gi = 0; gi < kSpGroups; ++gi) issue_keys8(src, st, 2 * wave + gi, rows[gi]);
   };
 
   const float sc = a.score_scale;
-  const uint32_t kbase = k_base(16 * wave);
-  const uint32_t vbase = v_base(16 * wave);
+  const uint32_t klat = k_lat() + wave * kTileKvc;
+  const uint32_t krope = k_rope() + wave * kTileKpe;
+  const uint32_t vlat = v_lat() + wave * kTileKvc;
+  uint64_t vm_cur[kSpGroups] = {0, 0}, vm_next[kSpGroups] = {0, 0};
   drain_vmem_before_loop();
-  if (nblk > 0) issue(0, st0, sm.valid[0]);
+  if (nblk > 0) issue(0, st0, vm_next);
   for (int b = 0; b < nblk; ++b) {
     const int cs = b & 1;
     const uint32_t cur = cs ? st1 : st0;
+    vm_cur[0] = vm_next[0];
+    vm_cur[1] = vm_next[1];
     if (b + 1 < nblk) {
-      issue(b + 1, cs ? st0 : st1, sm.valid[cs ^ 1]);
+      issue(b + 1, cs ? st0 : st1, vm_next);
       wait_vmcnt<kSpIPW>();
     } else {
       wait_vmcnt<0>();
     }
-    // DMA of block b landed (vmcnt above); validity bytes written with ds_write.
-    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     wg_barrier();
-    floatx4 sv;
-    score_tile<1>(&sv, cur, kbase, &qv);
+    floatx4 sv2[1][1];
+    score_tiles<1, 1>(sv2, (cur + klat), (cur + krope), qv);
+    floatx4 sv = sv2[0][0];
+    // Keys 4g + i of this wave's tile: group g/2, bit 8*(4(g&1) + i) of its mask.
+    const uint64_t vm = (g >> 1) ? vm_cur[1] : vm_cur[0];
     float mblk = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = sm.valid[cs][16 * wave + 4 * g + i] != 0;
+      const bool ok = ((vm >> (8 * (4 * (g & 1) + i))) & 1ull) != 0;
       const float x = ok ? score_log2(sv[i], sc, 0.f) : -INFINITY;
       sv[i] = x;
       mblk = fmaxf(mblk, x);
@@ -752,7 +769,7 @@ sparse_mla_kernel(SparseArgs a) {
     for (int dt0 = 0; dt0 < kDvTiles; dt0 += 4) {
       u32x2 vt[4];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) vt[d] = v_tr(cur, vbase, dt0 + d);
+      for (int d = 0; d < 4; ++d) vt[d] = lds_read_tr16((cur + vlat) ^ (uint32_t)((dt0 + d) << 5));
 #pragma unroll
       for (int d = 0; d < 4; ++d) acc[dt0 + d] = mfma_16x16x16(vt[d], pb, acc[dt0 + d]);
       sched_fence();
