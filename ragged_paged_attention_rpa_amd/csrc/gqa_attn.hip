@@ -366,7 +366,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
   constexpr int kEB = KV_DT == DT_BF16 ? 2 : 1;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int g = lane >> 4;
   const int G = a.geo.group;
   const SeqInfo s = seq_info(a, tile.seq);
@@ -538,8 +538,8 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
           mblk = fmaxf(mblk, sv[i]);
         }
       }
-      mblk = wave_max_xor(mblk, 16);
-      mblk = wave_max_xor(mblk, 32);
+      mblk = wave_max_xor<16>(mblk);
+      mblk = wave_max_xor<32>(mblk);
       const bool need = mblk > m_run + kLazyTau;
       if (wave_any(need)) {
         const float m_new = need ? mblk : m_run;
@@ -593,8 +593,8 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
             mblk = fmaxf(mblk, sv[kt][i]);
           }
       }
-      mblk = wave_max_xor(mblk, 16);
-      mblk = wave_max_xor(mblk, 32);
+      mblk = wave_max_xor<16>(mblk);
+      mblk = wave_max_xor<32>(mblk);
       const bool need = mblk > m_run + kLazyTau;
       if (wave_any(need)) {
         const float m_new = need ? mblk : m_run;
@@ -651,8 +651,8 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
   }
 
   // Row normaliser of this wave: the four lanes of a row each summed a quarter.
-  float l_row = wave_sum_xor(l_run, 16);
-  l_row = wave_sum_xor(l_row, 32);
+  float l_row = wave_sum_xor<16>(l_run);
+  l_row = wave_sum_xor<32>(l_row);
   float m_row = m_run;
   if (keysplit) {
     // Merge the four waves' states (disjoint key tiles) through LDS.

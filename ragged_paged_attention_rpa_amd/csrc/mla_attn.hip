@@ -67,25 +67,28 @@ struct RowSrc {
   int64_t sa, sb;
 };
 
-// DMA of block keys [8*grp, 8*grp + 8): their latent parts (one instruction
-// per key, 64 lanes x 16 bytes) and rope parts (one instruction, 8 keys x 8
-// lanes). `row` is the physical row of block key 8*grp + lane/8, or -1 for a
-// key that reads as zeros; the latent instructions take their row by readlane.
-__device__ __forceinline__ void issue_keys8(const RowSrc& src, uint32_t stage, int grp, int row) {
+// DMA instruction k (0..8) of block keys [8*grp, 8*grp + 8): k < 8 moves
+// the latent part of key 8*grp + k (64 lanes x 16 bytes), k = 8 the rope
+// parts of all eight keys (8 keys x 8 lanes). `row` is the physical row of
+// block key 8*grp + lane/8, or -1 for a key that reads as zeros; a latent
+// instruction takes its row by readlane and uses it as a scalar base with a
+// per-lane 32-bit offset.
+__device__ __forceinline__ void issue_key_dma(const RowSrc& src, uint32_t stage, int grp, int row,
+                                              int k) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int ii = 0; ii < 8; ++ii) {
-    const int r = __builtin_amdgcn_readlane(row, 8 * ii);
-    const int key = 8 * grp + ii;
+  if (k < 8) {
+    const int r = __builtin_amdgcn_readlane(row, 8 * k);
+    const int key = 8 * grp + k;
     const char* base = r >= 0 ? src.a + (int64_t)r * src.sa : (const char*)kZeroRow;
-    dma_b128(base + ((lane ^ swz(key)) << 4),
-             __builtin_amdgcn_readfirstlane(stage + (uint32_t)key * kKvcBytes));
+    dma_b128_s(base, xor_here((uint32_t)lane << 4, (uint32_t)(swz(key) << 4)),
+               __builtin_amdgcn_readfirstlane(stage + (uint32_t)key * kKvcBytes));
+  } else {
+    const int key = 8 * grp + (lane >> 3);
+    const char* base =
+        row >= 0 ? src.b + (int64_t)row * src.sb : (const char*)kZeroRow + kKvcBytes;
+    dma_b128(base + (((lane & 7) ^ swz_pe(key)) << 4),
+             __builtin_amdgcn_readfirstlane(stage + (uint32_t)(kKpeOff + grp * 1024)));
   }
-  const int key = 8 * grp + (lane >> 3);
-  const char* base =
-      row >= 0 ? src.b + (int64_t)row * src.sb : (const char*)kZeroRow + kKvcBytes;
-  dma_b128(base + (((lane & 7) ^ swz_pe(key)) << 4),
-           __builtin_amdgcn_readfirstlane(stage + (uint32_t)(kKpeOff + grp * 1024)));
 }
 
 // Q^T operand of one wave, lane l = head l%16. The contraction order is free
@@ -129,26 +132,38 @@ __device__ __forceinline__ uint32_t v_lat() {
 // S^T[key, head] for NT 16-key tiles and NH 16-head tiles; lat/rope are the
 // lane operand addresses of the first tile (stage included). Each K read
 // feeds NH MFMAs; the NT tiles give independent accumulation chains.
-template <int NT, int NH>
+// after_step(j) runs after the MFMAs of k-step j (the callers issue the next
+// block's DMA from it, spread over the k-steps).
+template <int NT, int NH, typename F>
 __device__ __forceinline__ void score_tiles(floatx4 (&sv)[NT][NH], uint32_t lat, uint32_t rope,
-                                            const u32x4 (&qv)[NH][kQSteps]) {
+                                            const u32x4 (&qv)[NH][kQSteps], F&& after_step) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int h = 0; h < NH; ++h) sv[t][h] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto kread = [&](int j, int t) -> u32x4 {
+    return j < 16 ? lds_read_b128((lat ^ (uint32_t)(j << 4)) + t * kTileKvc)
+                  : lds_read_b128((rope ^ (uint32_t)((j - 16) << 4)) + t * kTileKpe);
+  };
+  // The K reads of k-step j + 1 are issued before the MFMAs of k-step j.
+  u32x4 kf[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) kf[t] = kread(0, t);
 #pragma unroll
   for (int j = 0; j < kQSteps; ++j) {
-    u32x4 kf[NT];
+    u32x4 kn[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      kf[t] = j < 16 ? lds_read_b128((lat ^ (uint32_t)(j << 4)) + t * kTileKvc)
-                     : lds_read_b128((rope ^ (uint32_t)((j - 16) << 4)) + t * kTileKpe);
+    for (int t = 0; t < NT; ++t) kn[t] = j + 1 < kQSteps ? kread(j + 1, t) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pin_after(kf[t]);  // the prefetch stays ahead of this step's MFMAs
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < NH; ++h)
         sv[t][h] = mfma_16x16x32(as_bf16x8(kf[t]), as_bf16x8(qv[h][j]), sv[t][h]);
-    sched_fence();
+    after_step(j);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) kf[t] = kn[t];
   }
 }
 
@@ -182,12 +197,9 @@ constexpr int kMlaWaves = 8;
 constexpr int kMlaThreads = kMlaWaves * 64;
 constexpr int kMlaHT = 1;                             // 16-head tiles per wave
 constexpr int kMlaHeads = kMlaWaves * 16 * kMlaHT;    // heads per workgroup (128)
-constexpr int kMlaGroups = kBlk / 8 / kMlaWaves;      // 8-key DMA groups per wave
-constexpr int kMlaIPW = kMlaGroups * kDmaPer8;        // DMA instructions per wave per block
 constexpr int kPageWin = 1024;                        // page ids cached in LDS
 constexpr int kMlaMaxSplits = 16;
 constexpr int kMlaMinChunk = 256;
-constexpr int kPvStep = 2;                            // V tiles per PV step
 
 struct MlaSeq {
   int cu0, q_len, kv_len, kv_cap;
@@ -335,10 +347,13 @@ struct MlaShared {
 };
 static_assert(sizeof(MlaShared) <= 160 * 1024, "MLA LDS budget");
 
+// One tile: 128 heads (16 per wave) of one query token over a key range; a
+// 64-key block is taken as two halves of 32 keys, each with its own softmax
+// step, which keeps the per-step registers small.
 __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int ps_log2, int chunk) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int g = lane >> 4;
   const int seq = tl.x;
   const MlaSeq s = mla_seq(a, seq);
@@ -397,11 +412,11 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
   const uint32_t st1 = lds_addr(sm.stage[1]);
   const int P = a.total_num_pages;
 
-  // This wave's DMA groups of block b: each lane resolves the row of its key
-  // (key 8*grp + lane/8) before the group's first DMA instruction.
-  auto issue = [&](int b, uint32_t st) {
+  // Row of this wave's key 8*wave + lane/8 of block b (the wave moves keys
+  // 8*wave .. +7 of every block). Called by all waves at the same point: a
+  // page-window refill synchronises the workgroup.
+  auto prep_rows = [&](int b) -> int {
     const int kb = kb0 + b * kBlk;
-    // Refill the page window when this block runs past it.
     if (((kb + kBlk - 1) >> ps_log2) - pwin >= kPageWin) {
       wg_barrier();
       pwin = kb >> ps_log2;
@@ -411,121 +426,144 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
       }
       __syncthreads();
     }
-    int rows[kMlaGroups];
-#pragma unroll
-    for (int gi = 0; gi < kMlaGroups; ++gi) {
-      const int key = kb + 8 * (wave * kMlaGroups + gi) + (lane >> 3);
-      int row = -1;
-      if (key >= lo && key < hi) {
-        const int page = sm.pages[(key >> ps_log2) - pwin];
-        if (page >= 0 && page < P) row = (page << ps_log2) + (key & ps_mask);
-      }
-      rows[gi] = row;
+    const int key = kb + 8 * wave + (lane >> 3);
+    int row = -1;
+    if (key >= lo && key < hi) {
+      const int page = sm.pages[(key >> ps_log2) - pwin];
+      if (page >= 0 && page < P) row = (page << ps_log2) + (key & ps_mask);
     }
-#pragma unroll
-    for (int gi = 0; gi < kMlaGroups; ++gi) issue_keys8(src, st, wave * kMlaGroups + gi, rows[gi]);
+    return row;
   };
 
-  const float sc = a.score_scale;
-  const float cap = a.soft_cap;
+  // Log2-domain logit of a raw score: s * scale * log2(e), or with the soft
+  // cap c, c * tanh(s * scale / c) * log2(e) = c2 - c3 / (2^{s * c1} + 1).
+  const bool capped = a.soft_cap != 0.f;
+  const float c1 = capped ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
+  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
+  auto logit = [&](float sraw) -> float {
+    if (!capped) return sraw * c1;
+    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
+  };
   const uint32_t klat = k_lat(), krope = k_rope(), vlat = v_lat();
   drain_vmem_before_loop();
-  if (nblk > 0) issue(0, st0);
+  if (nblk > 0) {
+    const int row0 = prep_rows(0);
+#pragma unroll
+    for (int k = 0; k < kDmaPer8; ++k) issue_key_dma(src, st0, wave, row0, k);
+  }
   for (int b = 0; b < nblk; ++b) {
     const uint32_t cur = (b & 1) ? st1 : st0;
-    if (b + 1 < nblk) {
-      issue(b + 1, (b & 1) ? st0 : st1);
-      wait_vmcnt<kMlaIPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    const uint32_t nxt = (b & 1) ? st0 : st1;
+    // Block b was issued during the previous block's work; the barrier also
+    // means every wave is done with stage nxt, which block b + 1 now fills.
+    wait_vmcnt<0>();
     wg_barrier();
-    if (wave_active) {
-      // The block is taken as two halves of 32 keys, each with its own
-      // softmax step, which keeps the per-step registers small.
-#pragma unroll 1
-      for (int half = 0; half < 2; ++half) {
-        const int kb = kb0 + b * kBlk + 32 * half;
-        const uint32_t hc = cur + (uint32_t)(2 * half * kTileKvc);
-        u32x4 pb[kMlaHT];
-        floatx4 sv[2][kMlaHT];
-        score_tiles<2, kMlaHT>(sv, hc + klat, cur + (uint32_t)(2 * half * kTileKpe) + krope, qv);
+    const bool more = b + 1 < nblk;
+    const int nrow = more ? prep_rows(b + 1) : -1;
+    if (!wave_active) {
+      if (more) {
 #pragma unroll
-        for (int h = 0; h < kMlaHT; ++h) {
-          float mblk = -INFINITY;
+        for (int k = 0; k < kDmaPer8; ++k) issue_key_dma(src, nxt, wave, nrow, k);
+      }
+      continue;
+    }
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int kb = kb0 + b * kBlk + 32 * half;
+      const uint32_t hc = cur + (uint32_t)(2 * half * kTileKvc);
+      u32x4 pb[kMlaHT];
+      floatx4 sv[2][kMlaHT];
+      // The first half's k-steps carry this wave's DMA of block b + 1.
+      const bool dma_here = more && half == 0;
+      score_tiles<2, kMlaHT>(sv, hc + klat, cur + (uint32_t)(2 * half * kTileKpe) + krope, qv,
+                             [&](int j) {
+                               if (j < kDmaPer8 && dma_here) issue_key_dma(src, nxt, wave, nrow, j);
+                             });
+#pragma unroll
+      for (int h = 0; h < kMlaHT; ++h) {
+        float mblk = -INFINITY;
+        if (kb >= lo && kb + 32 <= hi) {  // all 32 keys visible: no mask
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              sv[kt][h][i] = logit(sv[kt][h][i]);
+              mblk = fmaxf(mblk, sv[kt][h][i]);
+            }
+        } else {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int key = kb + 16 * kt + 4 * g + i;
-              const float x =
-                  (key >= lo && key < hi) ? score_log2(sv[kt][h][i], sc, cap) : -INFINITY;
+              const float x = (key >= lo && key < hi) ? logit(sv[kt][h][i]) : -INFINITY;
               sv[kt][h][i] = x;
               mblk = fmaxf(mblk, x);
             }
-          mblk = wave_max_xor(mblk, 16);
-          mblk = wave_max_xor(mblk, 32);
-          const bool need = mblk > m_run[h] + kLazyTau;
-          if (wave_any(need)) {
-            const float m_new = need ? mblk : m_run[h];
-            const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.f;  // rows not moving keep scale 1
-            l_run[h] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < kDvTiles; ++dt) {
-              acc[h][dt][0] *= alpha;
-              acc[h][dt][1] *= alpha;
-              acc[h][dt][2] *= alpha;
-              acc[h][dt][3] *= alpha;
-            }
-            m_run[h] = m_new;
-          }
-          pb[h] = u32x4{0u, 0u, 0u, 0u};
-          if (m_run[h] != -INFINITY) {
-            float psum = 0.f;
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                sv[kt][h][i] = fast_exp2(sv[kt][h][i] - m_run[h]);
-                psum += sv[kt][h][i];
-              }
-            l_run[h] += psum;
-            pb[h][0] = pack_bf16x2(sv[0][h][0], sv[0][h][1]);
-            pb[h][1] = pack_bf16x2(sv[0][h][2], sv[0][h][3]);
-            pb[h][2] = pack_bf16x2(sv[1][h][0], sv[1][h][1]);
-            pb[h][3] = pack_bf16x2(sv[1][h][2], sv[1][h][3]);
-          }
         }
-        // O^T += V^T P^T over the 32 keys (one k-step: tiles 2*half and 2*half + 1).
-        const uint32_t vcur = hc + vlat;
+        mblk = wave_max_xor<16>(mblk);
+        mblk = wave_max_xor<32>(mblk);
+        const bool need = mblk > m_run[h] + kLazyTau;
+        if (wave_any(need)) {
+          const float m_new = need ? mblk : m_run[h];
+          const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.f;  // rows not moving keep scale 1
+          l_run[h] *= alpha;
 #pragma unroll
-        for (int dt0 = 0; dt0 < kDvTiles; dt0 += kPvStep) {
-          u32x4 vf[kPvStep];
-#pragma unroll
-          for (int d = 0; d < kPvStep; ++d) {
-            const uint32_t va = vcur ^ (uint32_t)((dt0 + d) << 5);
-            const u32x2 v0 = lds_read_tr16(va);
-            const u32x2 v1 = lds_read_tr16(va + kTileKvc);
-            vf[d] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          for (int dt = 0; dt < kDvTiles; ++dt) {
+            acc[h][dt][0] *= alpha;
+            acc[h][dt][1] *= alpha;
+            acc[h][dt][2] *= alpha;
+            acc[h][dt][3] *= alpha;
           }
+          m_run[h] = m_new;
+        }
+        pb[h] = u32x4{0u, 0u, 0u, 0u};
+        if (m_run[h] != -INFINITY) {
+          float psum = 0.f;
 #pragma unroll
-          for (int d = 0; d < kPvStep; ++d)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int h = 0; h < kMlaHT; ++h)
-              acc[h][dt0 + d] = mfma_16x16x32(as_bf16x8(vf[d]), as_bf16x8(pb[h]), acc[h][dt0 + d]);
-          sched_fence();
+            for (int i = 0; i < 4; ++i) {
+              sv[kt][h][i] = fast_exp2(sv[kt][h][i] - m_run[h]);
+              psum += sv[kt][h][i];
+            }
+          l_run[h] += psum;
+          pb[h][0] = pack_bf16x2(sv[0][h][0], sv[0][h][1]);
+          pb[h][1] = pack_bf16x2(sv[0][h][2], sv[0][h][3]);
+          pb[h][2] = pack_bf16x2(sv[1][h][0], sv[1][h][1]);
+          pb[h][3] = pack_bf16x2(sv[1][h][2], sv[1][h][3]);
         }
       }
+      // O^T += V^T P^T over the 32 keys (one k-step: tiles 2*half and
+      // 2*half + 1). The V^T reads of tile dt + 1 are issued before the MFMA
+      // of tile dt, so one LDS round trip overlaps one MFMA.
+      const uint32_t vcur = hc + vlat;
+      u32x2 v0 = lds_read_tr16(vcur), v1 = lds_read_tr16(vcur + kTileKvc);
+#pragma unroll
+      for (int dt = 0; dt < kDvTiles; ++dt) {
+        u32x2 n0 = {0u, 0u}, n1 = {0u, 0u};
+        if (dt + 1 < kDvTiles) {
+          const uint32_t va = xor_here(vcur, (uint32_t)((dt + 1) << 5));
+          n0 = lds_read_tr16(va);
+          n1 = lds_read_tr16(va + kTileKvc);
+        }
+        u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
+        pin_after(vf);  // the prefetch stays ahead of this tile's MFMA
+#pragma unroll
+        for (int h = 0; h < kMlaHT; ++h)
+          acc[h][dt] = mfma_16x16x32(as_bf16x8(vf), as_bf16x8(pb[h]), acc[h][dt]);
+        v0 = n0;
+        v1 = n1;
+      }
     }
-    wg_barrier();
   }
 
   if (!wave_active) return;
 #pragma unroll
   for (int h = 0; h < kMlaHT; ++h) {
     const int head = head0 + 16 * h + (lane & 15);
-    float l_row = wave_sum_xor(l_run[h], 16);
-    l_row = wave_sum_xor(l_row, 32);
+    float l_row = wave_sum_xor<16>(l_run[h]);
+    l_row = wave_sum_xor<32>(l_row);
     if (head >= a.num_heads) continue;
     if (split >= 0 && nsplit > 1) {
       const int64_t pidx = (int64_t)seq * kMlaMaxSplits + split;
@@ -636,7 +674,7 @@ sparse_mla_kernel(SparseArgs a) {
   __shared__ __attribute__((aligned(1024))) SparseShared sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int g = lane >> 4;
   const int qi = blockIdx.x;
   const int hbase = blockIdx.y * 16;
@@ -685,11 +723,10 @@ sparse_mla_kernel(SparseArgs a) {
   const int total = K * RB;
   const int nblk = cdiv_i(total, kBlk);
 
-  // This wave's two DMA groups of block b (keys 16*wave .. +15, the keys it
-  // also multiplies). Each lane resolves the row of key 8*grp + lane/8; the
-  // validity of the group's keys is returned as a lane mask (bit 8i: key i).
-  auto issue = [&](int b, uint32_t st, uint64_t* vmask) {
-    int rows[kSpGroups];
+  // Rows of this wave's two 8-key DMA groups of block b (keys 16*wave .. +15,
+  // the keys it also multiplies): lane l resolves key 8*gi + l/8 of group gi.
+  // The validity of a group's keys comes back as a lane mask (bit 8i: key i).
+  auto prep_rows = [&](int b, int* rows, uint64_t* vmask) {
 #pragma unroll
     for (int gi = 0; gi < kSpGroups; ++gi) {
       const int kk = b * kBlk + 16 * wave + 8 * gi + (lane >> 3);
@@ -704,8 +741,6 @@ sparse_mla_kernel(SparseArgs a) {
       rows[gi] = row;
       vmask[gi] = __builtin_amdgcn_ballot_w64(row >= 0);
     }
-#pragma unroll
-    for (int gi = 0; gi < kSpGroups; ++gi) issue_keys8(src, st, 2 * wave + gi, rows[gi]);
   };
 
   const float sc = a.score_scale;
@@ -714,21 +749,31 @@ sparse_mla_kernel(SparseArgs a) {
   const uint32_t vlat = v_lat() + wave * kTileKvc;
   uint64_t vm_cur[kSpGroups] = {0, 0}, vm_next[kSpGroups] = {0, 0};
   drain_vmem_before_loop();
-  if (nblk > 0) issue(0, st0, vm_next);
+  if (nblk > 0) {
+    int rows0[kSpGroups];
+    prep_rows(0, rows0, vm_next);
+#pragma unroll
+    for (int j = 0; j < kSpIPW; ++j)
+      issue_key_dma(src, st0, kSpGroups * wave + j / kDmaPer8, rows0[j / kDmaPer8], j % kDmaPer8);
+  }
   for (int b = 0; b < nblk; ++b) {
-    const int cs = b & 1;
-    const uint32_t cur = cs ? st1 : st0;
+    const uint32_t cur = (b & 1) ? st1 : st0;
+    const uint32_t nxt = (b & 1) ? st0 : st1;
     vm_cur[0] = vm_next[0];
     vm_cur[1] = vm_next[1];
-    if (b + 1 < nblk) {
-      issue(b + 1, cs ? st0 : st1, vm_next);
-      wait_vmcnt<kSpIPW>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // Block b was issued during the previous block's work; after the barrier
+    // every wave is also done with stage nxt, which block b + 1 now fills.
+    wait_vmcnt<0>();
     wg_barrier();
+    const bool more = b + 1 < nblk;
+    int nrows[kSpGroups] = {-1, -1};
+    if (more) prep_rows(b + 1, nrows, vm_next);
     floatx4 sv2[1][1];
-    score_tiles<1, 1>(sv2, (cur + klat), (cur + krope), qv);
+    // One DMA instruction of block b + 1 after each of the 18 k-steps.
+    score_tiles<1, 1>(sv2, (cur + klat), (cur + krope), qv, [&](int j) {
+      if (more)
+        issue_key_dma(src, nxt, kSpGroups * wave + j / kDmaPer8, nrows[j / kDmaPer8], j % kDmaPer8);
+    });
     floatx4 sv = sv2[0][0];
     // Keys 4g + i of this wave's tile: group g/2, bit 8*(4(g&1) + i) of its mask.
     const uint64_t vm = (g >> 1) ? vm_cur[1] : vm_cur[0];
@@ -740,8 +785,8 @@ sparse_mla_kernel(SparseArgs a) {
       sv[i] = x;
       mblk = fmaxf(mblk, x);
     }
-    mblk = wave_max_xor(mblk, 16);
-    mblk = wave_max_xor(mblk, 32);
+    mblk = wave_max_xor<16>(mblk);
+    mblk = wave_max_xor<32>(mblk);
     const bool need = mblk > m_run + kLazyTau;
     if (wave_any(need)) {
       const float m_new = need ? mblk : m_run;
@@ -774,11 +819,10 @@ sparse_mla_kernel(SparseArgs a) {
       for (int d = 0; d < 4; ++d) acc[dt0 + d] = mfma_16x16x16(vt[d], pb, acc[dt0 + d]);
       sched_fence();
     }
-    wg_barrier();
   }
   // The four waves hold the softmax state of disjoint key tiles: merge in LDS.
-  float l_row = wave_sum_xor(l_run, 16);
-  l_row = wave_sum_xor(l_row, 32);
+  float l_row = wave_sum_xor<16>(l_run);
+  l_row = wave_sum_xor<32>(l_row);
   __syncthreads();
   float* accs = reinterpret_cast<float*>(sm.stage[0]);             // [4][16][512]
   float* mls = accs + kSpWaves * 16 * kDl;                          // [4][16][2]

@@ -80,16 +80,48 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const bf16x8& a, const bf16x8& 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float floatx16 __attribute__((__vector_size__(16 * sizeof(float))));
+
+// D(32x32 f32) += A(32x16 bf16) * B(16x32 bf16) on one wave (twice the rate
+// of the 16x16x32 form on gfx950). Lane l holds A[l%32][8*(l/32) .. +7],
+// B[8*(l/32) .. +7][l%32], and D[8*(r/4) + 4*(l/32) + r%4][l%32] in register r.
+__device__ __forceinline__ floatx16 mfma_32x32x16(const bf16x8& a, const bf16x8& b,
+                                                  const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ float wave_max_xor(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask, 64));
+// {v of lane l, v of lane l ^ 16} (MASK 16) or {.., l ^ 32} (MASK 32) with
+// gfx950's v_permlane16_swap / v_permlane32_swap: swapping v with itself
+// leaves the even row's (even half's) value in the first result and the odd
+// row's (odd half's) in the second, in both lanes of the pair. Plain VALU
+// ops, unlike a ds_bpermute shuffle.
+template <int MASK>
+__device__ __forceinline__ void pair_xor(float v, float& a, float& b) {
+  static_assert(MASK == 16 || MASK == 32, "row or half swap only");
+  const uint32_t u = __float_as_uint(v);
+  const auto r = MASK == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                            : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ float wave_sum_xor(float v, int mask) {
-  return v + __shfl_xor(v, mask, 64);
+// max / sum of v over lanes l and l ^ MASK (MASK = 16 or 32); the sum adds
+// in the same order in both lanes, so they get identical bits.
+template <int MASK>
+__device__ __forceinline__ float wave_max_xor(float v) {
+  float a, b;
+  pair_xor<MASK>(v, a, b);
+  return fmaxf(a, b);
+}
+template <int MASK>
+__device__ __forceinline__ float wave_sum_xor(float v) {
+  float a, b;
+  pair_xor<MASK>(v, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ int cdiv_i(int a, int b) { return (a + b - 1) / b; }
@@ -137,6 +169,27 @@ __device__ __forceinline__ void dma_b128(const void* gaddr, uint32_t lds_base) {
       : "memory");
 }
 
+// As dma_b128 with a wave-uniform 64-bit base (SGPRs) plus a per-lane 32-bit
+// byte offset: lane L's 16 bytes at sbase + voff land at lds_base + 16*L.
+__device__ __forceinline__ void dma_b128_s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_nop 4"
+      :
+      : "s"(lds_base), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// x ^ s computed where it stands: the asm keeps the compiler from hoisting a
+// set of such values out of a loop and holding (or spilling) them.
+__device__ __forceinline__ uint32_t xor_here(uint32_t x, uint32_t s) {
+  uint32_t r;
+  asm volatile("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(s), "v"(x));
+  return r;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
@@ -152,6 +205,33 @@ __device__ __forceinline__ void drain_vmem_before_loop() { __builtin_amdgcn_s_wa
 // Compiler-only fence: memory accesses are not moved across it. Used to keep
 // the scheduler from hoisting a whole unrolled loop's LDS loads at once.
 __device__ __forceinline__ void sched_fence() { asm volatile("" : : : "memory"); }
+
+// Compiler fence that also pins `x`: memory accesses stay on their side of it
+// and every later use of x stays below it. Placed after a prefetch, it keeps
+// the MFMA that consumes x from being scheduled above the prefetch.
+template <typename T>
+__device__ __forceinline__ void pin_after(T& x) {
+  asm volatile("" : "+v"(x) : : "memory");
+}
+
+// x *= alpha for an MFMA accumulator element kept in an AGPR: the constraint
+// keeps the value in its AGPR (a plain multiply would make the compiler hold
+// the whole accumulator set in VGPRs around a rarely taken rescale).
+__device__ __forceinline__ void scale_acc(float& x, float alpha) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(alpha));
+}
+
+// Wait states between the MFMA that last wrote an accumulator and the
+// hand-written AGPR accesses above (and between those and the next MFMA).
+__device__ __forceinline__ void mfma_agpr_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
 
 // Workgroup barrier without the fence __syncthreads() carries (that fence
 // would drain outstanding LDS DMA); also a compiler barrier for memory.
