@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
     "mixed_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
     "tiny_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
     "mla_decode": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
-    "sparse_mla": "ragged_paged_attention_rpa_amd/csrc/sparse_mla.hip",
+    "sparse_mla": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
 }
 KERNEL_NAMES = {
     "decode_gqa": "gqa_tile_kernel",
