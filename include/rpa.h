@@ -127,11 +127,24 @@ const char* rpa_last_error(void);
  * Profiling hook for benchmarks. `start` and `stop` are hipEvent_t handles
  * created by the caller (NULL, NULL turns the hook off). While set, each
  * rpa_forward / mla_rpa_forward / sparse_mla_forward call on this host thread
- * records `start` on its stream right before its main attention kernel and
- * `stop` right after it, so hipEventElapsedTime(start, stop) is that kernel's
- * duration. The library does not own or destroy the events.
+ * records `start` on its stream right before its main attention kernel (for
+ * rpa_forward: the first of its prefill-tile and decode-tile kernels) and
+ * `stop` right after it (the last of them), so hipEventElapsedTime(start,
+ * stop) is the attention kernels' duration without the work-list planner and
+ * the split merge. The library does not own or destroy the events.
  */
 void rpa_set_profile_events(void* start, void* stop);
+
+/*
+ * Per-kernel profiling hook of rpa_forward. While set (both events of a pair
+ * non-NULL), each rpa_forward call on this host thread records pre_start /
+ * pre_stop around its prefill-tile kernel (launched only when that kernel
+ * serves the call's shapes) and dec_start / dec_stop around its decode-tile
+ * kernel. NULL pairs turn the respective hook off. The library does not own
+ * or destroy the events.
+ */
+void rpa_set_profile_events_split(void* pre_start, void* pre_stop, void* dec_start,
+                                  void* dec_stop);
 
 /*
  * Workspace bytes rpa_forward needs for these capacities (host-only query;

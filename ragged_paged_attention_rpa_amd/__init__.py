@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "librpa.so")
 
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
 EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_set_profile_events",
+                    "rpa_set_profile_events_split",
                     "rpa_workspace_size", "rpa_forward",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
                     "sparse_mla_workspace_size", "sparse_mla_forward")
@@ -80,6 +81,8 @@ def load_library():
     lib.rpa_last_error.restype = ctypes.c_char_p
     lib.rpa_set_profile_events.argtypes = [P, P]
     lib.rpa_set_profile_events.restype = None
+    lib.rpa_set_profile_events_split.argtypes = [P, P, P, P]
+    lib.rpa_set_profile_events_split.restype = None
     lib.rpa_workspace_size.argtypes = [MP, I32, I32, I32, I32]
     lib.rpa_workspace_size.restype = SZ
     lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P, SZ, P]

@@ -220,8 +220,11 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
     }
   }
   if (blockIdx.x == 0 && tid == 0) {
+    const int npre = min(run_pre, total);
     a.counters[0] = total;
-    a.counters[1] = 0;
+    a.counters[1] = a.pre_kernel ? npre : 0;  // this file's kernel starts past them
+    a.counters[2] = 0;
+    a.counters[3] = a.pre_kernel ? npre : 0;
   }
 }
 
@@ -957,6 +960,14 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   // slower: the compute of a block is then exposed).
   const int grid = max(1, min(a.tile_capacity, num_cus() * 2));
   prof_begin(stream);
+  if (a.pre_kernel) {
+    // Prefill-class tiles first, on the eight-wave kernel (one workgroup per CU).
+    prof_kernel_begin(stream, 0);
+    const hipError_t e = launch_gqa_prefill(a, ps_log2, num_cus(), stream);
+    if (e != hipSuccess) return e;
+    prof_kernel_end(stream, 0);
+  }
+  prof_kernel_begin(stream, 1);
   const bool cap = a.soft_cap != 0.f;
 #define RPA_TILE_LAUNCH(DT, CAP)                                                         \
   hipLaunchKernelGGL((gqa_tile_kernel<DT, kStages, CAP>), dim3(grid), dim3(kThreads), 0, \
@@ -973,6 +984,7 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
       RPA_TILE_LAUNCH(DT_FP8, false);
   }
 #undef RPA_TILE_LAUNCH
+  prof_kernel_end(stream, 1);
   prof_end(stream);
   if (a.geo.qdec > 0)
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(a.max_num_seqs * a.num_kv_heads), dim3(kThreads),

@@ -1,0 +1,485 @@
+// Prefill-class tiles of GQA ragged paged attention on gfx950 [RPA v2 page:
+// ragged_paged_attention, flash_attention].
+//
+// A prefill tile is (sequence, kv head, block of query tokens): its rows are
+// the (query token, q head of the group) pairs, up to 256 of them, against
+// every key the block's queries can see. The per-row arithmetic is the
+// page's: scale, optional soft cap, mask (causal offset kv_len - q_len,
+// optional sliding window), online softmax, P V.
+//
+// Workgroup: eight waves, 32 rows each, in two groups of four (A = waves
+// 0..3, B = waves 4..7; wave w and wave w + 4 share a SIMD). Keys arrive in
+// blocks of 64 through a ring of LDS stages. Each wave alternates two kinds
+// of phase over the blocks:
+//   MFMA phase j:  O^T += V_{j-1}^T P_{j-1}^T, then S^T_j = K_j Q^T
+//                  (v_mfma_f32_32x32x16_bf16 throughout);
+//   VALU phase j:  the online softmax of S_j (mask, cap, row max, exp2,
+//                  row sum) producing P_j in bf16.
+// Group B runs one phase behind group A and every phase ends with a
+// workgroup barrier, so on each SIMD one wave multiplies while the other
+// does its softmax: the matrix core and the vector ALU work at the same
+// time instead of taking turns inside one wave.
+//
+// Operand layouts (32x32x16, lane l, c = l / 32):
+//  * S^T = K Q^T: A = 32 keys x 16 dims (lane: key l%32, dims 8c..), B = Q^T
+//    held in registers for the whole tile (lane: row l%32, dims 16ks + 8c..).
+//    Lane l ends with row l%32's scores for keys 8q + 4c + t in register
+//    4q + t of each 32-key half of the block.
+//  * O^T += V^T P^T over 16-key steps u: the step's reduction index 8c + jj
+//    is taken to mean key 16u + 4c + jj (jj < 4) or 16u + 4c + 8 + (jj - 4),
+//    which is exactly what lane l already holds (registers 8(u%2) .. +7 of
+//    half u/2), so P needs no shuffle; V^T is read in the same key order with
+//    two ds_read_b64_tr_b16 per operand.
+//
+// LDS block layout: key-major, 512 bytes per key (K dims in 16-byte columns
+// 0..15, V dims in 16..31); column q of key k sits at q ^ kswz(k), which
+// keeps the K reads (16 keys, one column) and the transposed V reads (four
+// keys, four columns) free of bank conflicts. The DMA (global_load_lds,
+// 1 KB per instruction) applies the swizzle by choosing which global column
+// each lane fetches. fp8 pools land raw (256 bytes per key, column rc at
+// rc ^ (k & 15)) and group A widens them to bf16 exactly during its VALU
+// phase.
+#include <type_traits>
+
+#include "rpa_device.h"
+#include "rpa_internal.h"
+
+namespace rpa {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBN = 64;                            // keys per block
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 32;
+constexpr int kKeyBytes = 512;                     // K + V of one key, bf16
+constexpr int kRawKeyBytes = 256;                  // K + V of one key, fp8
+constexpr int kStage = kBN * kKeyBytes;            // 32 KB
+constexpr int kRawStage = kBN * kRawKeyBytes;      // 16 KB
+constexpr int kBf16Stages = 4;                     // bf16 pools: DMA ring
+constexpr int kConvStages = 3;                     // fp8 pools: widened ring
+constexpr int kRawStages = 2;                      // fp8 pools: raw DMA ring
+
+__device__ __attribute__((aligned(16))) const uint8_t kPreZero[512] = {0};
+
+template <int KV_DT>
+struct PreSmem {
+  char buf[KV_DT == DT_BF16 ? kBf16Stages * kStage : kConvStages * kStage + kRawStages * kRawStage];
+  int tile;
+};
+
+// Column swizzle of a key (its low four bits): a bit rotation, so sixteen
+// consecutive keys get sixteen distinct columns, and the four keys of an
+// aligned quad get distinct values in bits 2..3.
+__device__ __forceinline__ int kswz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+
+__device__ __forceinline__ uint32_t key_col(int key, int q) {
+  return (uint32_t)(key * kKeyBytes + ((q ^ kswz(key)) << 4));
+}
+
+// Scalar (SGPR) read of a wave-uniform int32 from global memory.
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) int32_t*>(
+      (const __attribute__((address_space(4))) char*)p);
+}
+
+template <int KV_DT, bool CAP>
+__device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& sm, int ps_log2) {
+  constexpr bool F8 = KV_DT == DT_FP8;
+  constexpr int kIPW = (F8 ? kRawStage : kStage) / 1024 / kWaves;  // DMA instructions per wave per block
+  constexpr int kEB = F8 ? 1 : 2;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int c = lane >> 5;
+  const int G = a.geo.group;
+  const int W = a.geo.window;
+
+  // Tile and sequence metadata are workgroup-uniform: keep them in SGPRs.
+  const int seq = __builtin_amdgcn_readfirstlane(tile.seq);
+  const int qtok0 = __builtin_amdgcn_readfirstlane(tile.qtok0);
+  const int kvh = __builtin_amdgcn_readfirstlane(tile.kvh);
+  const int cu0 = __builtin_amdgcn_readfirstlane(a.cu_q_lens[seq]);
+  const int q_len = __builtin_amdgcn_readfirstlane(a.cu_q_lens[seq + 1]) - cu0;
+  const int kv_len = __builtin_amdgcn_readfirstlane(a.kv_lens[seq]);
+  const int kv_cap = min(kv_len, a.pages_per_seq << ps_log2);
+  const int ntok = min(a.geo.bq, q_len - qtok0);
+  const int first = kv_len - q_len + qtok0;  // position of the block's first query
+  const int lo = W > 0 ? max(0, first - W + 1) : 0;
+  const int hi = min(first + ntok, kv_cap);
+  const int nrows = ntok * G;
+
+  const int r = kRowsPerWave * wave + (lane & 31);
+  const bool row_ok = r < nrows;
+  const bool wave_active = kRowsPerWave * wave < nrows;
+  const int qpos = first + r / G;
+  // Keys row r sees: [vlo_r, vhi_r) (empty past the tile's rows).
+  const int vlo_r = row_ok ? max(lo, W > 0 ? qpos - W + 1 : 0) : 0;
+  const int vhi_r = row_ok ? min(hi, qpos + 1) : 0;
+
+  // Q^T operand, k-step ks: row r, dims 16ks + 8c .. +7.
+  u32x4 qv[8];
+  {
+    const int tok = cu0 + qtok0 + (row_ok ? r / G : 0);
+    const int head = kvh * G + (row_ok ? r % G : 0);
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.num_q_heads + head) * kD + 8 * c;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      qv[ks] = v;
+    }
+  }
+
+  floatx16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
+  }
+  floatx16 sv[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sv[tt][i] = 0.f;
+  u32x4 pb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) pb[u] = u32x4{0u, 0u, 0u, 0u};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kb0 = (lo / kBN) * kBN;
+  const int nblk = hi > kb0 ? cdiv_i(hi - kb0, kBN) : 0;
+  const int32_t* table = a.page_indices + (int64_t)seq * a.pages_per_seq;
+  const int ps_mask = (1 << ps_log2) - 1;
+  const int64_t token_bytes = (int64_t)2 * a.num_kv_heads * kD * kEB;
+  const char* kv_head = (const char*)a.kv + (int64_t)(2 * kvh) * kD * kEB;
+  const uint32_t sbase = lds_addr(sm.buf);
+
+  // LDS byte address of the bf16 block j, and (fp8) of its raw copy.
+  auto stage = [&](int j) -> uint32_t {
+    return sbase + (uint32_t)(j % (F8 ? kConvStages : kBf16Stages)) * kStage;
+  };
+  auto raw_stage = [&](int j) -> uint32_t {
+    return sbase + (uint32_t)(kConvStages * kStage) + (uint32_t)(j % kRawStages) * kRawStage;
+  };
+
+  // This wave's share of block j: keys k8 .. k8 + 7, all in one page (page
+  // size >= 8), whose id comes through a scalar load. Keys outside [lo, hi)
+  // or on an invalid page read zeros instead.
+  auto issue = [&](int j) {
+    const int k8 = kb0 + j * kBN + 8 * wave;
+    const int lp = min(k8 >> ps_log2, a.pages_per_seq - 1);
+    const int page = load_uniform(table + lp);
+    const bool page_ok = page >= 0 && page < a.total_num_pages;
+    const char* rowbase = kv_head + (((int64_t)page << ps_log2) + (k8 & ps_mask)) * token_bytes;
+    const uint32_t dst = F8 ? raw_stage(j) : stage(j);
+#pragma unroll
+    for (int ii = 0; ii < kIPW; ++ii) {
+      const int sub = F8 ? lane >> 4 : lane >> 5;
+      const int e = (F8 ? 4 : 2) * ii + sub;  // key within the wave's eight
+      const int key = k8 + e;
+      const int col = F8 ? ((lane & 15) ^ (key & 15)) : ((lane & 31) ^ kswz(key));
+      const bool ok = page_ok && key >= lo && key < hi;
+      const char* src = ok ? rowbase + e * token_bytes + (col << 4)
+                           : (const char*)kPreZero + (col << 4);
+      dma_b128(src, __builtin_amdgcn_readfirstlane(dst + (uint32_t)(wave * kIPW + ii) * 1024));
+    }
+  };
+
+  // fp8: widen raw block j into bf16 stage j (group A's 256 threads; thread
+  // t takes raw column t/16 of keys t%16 + 16i). Exact: every E4M3FN value
+  // is a bf16 value.
+  auto widen = [&](int j) {
+    const uint32_t src = raw_stage(j), dst = stage(j);
+    const int rc = tid >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = (tid & 15) + 16 * i;
+      const u32x4 w = lds_read_b128(src + (uint32_t)(key * kRawKeyBytes + ((rc ^ (key & 15)) << 4)));
+      u32x4 lo4, hi4;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t a0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h], 1.0f, false));
+        const uint32_t a1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h], 1.0f, true));
+        const uint32_t b0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h + 1], 1.0f, false));
+        const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h + 1], 1.0f, true));
+        if (h == 0) lo4 = u32x4{a0, a1, b0, b1};
+        else hi4 = u32x4{a0, a1, b0, b1};
+      }
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (__attribute__((address_space(3))) char*)(uintptr_t)(dst + key_col(key, 2 * rc))) = lo4;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (__attribute__((address_space(3))) char*)(uintptr_t)(dst + key_col(key, 2 * rc + 1))) = hi4;
+    }
+  };
+
+  // Operand bases. K: key lane%32 of a 32-key half, column 2ks + c, at
+  // kbase ^ (ks << 5). V^T: dims 16(lane/16 % 2) + lane%16 of a 32-dim tile
+  // for keys 4c + (lane%16)/4 (vlo) and the same + 8 (vhi), tile dt at ^ (dt << 6).
+  uint32_t kbase, vlo, vhi;
+  {
+    const int kk = lane & 31;
+    kbase = (uint32_t)(kk * kKeyBytes + ((c ^ kswz(kk)) << 4));
+    const int jj = lane & 15;
+    const int x = 16 + 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
+    const int k_lo = 4 * c + (jj >> 2), k_hi = k_lo + 8;
+    vlo = (uint32_t)(k_lo * kKeyBytes + ((x ^ kswz(k_lo)) << 4) + 8 * (jj & 1));
+    vhi = (uint32_t)(k_hi * kKeyBytes + ((x ^ kswz(k_hi)) << 4) + 8 * (jj & 1));
+  }
+
+  // Log2-domain logit relative to a reference mref: s * c1 - mref, or with the
+  // soft cap, cap * tanh(s * scale / cap) * log2(e) - mref with tanh(z) taken
+  // as 1 - 2 / (e^{2z} + 1) (hardware exp2 and reciprocal).
+  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
+  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
+
+  auto mfma_phase = [&](int j) {
+    if (j >= 1) {
+      const uint32_t st = stage(j - 1);
+      auto vread = [&](int u, int dt) -> u32x4 {
+        const uint32_t b = st + (uint32_t)(u * 16 * kKeyBytes);
+        const u32x2 v0 = lds_read_tr16(b + xor_here(vlo, (uint32_t)(dt << 6)));
+        const u32x2 v1 = lds_read_tr16(b + xor_here(vhi, (uint32_t)(dt << 6)));
+        return u32x4{v0[0], v0[1], v1[0], v1[1]};
+      };
+      u32x4 vf = vread(0, 0);
+#pragma unroll
+      for (int n = 0; n < 16; ++n) {
+        const int u = n >> 2, dt = n & 3;
+        u32x4 vn = {0u, 0u, 0u, 0u};
+        if (n + 1 < 16) vn = vread((n + 1) >> 2, (n + 1) & 3);
+        pin_after(vf);
+        acc[dt] = mfma_32x32x16(as_bf16x8(vf), as_bf16x8(pb[u]), acc[dt]);
+        vf = vn;
+      }
+    }
+    if (j < nblk) {
+      const uint32_t st = stage(j);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[tt][i] = 0.f;
+      auto kread = [&](int ks, int tt) -> u32x4 {
+        return lds_read_b128(st + (uint32_t)(tt * 32 * kKeyBytes) + xor_here(kbase, (uint32_t)(ks << 5)));
+      };
+      u32x4 kf0 = kread(0, 0), kf1 = kread(0, 1);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        u32x4 kn0 = {0u, 0u, 0u, 0u}, kn1 = {0u, 0u, 0u, 0u};
+        if (ks + 1 < 8) {
+          kn0 = kread(ks + 1, 0);
+          kn1 = kread(ks + 1, 1);
+        }
+        pin_after(kf0);
+        pin_after(kf1);
+        sv[0] = mfma_32x32x16(as_bf16x8(kf0), as_bf16x8(qv[ks]), sv[0]);
+        sv[1] = mfma_32x32x16(as_bf16x8(kf1), as_bf16x8(qv[ks]), sv[1]);
+        kf0 = kn0;
+        kf1 = kn1;
+      }
+    }
+  };
+
+  auto valu_phase = [&](int j) {
+    const int kb = kb0 + j * kBN;
+    // Keys [kb, kb + 64) visible to every row of the wave: no mask needed.
+    const bool full =
+        __builtin_amdgcn_ballot_w64(row_ok && !(kb >= vlo_r && kb + kBN <= vhi_r)) == 0;
+    const bool fresh = m_run == -INFINITY;
+    const float mref = fresh ? 0.f : m_run;
+    const float c2r = c2 - mref;
+    auto rel = [&](float s) -> float {
+      if (!CAP) return fmaf(s, c1, -mref);
+      return fmaf(__builtin_amdgcn_rcpf(fast_exp2(s * c1) + 1.f), -c3, c2r);
+    };
+    float mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sv[tt][i] = rel(sv[tt][i]);
+          mx = fmaxf(mx, sv[tt][i]);
+        }
+    } else {
+      const uint32_t span = (uint32_t)(vhi_r - vlo_r);
+      const int kbase_r = kb + 4 * c - vlo_r;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool vis = (uint32_t)(kbase_r + 32 * tt + 8 * (i >> 2) + (i & 3)) < span;
+          sv[tt][i] = vis ? rel(sv[tt][i]) : -INFINITY;
+          mx = fmaxf(mx, sv[tt][i]);
+        }
+    }
+    mx = wave_max_xor<32>(mx);
+    // Lazy reference: a row moves its reference (and rescales) only on its
+    // first visible block or when the block max passes it by kLazyTau.
+    const bool need = fresh ? mx != -INFINITY : mx > kLazyTau;
+    if (wave_any(need)) {
+      const float d = need ? mx : 0.f;
+      const float alpha = (need && !fresh) ? fast_exp2(-d) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+      m_run = need ? (fresh ? mx : m_run + d) : m_run;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[tt][i] -= d;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[tt][i] = fast_exp2(sv[tt][i]);
+    // P in bf16 for the PV step; the row sum is taken from the same rounded
+    // weights with v_dot2_f32_bf16 against (1, 1).
+    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+    float ls = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = pack_bf16x2(sv[u >> 1][8 * (u & 1) + 2 * i], sv[u >> 1][8 * (u & 1) + 2 * i + 1]);
+        pb[u][i] = w;
+        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, ls, false);
+      }
+    l_run += ls;
+  };
+
+  // Block j is issued at phase 2j - 4 (bf16) or its raw copy at 2j - 4 and
+  // widened at 2j - 1 (fp8); A reads it in phases 2j and 2j + 2, B in 2j + 1
+  // and 2j + 3. Every wave waits for its own DMA before the barrier that
+  // precedes the block's first use.
+  drain_vmem_before_loop();
+  for (int j = 0; j < 2 && j < nblk; ++j) issue(j);
+  if (nblk > 1)
+    wait_vmcnt<kIPW>();
+  else
+    wait_vmcnt<0>();
+  if (F8) {
+    wg_barrier();
+    if (grp == 0 && nblk > 0) widen(0);
+  }
+  __syncthreads();
+
+  // Closes phase p: this wave's DMA that the next phase needs has landed
+  // (bf16: block (p + 1) / 2 after odd p; fp8: raw block p / 2 + 1 after even
+  // p, before group A widens it), then the workgroup barrier.
+  auto close_phase = [&](int p) {
+    const int jw = F8 ? ((p & 1) == 0 ? p / 2 + 1 : -1) : ((p & 1) == 1 ? (p + 1) / 2 : -1);
+    if (jw >= 0 && jw < nblk) {
+      if (jw + 1 < nblk)
+        wait_vmcnt<kIPW>();
+      else
+        wait_vmcnt<0>();
+    }
+    if (F8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+  };
+  // Iteration j (0 .. nblk) spans phases 2j and 2j + 1. Group A: MFMA phase
+  // j, then VALU phase j. Group B: VALU phase j - 1, then MFMA phase j. Each
+  // group runs its own copy of the loop, so across its back edge only P (A)
+  // or S (B) is live.
+  auto run = [&](auto group_b) {
+    constexpr bool kB = decltype(group_b)::value;
+    for (int j = 0; j <= nblk; ++j) {
+      if (j + 2 < nblk) issue(j + 2);
+      if (wave_active) {
+        if constexpr (kB) {
+          if (j >= 1) valu_phase(j - 1);
+        } else {
+          mfma_phase(j);
+        }
+      }
+      close_phase(2 * j);
+      if constexpr (F8 && !kB) {
+        if (j + 1 < nblk) widen(j + 1);
+      }
+      if (wave_active) {
+        if constexpr (kB) {
+          mfma_phase(j);
+        } else {
+          if (j < nblk) valu_phase(j);
+        }
+      }
+      close_phase(2 * j + 1);
+    }
+  };
+  if (grp == 0)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
+
+  if (!wave_active) return;
+  // Normalise and store: row lane%32, dims 32dt + 8q + 4c .. +3 in registers
+  // 4q .. 4q + 3 of acc[dt].
+  float ap, bp;
+  pair_xor<32>(l_run, ap, bp);
+  const float l_row = ap + bp;
+  if (!row_ok) return;
+  const float inv = l_row > 0.f ? a.v_scale / l_row : 0.f;
+  const int tok = cu0 + qtok0 + r / G;
+  const int head = kvh * G + r % G;
+  uint16_t* op = (uint16_t*)a.out + ((int64_t)tok * a.num_q_heads + head) * kD + 4 * c;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[dt][4 * qq] * inv, acc[dt][4 * qq + 1] * inv);
+      w[1] = pack_bf16x2(acc[dt][4 * qq + 2] * inv, acc[dt][4 * qq + 3] * inv);
+      *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * qq) = w;
+    }
+}
+
+template <int KV_DT, bool CAP>
+__global__ void __launch_bounds__(kThreads, 1) gqa_prefill_kernel(GqaArgs a, int ps_log2) {
+  __shared__ __attribute__((aligned(16))) PreSmem<KV_DT> sm;
+  const int count = a.counters[3];
+  for (;;) {
+    if (threadIdx.x == 0) sm.tile = atomicAdd(&a.counters[2], 1);
+    __syncthreads();
+    const int ti = sm.tile;
+    __syncthreads();
+    if (ti >= count) break;
+    prefill_tile<KV_DT, CAP>(a, a.tiles[ti], sm, ps_log2);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+int gqa_prefill_rows() { return kWaves * kRowsPerWave; }
+
+bool gqa_prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group, int page_size) {
+  return q_dtype == DT_BF16 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && head_dim == kD &&
+         group >= 1 && group <= kWaves * kRowsPerWave && page_size >= 8 &&
+         (page_size & (page_size - 1)) == 0;
+}
+
+hipError_t launch_gqa_prefill(const GqaArgs& a, int ps_log2, int grid, hipStream_t stream) {
+  const bool cap = a.soft_cap != 0.f;
+#define RPA_PRE_LAUNCH(DT, CAP) \
+  hipLaunchKernelGGL((gqa_prefill_kernel<DT, CAP>), dim3(grid), dim3(kThreads), 0, stream, a, ps_log2)
+  if (a.kv_dtype == DT_BF16) {
+    if (cap)
+      RPA_PRE_LAUNCH(DT_BF16, true);
+    else
+      RPA_PRE_LAUNCH(DT_BF16, false);
+  } else {
+    if (cap)
+      RPA_PRE_LAUNCH(DT_FP8, true);
+    else
+      RPA_PRE_LAUNCH(DT_FP8, false);
+  }
+#undef RPA_PRE_LAUNCH
+  return hipGetLastError();
+}
+
+}  // namespace rpa

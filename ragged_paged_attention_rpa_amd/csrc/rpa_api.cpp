@@ -23,6 +23,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
+thread_local hipEvent_t g_prof_k[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
 
 rpa_status fail(rpa_status st, const char* fmt, ...) {
   char buf[512];
@@ -145,6 +146,12 @@ void prof_begin(hipStream_t stream) {
 void prof_end(hipStream_t stream) {
   if (g_prof_stop) (void)hipEventRecord(g_prof_stop, stream);
 }
+void prof_kernel_begin(hipStream_t stream, int k) {
+  if (g_prof_k[k][0]) (void)hipEventRecord(g_prof_k[k][0], stream);
+}
+void prof_kernel_end(hipStream_t stream, int k) {
+  if (g_prof_k[k][1]) (void)hipEventRecord(g_prof_k[k][1], stream);
+}
 }  // namespace rpa
 
 extern "C" {
@@ -156,6 +163,16 @@ void rpa_set_profile_events(void* start, void* stop) {
   } else {
     g_prof_start = nullptr;
     g_prof_stop = nullptr;
+  }
+}
+
+void rpa_set_profile_events_split(void* pre_start, void* pre_stop, void* dec_start,
+                                  void* dec_stop) {
+  void* e[2][2] = {{pre_start, pre_stop}, {dec_start, dec_stop}};
+  for (int k = 0; k < 2; ++k) {
+    const bool on = e[k][0] && e[k][1];
+    g_prof_k[k][0] = on ? reinterpret_cast<hipEvent_t>(e[k][0]) : nullptr;
+    g_prof_k[k][1] = on ? reinterpret_cast<hipEvent_t>(e[k][1]) : nullptr;
   }
 }
 
@@ -243,6 +260,12 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   if (meta->max_num_tokens == 0) return ok();
   if (mfma) {
     rpa::gqa_bind_workspace(a, workspace);
+    if (rpa::gqa_prefill_supported(a.q_dtype, a.kv_dtype, head_dim, a.geo.group, page_size)) {
+      // Prefill-class tiles of 256 rows for the eight-wave kernel (fewer tiles
+      // than the workspace was sized for).
+      a.pre_kernel = 1;
+      a.geo.bq = rpa::gqa_prefill_rows() / a.geo.group;
+    }
     return hip_status(rpa::launch_gqa(a, stream), "rpa_forward launch");
   }
   return hip_status(rpa::launch_gqa_generic(a, stream), "rpa_forward launch");

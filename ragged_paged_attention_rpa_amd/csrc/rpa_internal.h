@@ -12,6 +12,10 @@ namespace rpa {
 // main kernel of an entry point; no-ops when the hook is off.
 void prof_begin(hipStream_t stream);
 void prof_end(hipStream_t stream);
+// Per-kernel events of rpa_forward (rpa_set_profile_events_split): kernel 0 is
+// the prefill-tile kernel, kernel 1 the decode-tile kernel.
+void prof_kernel_begin(hipStream_t stream, int k);
+void prof_kernel_end(hipStream_t stream, int k);
 
 // ---------------------------------------------------------------- update ----
 struct KvUpdateArgs {
@@ -44,7 +48,8 @@ struct Tile {
 struct GqaGeometry {
   int group;        // Hq / Hkv
   int qdec;         // sequences with q_len <= qdec are decode-class (q_len*group <= 16)
-  int bq;           // query tokens per prefill-class tile (bq*group <= 64)
+  int bq;           // query tokens per prefill-class tile (bq*group <= 64 on the four-wave
+                    // kernel, <= 256 on the prefill kernel)
   int split_keys;   // target keys per decode split
   int max_splits;   // cap on splits per decode sequence
   int window;       // sliding window (0 = none)
@@ -65,9 +70,11 @@ struct GqaArgs {
   float soft_cap;     // 0 = none
   float v_scale;
   GqaGeometry geo;
+  int pre_kernel;     // 1: prefill-class tiles go to gqa_prefill_kernel (geo.bq = its rows / group)
   // workspace
   Tile* tiles;
-  int32_t* counters;  // [0] tile count, [1] work cursor
+  int32_t* counters;  // [0] tile count, [1] decode-kernel cursor (starts past the prefill
+                      // tiles when pre_kernel), [2] prefill-kernel cursor, [3] prefill tiles
   float* part_acc;    // [max_num_seqs*Hkv*max_splits][16][D]
   float* part_ml;     // [max_num_seqs*Hkv*max_splits][16][2]
   int tile_capacity;
@@ -81,6 +88,10 @@ void gqa_bind_workspace(GqaArgs& a, void* ws);
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream);
 hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream);
+// Prefill-class tiles on eight waves (gqa_prefill.hip).
+int gqa_prefill_rows();
+bool gqa_prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group, int page_size);
+hipError_t launch_gqa_prefill(const GqaArgs& a, int ps_log2, int grid, hipStream_t stream);
 
 // ------------------------------------------------------------------- MLA ----
 struct MlaArgs {
