@@ -223,8 +223,8 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
     const int npre = min(run_pre, total);
     a.counters[0] = total;
     a.counters[1] = a.pre_kernel ? npre : 0;  // this file's kernel starts past them
-    a.counters[2] = 0;
     a.counters[3] = a.pre_kernel ? npre : 0;
+    for (int x = 0; x < kXcds; ++x) a.counters[kXcdCursor0 + x] = 0;
   }
 }
 

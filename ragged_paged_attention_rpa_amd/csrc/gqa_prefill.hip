@@ -166,12 +166,15 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   };
 
   // This wave's share of block j: keys k8 .. k8 + 7, all in one page (page
-  // size >= 8), whose id comes through a scalar load. Keys outside [lo, hi)
-  // or on an invalid page read zeros instead.
-  auto issue = [&](int j) {
+  // size >= 8). Its id comes through a scalar load issued an iteration ahead
+  // of the DMA (page_of), so the DMA never waits for the page table. Keys
+  // outside [lo, hi) or on an invalid page read zeros instead.
+  auto page_of = [&](int j) -> int {
     const int k8 = kb0 + j * kBN + 8 * wave;
-    const int lp = min(k8 >> ps_log2, a.pages_per_seq - 1);
-    const int page = load_uniform(table + lp);
+    return load_uniform(table + min(k8 >> ps_log2, a.pages_per_seq - 1));
+  };
+  auto issue = [&](int j, int page) {
+    const int k8 = kb0 + j * kBN + 8 * wave;
     const bool page_ok = page >= 0 && page < a.total_num_pages;
     const char* rowbase = kv_head + (((int64_t)page << ps_log2) + (k8 & ps_mask)) * token_bytes;
     const uint32_t dst = F8 ? raw_stage(j) : stage(j);
@@ -192,12 +195,15 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   // t takes raw column t/16 of keys t%16 + 16i). Exact: every E4M3FN value
   // is a bf16 value.
   auto widen = [&](int j) {
-    const uint32_t src = raw_stage(j), dst = stage(j);
-    const int rc = tid >> 4;
+    // Keys tid%16 + 16i share their low four bits, hence their swizzles: one
+    // lane offset per side, the key step is a constant (4 KB raw, 8 KB bf16).
+    const int k0 = tid & 15, rc = tid >> 4;
+    const uint32_t src = raw_stage(j) + (uint32_t)(k0 * kRawKeyBytes + ((rc ^ k0) << 4));
+    const uint32_t dlo = stage(j) + key_col(k0, 2 * rc);
+    const uint32_t dhi = stage(j) + key_col(k0, 2 * rc + 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = (tid & 15) + 16 * i;
-      const u32x4 w = lds_read_b128(src + (uint32_t)(key * kRawKeyBytes + ((rc ^ (key & 15)) << 4)));
+      const u32x4 w = lds_read_b128(src + (uint32_t)(i * 16 * kRawKeyBytes));
       u32x4 lo4, hi4;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -209,24 +215,33 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
         else hi4 = u32x4{a0, a1, b0, b1};
       }
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          (__attribute__((address_space(3))) char*)(uintptr_t)(dst + key_col(key, 2 * rc))) = lo4;
+          (__attribute__((address_space(3))) char*)(uintptr_t)(dlo + (uint32_t)(i * 16 * kKeyBytes))) = lo4;
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          (__attribute__((address_space(3))) char*)(uintptr_t)(dst + key_col(key, 2 * rc + 1))) = hi4;
+          (__attribute__((address_space(3))) char*)(uintptr_t)(dhi + (uint32_t)(i * 16 * kKeyBytes))) = hi4;
+      sched_fence();  // one key at a time: bounds the registers the widening holds
     }
   };
 
-  // Operand bases. K: key lane%32 of a 32-key half, column 2ks + c, at
-  // kbase ^ (ks << 5). V^T: dims 16(lane/16 % 2) + lane%16 of a 32-dim tile
-  // for keys 4c + (lane%16)/4 (vlo) and the same + 8 (vhi), tile dt at ^ (dt << 6).
-  uint32_t kbase, vlo, vhi;
+  // Per-lane operand offsets inside a block stage. K: key lane%32 of the
+  // first 32-key half, column 2ks + c (second half 16 KB further). V^T: dims
+  // 16(lane/16 % 2) + lane%16 of 32-dim tile dt for keys 4c + (lane%16)/4
+  // ([dt][0]) and the same + 8 ([dt][1]); 16-key step u is 8 KB further.
+  uint32_t kofs[8], vofs[4][2];
   {
     const int kk = lane & 31;
-    kbase = (uint32_t)(kk * kKeyBytes + ((c ^ kswz(kk)) << 4));
+    const uint32_t kb_ = (uint32_t)(kk * kKeyBytes + ((c ^ kswz(kk)) << 4));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kofs[ks] = kb_ ^ (uint32_t)(ks << 5);
     const int jj = lane & 15;
     const int x = 16 + 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
     const int k_lo = 4 * c + (jj >> 2), k_hi = k_lo + 8;
-    vlo = (uint32_t)(k_lo * kKeyBytes + ((x ^ kswz(k_lo)) << 4) + 8 * (jj & 1));
-    vhi = (uint32_t)(k_hi * kKeyBytes + ((x ^ kswz(k_hi)) << 4) + 8 * (jj & 1));
+    const uint32_t vlo = (uint32_t)(k_lo * kKeyBytes + ((x ^ kswz(k_lo)) << 4) + 8 * (jj & 1));
+    const uint32_t vhi = (uint32_t)(k_hi * kKeyBytes + ((x ^ kswz(k_hi)) << 4) + 8 * (jj & 1));
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      vofs[dt][0] = vlo ^ (uint32_t)(dt << 6);
+      vofs[dt][1] = vhi ^ (uint32_t)(dt << 6);
+    }
   }
 
   // Log2-domain logit relative to a reference mref: s * c1 - mref, or with the
@@ -235,49 +250,46 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
   const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
 
+  // MFMA phase j: O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs, if j >= 1), then
+  // S^T_j = K_j Q^T (16 MFMAs, if j < nblk). Operands are read kAhead MFMAs
+  // ahead of their use (an LDS read takes longer than one MFMA).
+  constexpr int kAhead = 8;
   auto mfma_phase = [&](int j) {
     if (j >= 1) {
       const uint32_t st = stage(j - 1);
-      auto vread = [&](int u, int dt) -> u32x4 {
-        const uint32_t b = st + (uint32_t)(u * 16 * kKeyBytes);
-        const u32x2 v0 = lds_read_tr16(b + xor_here(vlo, (uint32_t)(dt << 6)));
-        const u32x2 v1 = lds_read_tr16(b + xor_here(vhi, (uint32_t)(dt << 6)));
+      auto vread = [&](int n) -> u32x4 {
+        const uint32_t b = st + (uint32_t)((n >> 2) * 16 * kKeyBytes);
+        const u32x2 v0 = lds_read_tr16(b + vofs[n & 3][0]);
+        const u32x2 v1 = lds_read_tr16(b + vofs[n & 3][1]);
         return u32x4{v0[0], v0[1], v1[0], v1[1]};
       };
-      u32x4 vf = vread(0, 0);
+      u32x4 ring[kAhead];
+#pragma unroll
+      for (int n = 0; n < kAhead; ++n) ring[n] = vread(n);
 #pragma unroll
       for (int n = 0; n < 16; ++n) {
-        const int u = n >> 2, dt = n & 3;
-        u32x4 vn = {0u, 0u, 0u, 0u};
-        if (n + 1 < 16) vn = vread((n + 1) >> 2, (n + 1) & 3);
-        pin_after(vf);
-        acc[dt] = mfma_32x32x16(as_bf16x8(vf), as_bf16x8(pb[u]), acc[dt]);
-        vf = vn;
+        u32x4 x = ring[n % kAhead];
+        pin_after(x);
+        acc[n & 3] = mfma_32x32x16(as_bf16x8(x), as_bf16x8(pb[n >> 2]), acc[n & 3]);
+        if (n + kAhead < 16) ring[n % kAhead] = vread(n + kAhead);
       }
     }
     if (j < nblk) {
       const uint32_t st = stage(j);
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sv[tt][i] = 0.f;
-      auto kread = [&](int ks, int tt) -> u32x4 {
-        return lds_read_b128(st + (uint32_t)(tt * 32 * kKeyBytes) + xor_here(kbase, (uint32_t)(ks << 5)));
+      // Operand m: k-step m/2 of 32-key half m%2.
+      auto kread = [&](int m) -> u32x4 {
+        return lds_read_b128(st + kofs[m >> 1] + (uint32_t)((m & 1) * 32 * kKeyBytes));
       };
-      u32x4 kf0 = kread(0, 0), kf1 = kread(0, 1);
+      u32x4 ring[kAhead];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        u32x4 kn0 = {0u, 0u, 0u, 0u}, kn1 = {0u, 0u, 0u, 0u};
-        if (ks + 1 < 8) {
-          kn0 = kread(ks + 1, 0);
-          kn1 = kread(ks + 1, 1);
-        }
-        pin_after(kf0);
-        pin_after(kf1);
-        sv[0] = mfma_32x32x16(as_bf16x8(kf0), as_bf16x8(qv[ks]), sv[0]);
-        sv[1] = mfma_32x32x16(as_bf16x8(kf1), as_bf16x8(qv[ks]), sv[1]);
-        kf0 = kn0;
-        kf1 = kn1;
+      for (int m = 0; m < kAhead; ++m) ring[m] = kread(m);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        u32x4 x = ring[m % kAhead];
+        pin_after(x);
+        const floatx16 zero = {};  // k-step 0 starts from zero (an inline constant)
+        sv[m & 1] = mfma_32x32x16(as_bf16x8(x), as_bf16x8(qv[m >> 1]), m < 2 ? zero : sv[m & 1]);
+        if (m + kAhead < 16) ring[m % kAhead] = kread(m + kAhead);
       }
     }
   };
@@ -357,7 +369,8 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   // and 2j + 3. Every wave waits for its own DMA before the barrier that
   // precedes the block's first use.
   drain_vmem_before_loop();
-  for (int j = 0; j < 2 && j < nblk; ++j) issue(j);
+  for (int j = 0; j < 2 && j < nblk; ++j) issue(j, page_of(j));
+  int page_next = 2 < nblk ? page_of(2) : 0;  // page of the next block to issue
   if (nblk > 1)
     wait_vmcnt<kIPW>();
   else
@@ -389,7 +402,12 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   auto run = [&](auto group_b) {
     constexpr bool kB = decltype(group_b)::value;
     for (int j = 0; j <= nblk; ++j) {
-      if (j + 2 < nblk) issue(j + 2);
+      if (j + 2 < nblk) issue(j + 2, page_next);
+      if constexpr (kB) {
+        // The next page id is loaded where this wave's VALU phase begins: an
+        // outstanding scalar load makes every LDS wait drain to zero.
+        if (j + 3 < nblk) page_next = page_of(j + 3);
+      }
       if (wave_active) {
         if constexpr (kB) {
           if (j >= 1) valu_phase(j - 1);
@@ -400,6 +418,12 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
       close_phase(2 * j);
       if constexpr (F8 && !kB) {
         if (j + 1 < nblk) widen(j + 1);
+      }
+      if constexpr (!kB) {
+        // The next page id is loaded where the VALU phase begins (after the
+        // widening's LDS traffic): an outstanding scalar load makes every LDS
+        // wait drain to zero.
+        if (j + 3 < nblk) page_next = page_of(j + 3);
       }
       if (wave_active) {
         if constexpr (kB) {
@@ -438,16 +462,33 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
     }
 }
 
+// Workgroup b runs on XCD b % kXcds (the dispatcher places workgroups round
+// robin over the XCDs). The prefill tiles, listed by (sequence, kv head,
+// query block), are cut into kXcds contiguous ranges, one per XCD, so the
+// query blocks that stream the same keys share one L2; a workgroup whose
+// range is used up takes tiles from the other ranges.
+
 template <int KV_DT, bool CAP>
 __global__ void __launch_bounds__(kThreads, 1) gqa_prefill_kernel(GqaArgs a, int ps_log2) {
   __shared__ __attribute__((aligned(16))) PreSmem<KV_DT> sm;
-  const int count = a.counters[3];
+  const int npre = a.counters[3];
+  const int home = blockIdx.x % kXcds;
   for (;;) {
-    if (threadIdx.x == 0) sm.tile = atomicAdd(&a.counters[2], 1);
+    if (threadIdx.x == 0) {
+      int t = -1;
+      for (int k = 0; k < kXcds && t < 0; ++k) {
+        const int x = (home + k) % kXcds;
+        const int b = (int)((int64_t)npre * x / kXcds), e = (int)((int64_t)npre * (x + 1) / kXcds);
+        if (b >= e) continue;
+        const int i = atomicAdd(&a.counters[kXcdCursor0 + x], 1);
+        if (b + i < e) t = b + i;
+      }
+      sm.tile = t;
+    }
     __syncthreads();
     const int ti = sm.tile;
     __syncthreads();
-    if (ti >= count) break;
+    if (ti < 0) break;
     prefill_tile<KV_DT, CAP>(a, a.tiles[ti], sm, ps_log2);
     __syncthreads();
   }

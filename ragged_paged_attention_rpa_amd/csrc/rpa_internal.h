@@ -74,11 +74,15 @@ struct GqaArgs {
   // workspace
   Tile* tiles;
   int32_t* counters;  // [0] tile count, [1] decode-kernel cursor (starts past the prefill
-                      // tiles when pre_kernel), [2] prefill-kernel cursor, [3] prefill tiles
+                      // tiles when pre_kernel), [3] prefill tiles, [16 .. 23] prefill
+                      // cursors (one per XCD)
   float* part_acc;    // [max_num_seqs*Hkv*max_splits][16][D]
   float* part_ml;     // [max_num_seqs*Hkv*max_splits][16][2]
   int tile_capacity;
 };
+
+constexpr int kXcdCursor0 = 16;  // first per-XCD prefill cursor in GqaArgs::counters
+constexpr int kXcds = 8;         // XCDs of an MI355X (one prefill cursor each)
 
 GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window);
 size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads,
