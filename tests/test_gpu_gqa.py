@@ -70,6 +70,13 @@ RAGGED = [
     # chunks grow past the target split size
     ([(1, 20000), (2, 17000), (4, 1500), (1, 16385)], 32, 8, 16, None, None, "long-decode"),
     ([(1, 18000), (3, 9000)], 16, 4, 16, 5000, 30.0, "long-window"),
+    # prefill kernel at its smallest page size (8: one page per wave's keys)
+    ([(70, 300), (1, 33), (300, 1100)], 32, 8, 8, None, None, "page8"),
+    # page size 4: prefill-class tiles fall back to the four-wave kernel
+    ([(40, 300), (1, 77), (70, 200)], 16, 4, 4, 90, None, "page4-fallback"),
+    # large groups: 16 and 32 rows per query token (16 and 8 tokens per tile)
+    ([(33, 1000), (1, 500), (100, 100)], 32, 2, 16, None, 50.0, "g16"),
+    ([(20, 700), (57, 640), (1, 64)], 32, 1, 32, 200, None, "g32-window"),
 ]
 
 
@@ -83,11 +90,12 @@ def test_ragged_bf16(idx):
     _check(c, _run_gpu(c), _run_oracle(c), "bf16")
 
 
-@pytest.mark.parametrize("cap,qscale", [(None, 1.0), (50.0, 1.0), (50.0, 16.0)])
-def test_ragged_fp8_scales(cap, qscale):
-    _say(f"ragged fp8 cap={cap} qscale={qscale}")
+@pytest.mark.parametrize("cap,qscale,ps", [(None, 1.0, 16), (50.0, 1.0, 16), (50.0, 16.0, 16),
+                                            (None, 1.0, 8)])
+def test_ragged_fp8_scales(cap, qscale, ps):
+    _say(f"ragged fp8 cap={cap} qscale={qscale} page={ps}")
     seqs = [(1, 700), (1, 33), (150, 900), (2, 2), (64, 64)]
-    c = wl.make_gqa(seqs, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+    c = wl.make_gqa(seqs, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=ps,
                     q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn, seed=31, device="cuda",
                     kv_value_scale=2.0, q_value_scale=qscale, sliding_window=300, soft_cap=cap,
                     k_scale=0.5, v_scale=0.5, name="fp8")
