@@ -131,10 +131,11 @@ __device__ __forceinline__ uint32_t v_lat() {
 
 // S^T[key, head] for NT 16-key tiles and NH 16-head tiles; lat/rope are the
 // lane operand addresses of the first tile (stage included). Each K read
-// feeds NH MFMAs; the NT tiles give independent accumulation chains.
-// after_step(j) runs after the MFMAs of k-step j (the callers issue the next
-// block's DMA from it, spread over the k-steps).
-template <int NT, int NH, typename F>
+// feeds NH MFMAs; the NT tiles give independent accumulation chains. The K
+// reads run AH k-steps ahead of their MFMAs (an LDS round trip takes several
+// MFMAs). after_step(j) runs after the MFMAs of k-step j (the callers issue
+// the next block's DMA from it, spread over the k-steps).
+template <int NT, int NH, int AH, typename F>
 __device__ __forceinline__ void score_tiles(floatx4 (&sv)[NT][NH], uint32_t lat, uint32_t rope,
                                             const u32x4 (&qv)[NH][kQSteps], F&& after_step) {
 #pragma unroll
@@ -145,25 +146,29 @@ __device__ __forceinline__ void score_tiles(floatx4 (&sv)[NT][NH], uint32_t lat,
     return j < 16 ? lds_read_b128((lat ^ (uint32_t)(j << 4)) + t * kTileKvc)
                   : lds_read_b128((rope ^ (uint32_t)((j - 16) << 4)) + t * kTileKpe);
   };
-  // The K reads of k-step j + 1 are issued before the MFMAs of k-step j.
-  u32x4 kf[NT];
+  u32x4 ring[AH][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) kf[t] = kread(0, t);
+  for (int j = 0; j < AH; ++j)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ring[j][t] = kread(j, t);
 #pragma unroll
   for (int j = 0; j < kQSteps; ++j) {
-    u32x4 kn[NT];
+    u32x4 kf[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) kn[t] = j + 1 < kQSteps ? kread(j + 1, t) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int t = 0; t < NT; ++t) pin_after(kf[t]);  // the prefetch stays ahead of this step's MFMAs
+    for (int t = 0; t < NT; ++t) {
+      kf[t] = ring[j % AH][t];
+      pin_after(kf[t]);  // later reads stay behind this step's operands
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int h = 0; h < NH; ++h)
         sv[t][h] = mfma_16x16x32(as_bf16x8(kf[t]), as_bf16x8(qv[h][j]), sv[t][h]);
-    after_step(j);
+    if (j + AH < kQSteps) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) kf[t] = kn[t];
+      for (int t = 0; t < NT; ++t) ring[j % AH][t] = kread(j + AH, t);
+    }
+    after_step(j);
   }
 }
 
@@ -200,6 +205,7 @@ constexpr int kMlaHeads = kMlaWaves * 16 * kMlaHT;    // heads per workgroup (12
 constexpr int kPageWin = 1024;                        // page ids cached in LDS
 constexpr int kMlaMaxSplits = 16;
 constexpr int kMlaMinChunk = 256;
+constexpr int kMlaAhead = 2;                          // K k-steps read ahead of their MFMAs
 
 struct MlaSeq {
   int cu0, q_len, kv_len, kv_cap;
@@ -475,7 +481,7 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
       floatx4 sv[2][kMlaHT];
       // The first half's k-steps carry this wave's DMA of block b + 1.
       const bool dma_here = more && half == 0;
-      score_tiles<2, kMlaHT>(sv, hc + klat, cur + (uint32_t)(2 * half * kTileKpe) + krope, qv,
+      score_tiles<2, kMlaHT, kMlaAhead>(sv, hc + klat, cur + (uint32_t)(2 * half * kTileKpe) + krope, qv,
                              [&](int j) {
                                if (j < kDmaPer8 && dma_here) issue_key_dma(src, nxt, wave, nrow, j);
                              });
@@ -661,6 +667,8 @@ constexpr int kSpThreads = kSpWaves * 64;
 constexpr int kSpGroups = kBlk / 8 / kSpWaves;         // 8-key DMA groups per wave (2)
 constexpr int kSpIPW = kSpGroups * kDmaPer8;           // DMA instructions per wave per block
 constexpr int kSpMaxUnits = 256;
+constexpr int kSpAhead = 6;                            // K k-steps read ahead of their MFMAs
+constexpr int kSpVAhead = 8;                           // V^T tiles read ahead of their MFMAs
 
 struct SparseShared {
   char stage[2][kStageBytes];
@@ -770,7 +778,7 @@ sparse_mla_kernel(SparseArgs a) {
     if (more) prep_rows(b + 1, nrows, vm_next);
     floatx4 sv2[1][1];
     // One DMA instruction of block b + 1 after each of the 18 k-steps.
-    score_tiles<1, 1>(sv2, (cur + klat), (cur + krope), qv, [&](int j) {
+    score_tiles<1, 1, kSpAhead>(sv2, (cur + klat), (cur + krope), qv, [&](int j) {
       if (more)
         issue_key_dma(src, nxt, kSpGroups * wave + j / kDmaPer8, nrows[j / kDmaPer8], j % kDmaPer8);
     });
@@ -810,14 +818,19 @@ sparse_mla_kernel(SparseArgs a) {
       pb[0] = pack_bf16x2(p[0], p[1]);
       pb[1] = pack_bf16x2(p[2], p[3]);
     }
+    {
+      // V^T tiles read kSpVAhead tiles ahead of their MFMAs.
+      u32x2 vr[kSpVAhead];
 #pragma unroll
-    for (int dt0 = 0; dt0 < kDvTiles; dt0 += 4) {
-      u32x2 vt[4];
+      for (int d = 0; d < kSpVAhead; ++d) vr[d] = lds_read_tr16((cur + vlat) ^ (uint32_t)(d << 5));
 #pragma unroll
-      for (int d = 0; d < 4; ++d) vt[d] = lds_read_tr16((cur + vlat) ^ (uint32_t)((dt0 + d) << 5));
-#pragma unroll
-      for (int d = 0; d < 4; ++d) acc[dt0 + d] = mfma_16x16x16(vt[d], pb, acc[dt0 + d]);
-      sched_fence();
+      for (int dt = 0; dt < kDvTiles; ++dt) {
+        u32x2 x = vr[dt % kSpVAhead];
+        pin_after(x);
+        acc[dt] = mfma_16x16x16(x, pb, acc[dt]);
+        if (dt + kSpVAhead < kDvTiles)
+          vr[dt % kSpVAhead] = lds_read_tr16(xor_here(cur + vlat, (uint32_t)((dt + kSpVAhead) << 5)));
+      }
     }
   }
   // The four waves hold the softmax state of disjoint key tiles: merge in LDS.
