@@ -173,21 +173,43 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
     const int k8 = kb0 + j * kBN + 8 * wave;
     return load_uniform(table + min(k8 >> ps_log2, a.pages_per_seq - 1));
   };
+  // This wave's share of block j: kIPW DMA instructions of 1 KB. The wave's
+  // eight keys start at k8 = kb0 + 64 j + 8 wave, so their low four bits (and
+  // with them the swizzled columns) are the same in every block: each lane's
+  // byte offset from the chunk's first row is fixed (dofs), and its low bits
+  // are the column's offset (a row is a multiple of 512 bytes for bf16, of
+  // 256 for fp8). A chunk wholly inside [lo, hi) on a valid page (all but the
+  // range's ends) is addressed as one SGPR base plus these fixed offsets;
+  // otherwise each lane checks its key and reads zeros for keys outside the
+  // range or on an invalid page.
+  uint32_t dofs[kIPW];
+#pragma unroll
+  for (int ii = 0; ii < kIPW; ++ii) {
+    const int sub = F8 ? lane >> 4 : lane >> 5;
+    const int e = (F8 ? 4 : 2) * ii + sub;
+    const int klow = 8 * (wave & 1) + e;  // key & 15
+    const int col = F8 ? ((lane & 15) ^ klow) : ((lane & 31) ^ kswz(klow));
+    dofs[ii] = (uint32_t)(e * token_bytes + (col << 4));
+  }
   auto issue = [&](int j, int page) {
     const int k8 = kb0 + j * kBN + 8 * wave;
     const bool page_ok = page >= 0 && page < a.total_num_pages;
     const char* rowbase = kv_head + (((int64_t)page << ps_log2) + (k8 & ps_mask)) * token_bytes;
-    const uint32_t dst = F8 ? raw_stage(j) : stage(j);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane((F8 ? raw_stage(j) : stage(j)) +
+                                                       (uint32_t)(wave * kIPW) * 1024);
+    if (page_ok && k8 >= lo && k8 + 8 <= hi) {
 #pragma unroll
-    for (int ii = 0; ii < kIPW; ++ii) {
+      for (int ii = 0; ii < kIPW; ++ii) dma_b128_s(rowbase, dofs[ii], dst + (uint32_t)ii * 1024);
+    } else {
       const int sub = F8 ? lane >> 4 : lane >> 5;
-      const int e = (F8 ? 4 : 2) * ii + sub;  // key within the wave's eight
-      const int key = k8 + e;
-      const int col = F8 ? ((lane & 15) ^ (key & 15)) : ((lane & 31) ^ kswz(key));
-      const bool ok = page_ok && key >= lo && key < hi;
-      const char* src = ok ? rowbase + e * token_bytes + (col << 4)
-                           : (const char*)kPreZero + (col << 4);
-      dma_b128(src, __builtin_amdgcn_readfirstlane(dst + (uint32_t)(wave * kIPW + ii) * 1024));
+#pragma unroll
+      for (int ii = 0; ii < kIPW; ++ii) {
+        const int key = k8 + (F8 ? 4 : 2) * ii + sub;
+        const bool ok = page_ok && key >= lo && key < hi;
+        const char* src = ok ? rowbase + dofs[ii]
+                             : (const char*)kPreZero + (dofs[ii] & (F8 ? 0xF0u : 0x1F0u));
+        dma_b128(src, dst + (uint32_t)ii * 1024);
+      }
     }
   };
 
@@ -223,99 +245,94 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   };
 
   // Per-lane operand offsets inside a block stage. K: key lane%32 of the
-  // first 32-key half, column 2ks + c (second half 16 KB further). V^T: dims
-  // 16(lane/16 % 2) + lane%16 of 32-dim tile dt for keys 4c + (lane%16)/4
-  // ([dt][0]) and the same + 8 ([dt][1]); 16-key step u is 8 KB further.
-  uint32_t kofs[8], vofs[4][2];
+  // first 32-key half, column 2ks + c, at kbase ^ (ks << 5) (second half 16 KB
+  // further). V^T: dims 16(lane/16 % 2) + lane%16 of 32-dim tile dt for keys
+  // 4c + (lane%16)/4 at vbase[0] ^ (dt << 6) and the same + 8 at
+  // vbase[1] ^ (dt << 6); 16-key step u is 8 KB further. The XORs are taken
+  // at each read (xor_here): the MFMA wave has VALU slots to spare, and
+  // sixteen precomputed offsets would be sixteen registers.
+  uint32_t kbase, vbase[2];
   {
     const int kk = lane & 31;
-    const uint32_t kb_ = (uint32_t)(kk * kKeyBytes + ((c ^ kswz(kk)) << 4));
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kofs[ks] = kb_ ^ (uint32_t)(ks << 5);
+    kbase = (uint32_t)(kk * kKeyBytes + ((c ^ kswz(kk)) << 4));
     const int jj = lane & 15;
     const int x = 16 + 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1);
     const int k_lo = 4 * c + (jj >> 2), k_hi = k_lo + 8;
-    const uint32_t vlo = (uint32_t)(k_lo * kKeyBytes + ((x ^ kswz(k_lo)) << 4) + 8 * (jj & 1));
-    const uint32_t vhi = (uint32_t)(k_hi * kKeyBytes + ((x ^ kswz(k_hi)) << 4) + 8 * (jj & 1));
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      vofs[dt][0] = vlo ^ (uint32_t)(dt << 6);
-      vofs[dt][1] = vhi ^ (uint32_t)(dt << 6);
-    }
+    vbase[0] = (uint32_t)(k_lo * kKeyBytes + ((x ^ kswz(k_lo)) << 4) + 8 * (jj & 1));
+    vbase[1] = (uint32_t)(k_hi * kKeyBytes + ((x ^ kswz(k_hi)) << 4) + 8 * (jj & 1));
   }
 
-  // Log2-domain logit relative to a reference mref: s * c1 - mref, or with the
-  // soft cap, cap * tanh(s * scale / cap) * log2(e) - mref with tanh(z) taken
-  // as 1 - 2 / (e^{2z} + 1) (hardware exp2 and reciprocal).
-  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
-  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
+  // Log2-domain logit of a raw score s: s * c1, or with the soft cap
+  // cap * tanh(s * scale / cap) * log2(e), tanh(z) taken as 1 - 2 / (e^{2z} + 1)
+  // (hardware exp2 and reciprocal): c2 - c3 / (2^{s c1} + 1).
+  // cap * tanh(x / cap) is even in cap: |cap| is used, so c1 > 0 whenever the
+  // score scale is (the launcher's precondition).
+  const float cap = fabsf(a.soft_cap);
+  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / cap : a.score_scale * kLog2e;
+  const float c2 = cap * kLog2e, c3 = 2.f * cap * kLog2e;
 
-  // MFMA phase j: O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs, if j >= 1), then
-  // S^T_j = K_j Q^T (16 MFMAs, if j < nblk). Operands are read kAhead MFMAs
-  // ahead of their use (an LDS read takes longer than one MFMA).
-  constexpr int kAhead = 8;
-  auto mfma_phase = [&](int j) {
-    if (j >= 1) {
-      const uint32_t st = stage(j - 1);
-      auto vread = [&](int n) -> u32x4 {
-        const uint32_t b = st + (uint32_t)((n >> 2) * 16 * kKeyBytes);
-        const u32x2 v0 = lds_read_tr16(b + vofs[n & 3][0]);
-        const u32x2 v1 = lds_read_tr16(b + vofs[n & 3][1]);
-        return u32x4{v0[0], v0[1], v1[0], v1[1]};
-      };
-      u32x4 ring[kAhead];
-#pragma unroll
-      for (int n = 0; n < kAhead; ++n) ring[n] = vread(n);
-#pragma unroll
-      for (int n = 0; n < 16; ++n) {
-        u32x4 x = ring[n % kAhead];
-        pin_after(x);
-        acc[n & 3] = mfma_32x32x16(as_bf16x8(x), as_bf16x8(pb[n >> 2]), acc[n & 3]);
-        if (n + kAhead < 16) ring[n % kAhead] = vread(n + kAhead);
-      }
+  // MFMA phase j: O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs), then S^T_j = K_j Q^T
+  // (16 MFMAs). The 32 A operands (V^T from block j - 1, then K from block j)
+  // stream through one ring of kAhead registers: operand t + kAhead is read
+  // while MFMA t runs (an LDS read takes several MFMAs to return), and the
+  // ring's first kAhead reads can be issued at the end of the wave's previous
+  // phase (ring_start), so the phase opens with its operands in flight. One
+  // copy of this code serves every phase: at j == 0 block -1 is a zeroed
+  // stage (and P is zero), at j == nblk the QK half runs on a stale stage and
+  // its scores are never used.
+  constexpr int kStages = F8 ? kConvStages : kBf16Stages;
+  auto pv_stage = [&](int j) -> uint32_t {
+    return sbase + (uint32_t)((j + kStages - 1) % kStages) * kStage;
+  };
+  auto operand = [&](int j, int t) -> u32x4 {
+    if (t < 16) {
+      const uint32_t b = pv_stage(j) + (uint32_t)((t >> 2) * 16 * kKeyBytes);
+      const u32x2 v0 = lds_read_tr16(b + xor_here(vbase[0], (uint32_t)((t & 3) << 6)));
+      const u32x2 v1 = lds_read_tr16(b + xor_here(vbase[1], (uint32_t)((t & 3) << 6)));
+      return u32x4{v0[0], v0[1], v1[0], v1[1]};
     }
-    if (j < nblk) {
-      const uint32_t st = stage(j);
-      // Operand m: k-step m/2 of 32-key half m%2.
-      auto kread = [&](int m) -> u32x4 {
-        return lds_read_b128(st + kofs[m >> 1] + (uint32_t)((m & 1) * 32 * kKeyBytes));
-      };
-      u32x4 ring[kAhead];
+    const int m = t - 16;  // k-step m/2 of 32-key half m%2
+    return lds_read_b128(stage(j) + xor_here(kbase, (uint32_t)((m >> 1) << 5)) +
+                         (uint32_t)((m & 1) * 32 * kKeyBytes));
+  };
+  constexpr int kAhead = 8;
+  u32x4 ring[kAhead];
+  auto ring_start = [&](int j) {
+    sched_fence();  // the reads stay after the wave's preceding work
 #pragma unroll
-      for (int m = 0; m < kAhead; ++m) ring[m] = kread(m);
+    for (int t = 0; t < kAhead; ++t) ring[t] = operand(j, t);
+  };
+  auto mfma_phase = [&](int j) {
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        u32x4 x = ring[m % kAhead];
-        pin_after(x);
+    for (int t = 0; t < 32; ++t) {
+      u32x4 x = ring[t % kAhead];
+      pin_after(x);
+      if (t < 16) {
+        acc[t & 3] = mfma_32x32x16(as_bf16x8(x), as_bf16x8(pb[t >> 2]), acc[t & 3]);
+      } else {
+        const int m = t - 16;
         const floatx16 zero = {};  // k-step 0 starts from zero (an inline constant)
         sv[m & 1] = mfma_32x32x16(as_bf16x8(x), as_bf16x8(qv[m >> 1]), m < 2 ? zero : sv[m & 1]);
-        if (m + kAhead < 16) ring[m % kAhead] = kread(m + kAhead);
       }
+      if (t + kAhead < 32) ring[t % kAhead] = operand(j, t + kAhead);
     }
   };
 
+  // VALU phase j: the online softmax of S_j. A row keeps a reference m_run
+  // and its weights are p = 2^{logit - m_run} (log2-domain logits), in bf16
+  // for the PV step. The reference only has to keep the weights in range, so
+  // a block is first weighted against the current reference and its row sums
+  // are checked (kSumBound). Only a fresh row (no reference yet) or a sum
+  // above the bound takes the row maximum (on raw scores: both logit maps
+  // are increasing) and moves the reference if the maximum passes it by
+  // kLazyTau, rescaling O and l, before weighting the block again.
   auto valu_phase = [&](int j) {
     const int kb = kb0 + j * kBN;
     // Keys [kb, kb + 64) visible to every row of the wave: no mask needed.
     const bool full =
         __builtin_amdgcn_ballot_w64(row_ok && !(kb >= vlo_r && kb + kBN <= vhi_r)) == 0;
-    const bool fresh = m_run == -INFINITY;
-    const float mref = fresh ? 0.f : m_run;
-    const float c2r = c2 - mref;
-    auto rel = [&](float s) -> float {
-      if (!CAP) return fmaf(s, c1, -mref);
-      return fmaf(__builtin_amdgcn_rcpf(fast_exp2(s * c1) + 1.f), -c3, c2r);
-    };
-    float mx = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sv[tt][i] = rel(sv[tt][i]);
-          mx = fmaxf(mx, sv[tt][i]);
-        }
-    } else {
+    // Keys outside the row's range become -inf.
+    auto mask = [&]() {
       const uint32_t span = (uint32_t)(vhi_r - vlo_r);
       const int kbase_r = kb + 4 * c - vlo_r;
 #pragma unroll
@@ -323,54 +340,112 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const bool vis = (uint32_t)(kbase_r + 32 * tt + 8 * (i >> 2) + (i & 3)) < span;
-          sv[tt][i] = vis ? rel(sv[tt][i]) : -INFINITY;
-          mx = fmaxf(mx, sv[tt][i]);
+          sv[tt][i] = vis ? sv[tt][i] : -INFINITY;
         }
-    }
-    mx = wave_max_xor<32>(mx);
-    // Lazy reference: a row moves its reference (and rescales) only on its
-    // first visible block or when the block max passes it by kLazyTau.
-    const bool need = fresh ? mx != -INFINITY : mx > kLazyTau;
-    if (wave_any(need)) {
-      const float d = need ? mx : 0.f;
-      const float alpha = (need && !fresh) ? fast_exp2(-d) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-      m_run = need ? (fresh ? mx : m_run + d) : m_run;
+    };
+    if (!CAP && !full) mask();
+    // Logits are taken relative to mref (the reference, 0 for a fresh row).
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
+    if (CAP) {
+      // Capped logits minus mref, one pass per step over the 32 scores in
+      // place (independent neighbours hide each step's latency).
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[tt][i] -= d;
+        for (int i = 0; i < 16; ++i) sv[tt][i] = fast_exp2(sv[tt][i] * c1) + 1.f;
+      const float c2r = c2 - mref;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sv[tt][i] = fmaf(__builtin_amdgcn_rcpf(sv[tt][i]), -c3, c2r);
+      if (!full) mask();
     }
+    // Weights p = 2^{logit - mref - shift} into pb (bf16); returns this
+    // lane's half-row sum of the fp32 weights, in four add chains.
+    // (v_dot2_f32_bf16 would sum the rounded pairs in one instruction, but on
+    // gfx950 it waits for the SIMD's matrix pipe, which the partner wave
+    // keeps busy.)
+    auto weights = [&](float shift) -> float {
+      const float nref = -(mref + shift);
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[tt][i] = fast_exp2(sv[tt][i]);
-    // P in bf16 for the PV step; the row sum is taken from the same rounded
-    // weights with v_dot2_f32_bf16 against (1, 1).
-    const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+        for (int i = 0; i < 4; ++i) {
+          float w2[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float x = sv[u >> 1][8 * (u & 1) + 2 * i + h];
+            w2[h] = fast_exp2(CAP ? x - shift : fmaf(x, c1, nref));
+          }
+          pb[u][i] = pack_bf16x2(w2[0], w2[1]);
+          ls[i & 3] += w2[0] + w2[1];
+        }
+      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // A row sum of at most 64 * 2^kLazyTau bounds every weight by 2^(kLazyTau
+    // + 6) (a safe range for bf16 P and the fp32 sums), and a sum above it
+    // means a weight above 2^kLazyTau, so the maximum then always moves the
+    // reference. (A bound of 2^kLazyTau would also trip on blocks whose
+    // weights are all in range, e.g. after a reference taken from a few keys,
+    // and redo them every time.)
+    constexpr float kSumBound = 64.f * 256.f;  // 64 * 2^kLazyTau
     float ls = 0.f;
+    bool slow = wave_any(row_ok && m_run == -INFINITY);
+    if (!slow) {
+      ls = weights(0.f);
+      float ap, bp;
+      pair_xor<32>(ls, ap, bp);
+      slow = wave_any(row_ok && ap + bp > kSumBound);
+    }
+    if (slow) {
+      // Row maximum: four independent max chains (v_max3), then the row's
+      // other lane; mb is the block maximum relative to mref.
+      float mq[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int q = 0; q < 4; ++q) {
+        mq[q] = fmaxf(sv[q >> 1][8 * (q & 1)], sv[q >> 1][8 * (q & 1) + 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = pack_bf16x2(sv[u >> 1][8 * (u & 1) + 2 * i], sv[u >> 1][8 * (u & 1) + 2 * i + 1]);
-        pb[u][i] = w;
-        ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, ls, false);
+        for (int i = 2; i < 8; ++i) mq[q] = fmaxf(mq[q], sv[q >> 1][8 * (q & 1) + i]);
       }
+      const float mx = wave_max_xor<32>(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+      const float mb = CAP ? mx : (mx == -INFINITY ? -INFINITY : fmaf(mx, c1, -mref));
+      const bool fresh = m_run == -INFINITY;
+      const bool need = fresh ? mb != -INFINITY : mb > kLazyTau;
+      const float d = need ? mb : 0.f;
+      if (wave_any(need)) {
+        const float alpha = (need && !fresh) ? fast_exp2(-d) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        m_run = need ? mref + d : m_run;
+      }
+      ls = weights(d);
+    }
     l_run += ls;
   };
 
-  // Block j is issued at phase 2j - 4 (bf16) or its raw copy at 2j - 4 and
-  // widened at 2j - 1 (fp8); A reads it in phases 2j and 2j + 2, B in 2j + 1
-  // and 2j + 3. Every wave waits for its own DMA before the barrier that
-  // precedes the block's first use.
+  // Block j (its raw copy for fp8) is issued in phases 2j - 4 and 2j - 3
+  // (one group each); fp8 blocks are widened by A in phase 2j - 1. A reads K_j
+  // in phase 2j and V_j from the end of phase 2j + 1 through 2j + 2, B reads
+  // K_j in phase 2j + 1 and V_j from the end of 2j + 2 through 2j + 3, so the
+  // stage is free again when block j + 4 is issued in phase 2j + 4. Every
+  // wave waits for its own DMA before the barrier that precedes the block's
+  // first use.
   drain_vmem_before_loop();
   for (int j = 0; j < 2 && j < nblk; ++j) issue(j, page_of(j));
   int page_next = 2 < nblk ? page_of(2) : 0;  // page of the next block to issue
+  {
+    // Block -1 (the PV operand of MFMA phase 0): zeros.
+    const uint32_t z = pv_stage(0) + (uint32_t)tid * 16;
+#pragma unroll
+    for (int i = 0; i < kStage / (16 * kThreads); ++i)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          (__attribute__((address_space(3))) char*)(uintptr_t)(z + (uint32_t)(i * 16 * kThreads))) =
+          u32x4{0u, 0u, 0u, 0u};
+  }
   if (nblk > 1)
     wait_vmcnt<kIPW>();
   else
@@ -384,10 +459,22 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   // Closes phase p: this wave's DMA that the next phase needs has landed
   // (bf16: block (p + 1) / 2 after odd p; fp8: raw block p / 2 + 1 after even
   // p, before group A widens it), then the workgroup barrier.
-  auto close_phase = [&](int p) {
+  // Which group issues its share of block j + 2 in the iteration's odd phase
+  // (the other issues in the even phase). The DMA instructions go where the
+  // wave has slack: in the VALU phases without the soft cap (B in phase 2j,
+  // A in phase 2j + 1), in the MFMA phases with it (A in phase 2j, B in
+  // phase 2j + 1), whose softmax is the longer half.
+#ifndef RPA_PRE_LATEB
+#define RPA_PRE_LATEB CAP
+#endif
+  constexpr bool kLateB = RPA_PRE_LATEB;
+  auto close_phase = [&](int p, auto group_b) {
+    constexpr bool kB = decltype(group_b)::value;
     const int jw = F8 ? ((p & 1) == 0 ? p / 2 + 1 : -1) : ((p & 1) == 1 ? (p + 1) / 2 : -1);
     if (jw >= 0 && jw < nblk) {
-      if (jw + 1 < nblk)
+      // The group that issues in the odd phase (kLateB) has not issued the
+      // block after jw yet at an even close.
+      if (jw + 1 < nblk && (kB != kLateB || (p & 1) == 1))
         wait_vmcnt<kIPW>();
       else
         wait_vmcnt<0>();
@@ -397,12 +484,28 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   };
   // Iteration j (0 .. nblk) spans phases 2j and 2j + 1. Group A: MFMA phase
   // j, then VALU phase j. Group B: VALU phase j - 1, then MFMA phase j. Each
+  // wave issues its share of block j + 2 in the phase kLateB names. Each wave
+  // starts the ring of its next MFMA phase before the barrier that opens it
+  // (the V half reads block j - 1, which every wave already holds). Each
   // group runs its own copy of the loop, so across its back edge only P (A)
-  // or S (B) is live.
+  // or S (B) and the ring are live.
   auto run = [&](auto group_b) {
     constexpr bool kB = decltype(group_b)::value;
+    constexpr bool kLate = kB == kLateB;
+    // fp8: group A's VALU phase also widens the next block, and a ring held
+    // across it would spill; A starts its ring in the MFMA phase instead.
+#ifndef RPA_PRE_EARLY
+#define RPA_PRE_EARLY (!CAP && (kB || !F8))
+#endif
+    constexpr bool kEarly = RPA_PRE_EARLY;
+    if constexpr (!kB) {
+      if (wave_active && kEarly) ring_start(0);
+    }
     for (int j = 0; j <= nblk; ++j) {
-      if (j + 2 < nblk) issue(j + 2, page_next);
+      const int page_dma = page_next;  // page of block j + 2
+      if constexpr (!kLate) {
+        if (j + 2 < nblk) issue(j + 2, page_dma);
+      }
       if constexpr (kB) {
         // The next page id is loaded where this wave's VALU phase begins: an
         // outstanding scalar load makes every LDS wait drain to zero.
@@ -411,15 +514,20 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
       if (wave_active) {
         if constexpr (kB) {
           if (j >= 1) valu_phase(j - 1);
+          if constexpr (kEarly) ring_start(j);
         } else {
+          if constexpr (!kEarly) ring_start(j);
           mfma_phase(j);
         }
       }
-      close_phase(2 * j);
-      if constexpr (F8 && !kB) {
-        if (j + 1 < nblk) widen(j + 1);
+      close_phase(2 * j, group_b);
+      if constexpr (kLate) {
+        if (j + 2 < nblk) issue(j + 2, page_dma);
       }
       if constexpr (!kB) {
+        if constexpr (F8) {
+          if (grp == 0 && j + 1 < nblk) widen(j + 1);  // group A's 256 threads
+        }
         // The next page id is loaded where the VALU phase begins (after the
         // widening's LDS traffic): an outstanding scalar load makes every LDS
         // wait drain to zero.
@@ -427,15 +535,20 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
       }
       if (wave_active) {
         if constexpr (kB) {
+          if constexpr (!kEarly) ring_start(j);
           mfma_phase(j);
         } else {
           if (j < nblk) valu_phase(j);
+          if (kEarly && j < nblk) ring_start(j + 1);
         }
       }
-      close_phase(2 * j + 1);
+      close_phase(2 * j + 1, group_b);
     }
   };
-  if (grp == 0)
+#ifndef RPA_PRE_SYNC
+#define RPA_PRE_SYNC 0
+#endif
+  if (grp == 0 || RPA_PRE_SYNC)
     run(std::false_type{});
   else
     run(std::true_type{});

@@ -260,7 +260,10 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   if (meta->max_num_tokens == 0) return ok();
   if (mfma) {
     rpa::gqa_bind_workspace(a, workspace);
-    if (rpa::gqa_prefill_supported(a.q_dtype, a.kv_dtype, head_dim, a.geo.group, page_size)) {
+    // The prefill kernel takes row maxima on raw scores, which needs an
+    // increasing logit map: a positive score scale.
+    if (a.score_scale > 0.f &&
+        rpa::gqa_prefill_supported(a.q_dtype, a.kv_dtype, head_dim, a.geo.group, page_size)) {
       // Prefill-class tiles of 256 rows for the eight-wave kernel (fewer tiles
       // than the workspace was sized for).
       a.pre_kernel = 1;

@@ -92,7 +92,8 @@ void gqa_bind_workspace(GqaArgs& a, void* ws);
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream);
 hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream);
-// Prefill-class tiles on eight waves (gqa_prefill.hip).
+// Prefill-class tiles on eight waves (gqa_prefill.hip). Requires
+// a.score_scale > 0 (the kernel takes row maxima on raw scores).
 int gqa_prefill_rows();
 bool gqa_prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group, int page_size);
 hipError_t launch_gqa_prefill(const GqaArgs& a, int ps_log2, int grid, hipStream_t stream);
