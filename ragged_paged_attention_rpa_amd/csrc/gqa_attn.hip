@@ -204,11 +204,7 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
         // Query blocks in descending order: within a (sequence, kv head) the
         // blocks with the most keys are taken first, so the last tiles a
         // workgroup picks up are the short ones.
-#ifdef RPA_QB_ASC
-        tl.qtok0 = (local % nqb) * a.geo.bq;
-#else
         tl.qtok0 = (nqb - 1 - local % nqb) * a.geo.bq;
-#endif
         tl.split = -1;
       } else {
         const int u = t - run_pre;

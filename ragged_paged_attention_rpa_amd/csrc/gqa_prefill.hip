@@ -464,10 +464,7 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   // wave has slack: in the VALU phases without the soft cap (B in phase 2j,
   // A in phase 2j + 1), in the MFMA phases with it (A in phase 2j, B in
   // phase 2j + 1), whose softmax is the longer half.
-#ifndef RPA_PRE_LATEB
-#define RPA_PRE_LATEB CAP
-#endif
-  constexpr bool kLateB = RPA_PRE_LATEB;
+  constexpr bool kLateB = CAP;
   auto close_phase = [&](int p, auto group_b) {
     constexpr bool kB = decltype(group_b)::value;
     const int jw = F8 ? ((p & 1) == 0 ? p / 2 + 1 : -1) : ((p & 1) == 1 ? (p + 1) / 2 : -1);
@@ -492,12 +489,12 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   auto run = [&](auto group_b) {
     constexpr bool kB = decltype(group_b)::value;
     constexpr bool kLate = kB == kLateB;
-    // fp8: group A's VALU phase also widens the next block, and a ring held
-    // across it would spill; A starts its ring in the MFMA phase instead.
-#ifndef RPA_PRE_EARLY
-#define RPA_PRE_EARLY (!CAP && (kB || !F8))
-#endif
-    constexpr bool kEarly = RPA_PRE_EARLY;
+    // Whether the ring of the next MFMA phase is started at the end of the
+    // VALU phase (measured faster without the soft cap) or at the start of
+    // the MFMA phase (with it: its VALU phase is the longer one). fp8: group
+    // A's VALU phase also widens the next block, and a ring held across it
+    // would spill.
+    constexpr bool kEarly = !CAP && (kB || !F8);
     if constexpr (!kB) {
       if (wave_active && kEarly) ring_start(0);
     }
@@ -545,10 +542,7 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
       close_phase(2 * j + 1, group_b);
     }
   };
-#ifndef RPA_PRE_SYNC
-#define RPA_PRE_SYNC 0
-#endif
-  if (grp == 0 || RPA_PRE_SYNC)
+  if (grp == 0)
     run(std::false_type{});
   else
     run(std::true_type{});
