@@ -37,8 +37,10 @@
 // keys, four columns) free of bank conflicts. The DMA (global_load_lds,
 // 1 KB per instruction) applies the swizzle by choosing which global column
 // each lane fetches. fp8 pools land raw (256 bytes per key, column rc at
-// rc ^ (k & 15)) and group A widens them to bf16 exactly during its VALU
-// phase.
+// rc ^ (k & 15)) and group A widens each block once to bf16, exactly (every
+// E4M3FN value is a bf16 value), during its VALU phase; widening each
+// wave's operands in registers instead would convert every block eight
+// times over.
 #include <type_traits>
 
 #include "rpa_device.h"
@@ -77,6 +79,7 @@ __device__ __forceinline__ int kswz(int key) { return ((key & 3) << 2) | ((key >
 __device__ __forceinline__ uint32_t key_col(int key, int q) {
   return (uint32_t)(key * kKeyBytes + ((q ^ kswz(key)) << 4));
 }
+
 
 // Scalar (SGPR) read of a wave-uniform int32 from global memory.
 __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
@@ -157,9 +160,12 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   const char* kv_head = (const char*)a.kv + (int64_t)(2 * kvh) * kD * kEB;
   const uint32_t sbase = lds_addr(sm.buf);
 
-  // LDS byte address of the bf16 block j, and (fp8) of its raw copy.
+  // LDS byte address of the bf16 block j (j >= -1; block -1 is the zeroed
+  // stage the first MFMA phase multiplies by P = 0), and (fp8) of its raw
+  // copy.
+  constexpr int kStages = F8 ? kConvStages : kBf16Stages;
   auto stage = [&](int j) -> uint32_t {
-    return sbase + (uint32_t)(j % (F8 ? kConvStages : kBf16Stages)) * kStage;
+    return sbase + (uint32_t)((j + kStages) % kStages) * kStage;
   };
   auto raw_stage = [&](int j) -> uint32_t {
     return sbase + (uint32_t)(kConvStages * kStage) + (uint32_t)(j % kRawStages) * kRawStage;
@@ -214,8 +220,7 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   };
 
   // fp8: widen raw block j into bf16 stage j (group A's 256 threads; thread
-  // t takes raw column t/16 of keys t%16 + 16i). Exact: every E4M3FN value
-  // is a bf16 value.
+  // t takes raw column t/16 of keys t%16 + 16i).
   auto widen = [&](int j) {
     // Keys tid%16 + 16i share their low four bits, hence their swizzles: one
     // lane offset per side, the key step is a constant (4 KB raw, 8 KB bf16).
@@ -226,16 +231,8 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 w = lds_read_b128(src + (uint32_t)(i * 16 * kRawKeyBytes));
-      u32x4 lo4, hi4;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t a0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h], 1.0f, false));
-        const uint32_t a1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h], 1.0f, true));
-        const uint32_t b0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h + 1], 1.0f, false));
-        const uint32_t b1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[2 * h + 1], 1.0f, true));
-        if (h == 0) lo4 = u32x4{a0, a1, b0, b1};
-        else hi4 = u32x4{a0, a1, b0, b1};
-      }
+      const u32x4 lo4 = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
+      const u32x4 hi4 = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
           (__attribute__((address_space(3))) char*)(uintptr_t)(dlo + (uint32_t)(i * 16 * kKeyBytes))) = lo4;
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
@@ -280,29 +277,41 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   // copy of this code serves every phase: at j == 0 block -1 is a zeroed
   // stage (and P is zero), at j == nblk the QK half runs on a stale stage and
   // its scores are never used.
-  constexpr int kStages = F8 ? kConvStages : kBf16Stages;
-  auto pv_stage = [&](int j) -> uint32_t {
-    return sbase + (uint32_t)((j + kStages - 1) % kStages) * kStage;
+  auto pv_stage = [&](int j) -> uint32_t { return stage(j - 1); };
+  // Per-phase bases: the stage address plus a lane's offset, taken once per
+  // phase (ring_start); each read then only XORs in its column (stage
+  // addresses are multiples of 16 KB, so the XOR stays inside the offset) and
+  // adds a constant (folded into the read's offset field).
+  uint32_t pvb[2] = {0u, 0u}, kb = 0u;
+  auto phase_bases = [&](int j) {
+    pvb[0] = pv_stage(j) + vbase[0];
+    pvb[1] = pv_stage(j) + vbase[1];
+    kb = stage(j) + kbase;
   };
-  auto operand = [&](int j, int t) -> u32x4 {
+  auto operand = [&](int t) -> u32x4 {
     if (t < 16) {
-      const uint32_t b = pv_stage(j) + (uint32_t)((t >> 2) * 16 * kKeyBytes);
-      const u32x2 v0 = lds_read_tr16(b + xor_here(vbase[0], (uint32_t)((t & 3) << 6)));
-      const u32x2 v1 = lds_read_tr16(b + xor_here(vbase[1], (uint32_t)((t & 3) << 6)));
+      const uint32_t u = (uint32_t)((t >> 2) * 16 * kKeyBytes);
+      const u32x2 v0 = lds_read_tr16(xor_here(pvb[0], (uint32_t)((t & 3) << 6)) + u);
+      const u32x2 v1 = lds_read_tr16(xor_here(pvb[1], (uint32_t)((t & 3) << 6)) + u);
       return u32x4{v0[0], v0[1], v1[0], v1[1]};
     }
     const int m = t - 16;  // k-step m/2 of 32-key half m%2
-    return lds_read_b128(stage(j) + xor_here(kbase, (uint32_t)((m >> 1) << 5)) +
-                         (uint32_t)((m & 1) * 32 * kKeyBytes));
+    return lds_read_b128(xor_here(kb, (uint32_t)((m >> 1) << 5)) + (uint32_t)((m & 1) * 32 * kKeyBytes));
   };
   constexpr int kAhead = 8;
   u32x4 ring[kAhead];
   auto ring_start = [&](int j) {
     sched_fence();  // the reads stay after the wave's preceding work
+    phase_bases(j);
 #pragma unroll
-    for (int t = 0; t < kAhead; ++t) ring[t] = operand(j, t);
+    for (int t = 0; t < kAhead; ++t) ring[t] = operand(t);
   };
   auto mfma_phase = [&](int j) {
+    // With the soft cap the partner wave's long VALU stream would otherwise
+    // win issue slots over this wave's operand reads (the older wave goes
+    // first): the MFMA wave takes the higher priority for its phase
+    // (measured: a loss without the cap, where the VALU phase is shorter).
+    if constexpr (CAP) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       u32x4 x = ring[t % kAhead];
@@ -314,8 +323,9 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
         const floatx16 zero = {};  // k-step 0 starts from zero (an inline constant)
         sv[m & 1] = mfma_32x32x16(as_bf16x8(x), as_bf16x8(qv[m >> 1]), m < 2 ? zero : sv[m & 1]);
       }
-      if (t + kAhead < 32) ring[t % kAhead] = operand(j, t + kAhead);
+      if (t + kAhead < 32) ring[t % kAhead] = operand(t + kAhead);
     }
+    if constexpr (CAP) __builtin_amdgcn_s_setprio(0);
   };
 
   // VALU phase j: the online softmax of S_j. A row keeps a reference m_run
@@ -427,8 +437,7 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
     l_run += ls;
   };
 
-  // Block j (its raw copy for fp8) is issued in phases 2j - 4 and 2j - 3
-  // (one group each); fp8 blocks are widened by A in phase 2j - 1. A reads K_j
+  // Block j is issued in phases 2j - 4 and 2j - 3 (one group each). A reads K_j
   // in phase 2j and V_j from the end of phase 2j + 1 through 2j + 2, B reads
   // K_j in phase 2j + 1 and V_j from the end of 2j + 2 through 2j + 3, so the
   // stage is free again when block j + 4 is issued in phase 2j + 4. Every
@@ -456,22 +465,22 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   }
   __syncthreads();
 
+  // Whether group B issues its share of block b in phase 2b - 3 (and A in
+  // 2b - 4) rather than the other way round. The DMA instructions go where
+  // the wave has slack: in the VALU phases without the soft cap, in the MFMA
+  // phases with it, whose softmax is the longer half.
+  constexpr bool kLateB = CAP;
+
   // Closes phase p: this wave's DMA that the next phase needs has landed
   // (bf16: block (p + 1) / 2 after odd p; fp8: raw block p / 2 + 1 after even
-  // p, before group A widens it), then the workgroup barrier.
-  // Which group issues its share of block j + 2 in the iteration's odd phase
-  // (the other issues in the even phase). The DMA instructions go where the
-  // wave has slack: in the VALU phases without the soft cap (B in phase 2j,
-  // A in phase 2j + 1), in the MFMA phases with it (A in phase 2j, B in
-  // phase 2j + 1), whose softmax is the longer half.
-  constexpr bool kLateB = CAP;
+  // p, before group A widens it; the late group has not issued the block
+  // after that one yet), then the workgroup barrier (fp8: after the
+  // widening's LDS writes have completed).
   auto close_phase = [&](int p, auto group_b) {
-    constexpr bool kB = decltype(group_b)::value;
+    constexpr bool kLate = decltype(group_b)::value == kLateB;
     const int jw = F8 ? ((p & 1) == 0 ? p / 2 + 1 : -1) : ((p & 1) == 1 ? (p + 1) / 2 : -1);
     if (jw >= 0 && jw < nblk) {
-      // The group that issues in the odd phase (kLateB) has not issued the
-      // block after jw yet at an even close.
-      if (jw + 1 < nblk && (kB != kLateB || (p & 1) == 1))
+      if (jw + 1 < nblk && !(F8 && kLate))
         wait_vmcnt<kIPW>();
       else
         wait_vmcnt<0>();
@@ -479,73 +488,88 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
     if (F8) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     wg_barrier();
   };
-  // Iteration j (0 .. nblk) spans phases 2j and 2j + 1. Group A: MFMA phase
-  // j, then VALU phase j. Group B: VALU phase j - 1, then MFMA phase j. Each
-  // wave issues its share of block j + 2 in the phase kLateB names. Each wave
-  // starts the ring of its next MFMA phase before the barrier that opens it
-  // (the V half reads block j - 1, which every wave already holds). Each
-  // group runs its own copy of the loop, so across its back edge only P (A)
-  // or S (B) and the ring are live.
-  auto run = [&](auto group_b) {
-    constexpr bool kB = decltype(group_b)::value;
-    constexpr bool kLate = kB == kLateB;
-    // Whether the ring of the next MFMA phase is started at the end of the
-    // VALU phase (measured faster without the soft cap) or at the start of
-    // the MFMA phase (with it: its VALU phase is the longer one). fp8: group
-    // A's VALU phase also widens the next block, and a ring held across it
-    // would spill.
-    constexpr bool kEarly = !CAP && (kB || !F8);
-    if constexpr (!kB) {
-      if (wave_active && kEarly) ring_start(0);
-    }
+  // Whether the ring of the next MFMA phase is started at the end of the
+  // VALU phase (measured faster without the soft cap) or at the start of the
+  // MFMA phase (with it: its VALU phase is the longer one). fp8: group A's
+  // VALU phase also widens the next block, and a ring held across it would
+  // spill.
+  constexpr bool kEarlyA = !CAP && !F8, kEarlyB = !CAP;
+  // Group A: iteration j is MFMA phase j (phase 2j), then VALU phase j (phase
+  // 2j + 1). Group B runs one phase later: after phase 0, its iteration j is
+  // MFMA phase j (phase 2j + 1), then VALU phase j (phase 2j + 2). Each
+  // group's loop thus carries only P across its back edge. Block b is issued
+  // in phase 2b - 4 by the group that issues early and in phase 2b - 3 by the
+  // other (kLateB), and each wave starts the ring of its next MFMA phase at
+  // the end of its VALU phase when kEarly.
+  using GA = std::false_type;
+  using GB = std::true_type;
+  auto run_a = [&]() {
+    constexpr bool kLate = !kLateB;
+    constexpr bool kEarly = kEarlyA;
+    if (wave_active && kEarly) ring_start(0);
     for (int j = 0; j <= nblk; ++j) {
       const int page_dma = page_next;  // page of block j + 2
       if constexpr (!kLate) {
         if (j + 2 < nblk) issue(j + 2, page_dma);
       }
-      if constexpr (kB) {
-        // The next page id is loaded where this wave's VALU phase begins: an
-        // outstanding scalar load makes every LDS wait drain to zero.
-        if (j + 3 < nblk) page_next = page_of(j + 3);
-      }
       if (wave_active) {
-        if constexpr (kB) {
-          if (j >= 1) valu_phase(j - 1);
-          if constexpr (kEarly) ring_start(j);
-        } else {
-          if constexpr (!kEarly) ring_start(j);
-          mfma_phase(j);
-        }
+        if constexpr (!kEarly) ring_start(j);
+        mfma_phase(j);
       }
-      close_phase(2 * j, group_b);
+      close_phase(2 * j, GA{});
       if constexpr (kLate) {
         if (j + 2 < nblk) issue(j + 2, page_dma);
       }
-      if constexpr (!kB) {
-        if constexpr (F8) {
-          if (grp == 0 && j + 1 < nblk) widen(j + 1);  // group A's 256 threads
-        }
-        // The next page id is loaded where the VALU phase begins (after the
-        // widening's LDS traffic): an outstanding scalar load makes every LDS
-        // wait drain to zero.
+      if constexpr (F8) {
+        if (j + 1 < nblk) widen(j + 1);
+      }
+      // The next page id is loaded where the VALU phase begins (after the
+      // widening's LDS traffic): an outstanding scalar load makes every LDS
+      // wait drain to zero.
+      if (j + 3 < nblk) page_next = page_of(j + 3);
+      if (wave_active && j < nblk) {
+        valu_phase(j);
+        if constexpr (kEarly) ring_start(j + 1);
+      }
+      close_phase(2 * j + 1, GA{});
+    }
+  };
+  auto run_b = [&]() {
+    constexpr bool kEarly = kEarlyB;
+    if constexpr (!kLateB) {
+      if (2 < nblk) issue(2, page_next);
+      if (3 < nblk) page_next = page_of(3);
+    }
+    if (wave_active && kEarly) ring_start(0);
+    close_phase(0, GB{});
+    for (int j = 0; j <= nblk; ++j) {
+      if constexpr (kLateB) {
+        if (j + 2 < nblk) issue(j + 2, page_next);
+      }
+      if (wave_active) {
+        if constexpr (!kEarly) ring_start(j);
+        mfma_phase(j);
+      }
+      close_phase(2 * j + 1, GB{});
+      if (j == nblk) break;
+      // Page ids as in group A: loaded where the VALU phase begins.
+      if constexpr (!kLateB) {
+        if (j + 3 < nblk) issue(j + 3, page_next);
+        if (j + 4 < nblk) page_next = page_of(j + 4);
+      } else {
         if (j + 3 < nblk) page_next = page_of(j + 3);
       }
       if (wave_active) {
-        if constexpr (kB) {
-          if constexpr (!kEarly) ring_start(j);
-          mfma_phase(j);
-        } else {
-          if (j < nblk) valu_phase(j);
-          if (kEarly && j < nblk) ring_start(j + 1);
-        }
+        valu_phase(j);
+        if constexpr (kEarly) ring_start(j + 1);
       }
-      close_phase(2 * j + 1, group_b);
+      close_phase(2 * j + 2, GB{});
     }
   };
   if (grp == 0)
-    run(std::false_type{});
+    run_a();
   else
-    run(std::true_type{});
+    run_b();
 
   if (!wave_active) return;
   // Normalise and store: row lane%32, dims 32dt + 8q + 4c .. +3 in registers
@@ -577,7 +601,7 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
 
 template <int KV_DT, bool CAP>
 __global__ void __launch_bounds__(kThreads, 1) gqa_prefill_kernel(GqaArgs a, int ps_log2) {
-  __shared__ __attribute__((aligned(16))) PreSmem<KV_DT> sm;
+  __shared__ __attribute__((aligned(1024))) PreSmem<KV_DT> sm;
   const int npre = a.counters[3];
   const int home = blockIdx.x % kXcds;
   for (;;) {

@@ -255,6 +255,18 @@ __device__ __forceinline__ u32x2 lds_read_tr16(uint32_t addr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Eight OCP E4M3FN bytes (in order) to eight bf16 (in order), exactly: every
+// E4M3FN value is a bf16 value (v_cvt_scalef32_pk_bf16_fp8 at scale 1).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    r[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[h], 1.0f, false));
+    r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[h], 1.0f, true));
+  }
+  return r;
+}
+
 // Largest i in [0, n) with cu[i] <= t (the sequence owning packed token t),
 // or -1 when t is past cu[n].
 __device__ __forceinline__ int find_seq(const int32_t* cu, int n, int t) {
