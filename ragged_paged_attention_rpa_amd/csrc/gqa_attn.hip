@@ -364,6 +364,95 @@ __device__ __forceinline__ void wait_blocks_ahead(int ahead) {
     wait_vmcnt<3 * kIPW>();
 }
 
+// Writes a tile's result: with the keys split over the four waves their
+// softmax states are merged first (through `scratch`, LDS the key pipeline no
+// longer uses: 4*16*(kD + 2) floats); then either a split partial (m, l, acc)
+// or the normalised output rows.
+__device__ __forceinline__ void finish_tile(const GqaArgs& a, const Tile& tile, const TileCtx& t,
+                                            const SeqInfo& s, floatx4 (&acc)[8], float m_run,
+                                            float l_run, bool keysplit, bool wave_active,
+                                            bool row_ok, int r, float* scratch) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int G = a.geo.group;
+  // Row normaliser of this wave: the four lanes of a row each summed a quarter.
+  float l_row = wave_sum_xor<16>(l_run);
+  l_row = wave_sum_xor<32>(l_row);
+  float m_row = m_run;
+  if (keysplit) {
+    // Merge the four waves' states (disjoint key tiles) through LDS.
+    float* accs = scratch;            // [4][16][128]
+    float* mls = accs + 4 * 16 * kD;  // [4][16][2]
+    const int hl = lane & 15;
+    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<floatx4*>(accs + (wave * 16 + hl) * kD + 16 * dt + 4 * g) = acc[dt];
+    if (g == 0) {
+      mls[(wave * 16 + hl) * 2] = m_run;
+      mls[(wave * 16 + hl) * 2 + 1] = l_row;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * 16 + hl) * 2]);
+    float wt[4];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wt[w] = M == -INFINITY ? 0.f : fast_exp2(mls[(w * 16 + hl) * 2] - M);
+      L += wt[w] * mls[(w * 16 + hl) * 2 + 1];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      floatx4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const floatx4 x = *reinterpret_cast<const floatx4*>(accs + (w * 16 + hl) * kD + 16 * dt + 4 * g);
+        o[0] += wt[w] * x[0];
+        o[1] += wt[w] * x[1];
+        o[2] += wt[w] * x[2];
+        o[3] += wt[w] * x[3];
+      }
+      acc[dt] = o;
+    }
+    m_row = M;
+    l_row = L;
+  } else if (!wave_active) {
+    return;
+  }
+
+  if (tile.split >= 0 && t.nsplit > 1) {
+    const int64_t pidx = ((int64_t)t.seq * a.num_kv_heads + t.kvh) * a.geo.max_splits + tile.split;
+    if (row_ok) {
+      float* pa = a.part_acc + (pidx * kPartRows + r) * kD;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<floatx4*>(pa + 16 * dt + 4 * g) = acc[dt];
+      if (g == 0) {
+        float* pm = a.part_ml + (pidx * kPartRows + r) * 2;
+        pm[0] = m_row;
+        pm[1] = l_row;
+      }
+    }
+    return;
+  }
+  if (!row_ok) return;
+  const float inv = l_row > 0.f ? a.v_scale / l_row : 0.f;
+  const int tok = s.cu0 + t.qtok0 + r / G;
+  const int head = t.kvh * G + r % G;
+  uint16_t* op = (uint16_t*)a.out + ((int64_t)tok * a.num_q_heads + head) * kD;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    u32x2 w;
+    w[0] = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+    w[1] = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+    *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = w;
+  }
+}
+
 template <int KV_DT, int NST, bool CAP>
 __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT, NST>& sm,
                              int ps_log2) {
@@ -656,81 +745,8 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     wg_barrier();
   }
 
-  // Row normaliser of this wave: the four lanes of a row each summed a quarter.
-  float l_row = wave_sum_xor<16>(l_run);
-  l_row = wave_sum_xor<32>(l_row);
-  float m_row = m_run;
-  if (keysplit) {
-    // Merge the four waves' states (disjoint key tiles) through LDS.
-    float* accs = reinterpret_cast<float*>(sm.stage);       // [4][16][128]
-    float* mls = accs + 4 * 16 * kD;                         // [4][16][2]
-    const int hl = lane & 15;
-    __syncthreads();
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<floatx4*>(accs + (wave * 16 + hl) * kD + 16 * dt + 4 * g) = acc[dt];
-    if (g == 0) {
-      mls[(wave * 16 + hl) * 2] = m_run;
-      mls[(wave * 16 + hl) * 2 + 1] = l_row;
-    }
-    __syncthreads();
-    if (wave != 0) return;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mls[(w * 16 + hl) * 2]);
-    float wt[4];
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      wt[w] = M == -INFINITY ? 0.f : fast_exp2(mls[(w * 16 + hl) * 2] - M);
-      L += wt[w] * mls[(w * 16 + hl) * 2 + 1];
-    }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      floatx4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const floatx4 x = *reinterpret_cast<const floatx4*>(accs + (w * 16 + hl) * kD + 16 * dt + 4 * g);
-        o[0] += wt[w] * x[0];
-        o[1] += wt[w] * x[1];
-        o[2] += wt[w] * x[2];
-        o[3] += wt[w] * x[3];
-      }
-      acc[dt] = o;
-    }
-    m_row = M;
-    l_row = L;
-  } else if (!wave_active) {
-    return;
-  }
-
-  if (tile.split >= 0 && t.nsplit > 1) {
-    const int64_t pidx = ((int64_t)t.seq * a.num_kv_heads + t.kvh) * a.geo.max_splits + tile.split;
-    if (row_ok) {
-      float* pa = a.part_acc + (pidx * kPartRows + r) * kD;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<floatx4*>(pa + 16 * dt + 4 * g) = acc[dt];
-      if (g == 0) {
-        float* pm = a.part_ml + (pidx * kPartRows + r) * 2;
-        pm[0] = m_row;
-        pm[1] = l_row;
-      }
-    }
-    return;
-  }
-  if (!row_ok) return;
-  const float inv = l_row > 0.f ? a.v_scale / l_row : 0.f;
-  const int tok = s.cu0 + t.qtok0 + r / G;
-  const int head = t.kvh * G + r % G;
-  uint16_t* op = (uint16_t*)a.out + ((int64_t)tok * a.num_q_heads + head) * kD;
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    u32x2 w;
-    w[0] = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
-    w[1] = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
-    *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = w;
-  }
+  finish_tile(a, tile, t, s, acc, m_run, l_run, keysplit, wave_active, row_ok, r,
+              reinterpret_cast<float*>(sm.stage));
 }
 
 template <int KV_DT, int NST, bool CAP>
@@ -745,6 +761,256 @@ __global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_lo
     if (ti >= count) break;
     const Tile tile = a.tiles[ti];
     process_tile<KV_DT, NST, CAP>(a, tile, sm, ps_log2);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------- fp8 decode kernel --
+//
+// Decode-class tiles of an fp8 pool whenever the prefill-class tiles go to the
+// prefill kernel, so every tile here has at most 16 rows. Blocks of 128 keys
+// land raw (256 bytes per key, 32 KB, two stages) and are never widened in
+// LDS: wave w owns keys 32w .. 32w+31 of each block as two 16-key score tiles
+// and widens its own operands in registers (v_cvt_scalef32_pk_bf16_fp8,
+// exact). K comes from ds_read_b64 (eight dims of one key per lane). The two
+// score tiles leave keys 4g..4g+3 and 16+4g..16+4g+3 in lane group g, which is
+// exactly the B operand (P^T) of one 16x16x32 PV MFMA per 16 value dims, and
+// V^T for it comes from the raw rows through ds_read_b64_tr_b8 (eight keys of
+// one dim per lane). Against the 64-key path this doubles the bytes in flight
+// per workgroup and drops the widening pass with its two extra barriers.
+constexpr int kBN8 = 128;                          // keys per block
+constexpr int kRaw8Stage = kBN8 * kRawKeyBytes;    // 32768
+constexpr int kStages8 = 2;
+constexpr int kIPW8 = kRaw8Stage / 1024 / kWaves;  // DMA instructions per wave per block (8)
+constexpr int kWaveKeys8 = kBN8 / kWaves;          // keys per wave per block (32)
+
+struct Dec8Smem {
+  char stage[kStages8 * kRaw8Stage];
+  int pages[kPageWin];
+  int tile;
+};
+static_assert(4 * 16 * (kD + 2) * sizeof(float) <= sizeof(Dec8Smem::stage), "merge scratch");
+
+// Raw column rc (16 bytes: 0..7 K dims 16rc.., 8..15 V dims 16(rc-8)..) of key
+// k of a wave's 32 sits at rc ^ sw8(k). sw8 is one-to-one on each 16-key score
+// tile (the K reads) and on the keys {4g..4g+3, 16+4g..16+4g+3 : g = 2h, 2h+1}
+// that half h of the wave names in a transposed V read, so neither read has
+// bank conflicts.
+__device__ __forceinline__ int sw8(int key) { return (key & 15) ^ (((key >> 4) & 1) << 3); }
+
+template <bool CAP>
+__device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm, int ps_log2) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int g = lane >> 4;
+  const int G = a.geo.group;
+  const SeqInfo s = seq_info(a, tile.seq);
+  const TileCtx t = tile_ctx(a, tile, s);
+  const int W = a.geo.window;
+  // Every wave holds rows 0..15 (query token, q head) of the tile.
+  const int r = lane & 15;
+  const bool row_ok = r < t.nrows;
+  const int qpos = row_ok ? t.first_pos + r / G : kNegBig;
+
+  u32x4 qv[4];
+  {
+    const int tok = s.cu0 + t.qtok0 + (row_ok ? r / G : 0);
+    const int head = t.kvh * G + (row_ok ? r % G : 0);
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.num_q_heads + head) * kD;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * j + 8 * g);
+      qv[j] = v;
+    }
+  }
+
+  floatx4 acc[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kb0 = (t.lo / kBN8) * kBN8;
+  const int nblk = t.hi > kb0 ? cdiv_i(t.hi - kb0, kBN8) : 0;
+  const int32_t* table = a.page_indices + (int64_t)t.seq * a.pages_per_seq;
+  const int ps_mask = (1 << ps_log2) - 1;
+  int pwin = kb0 >> ps_log2;
+  for (int i = tid; i < kPageWin; i += kThreads) {
+    const int lp = pwin + i;
+    sm.pages[i] = lp < a.pages_per_seq ? table[lp] : -1;
+  }
+  __syncthreads();
+
+  const int64_t token_bytes = (int64_t)2 * a.num_kv_heads * kD;
+  const char* kv_head = (const char*)a.kv + (int64_t)(2 * t.kvh) * kD;
+  const uint32_t sbase = lds_addr(sm.stage);
+
+  // Block b: wave w moves its own 32 keys, four per instruction (lane L takes
+  // 16 bytes of key L/16: raw column (L%16) ^ sw8(key), so LDS position L%16
+  // of the key holds that column).
+  auto issue = [&](int b) {
+    const int kb = kb0 + b * kBN8;
+    if (((kb + kBN8 - 1) >> ps_log2) - pwin >= kPageWin) {
+      wg_barrier();
+      pwin = kb >> ps_log2;
+      for (int i = tid; i < kPageWin; i += kThreads) {
+        const int lp = pwin + i;
+        sm.pages[i] = lp < a.pages_per_seq ? table[lp] : -1;
+      }
+      __syncthreads();
+    }
+    const int key = kb + kWaveKeys8 * wave + (lane & 31);
+    const char* row = (const char*)kZeroKV;
+    if (key >= t.lo && key < t.hi) {
+      const int page = sm.pages[(key >> ps_log2) - pwin];
+      if (page >= 0 && page < a.total_num_pages)
+        row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+    }
+    const uint32_t rlo = (uint32_t)(uintptr_t)row;
+    const uint32_t rhi = (uint32_t)((uintptr_t)row >> 32);
+    const uint32_t st = sbase + (uint32_t)(b % kStages8) * kRaw8Stage +
+                        (uint32_t)wave * (kWaveKeys8 * kRawKeyBytes);
+    const int sub = lane >> 4;
+#pragma unroll
+    for (int ii = 0; ii < kIPW8; ++ii) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t l = __builtin_amdgcn_readlane(rlo, 4 * ii + k);
+        const uint32_t h = __builtin_amdgcn_readlane(rhi, 4 * ii + k);
+        lo = sub == k ? l : lo;
+        hi = sub == k ? h : hi;
+      }
+      const char* base = (const char*)(((uint64_t)hi << 32) | lo);
+      dma_b128(base + (((lane & 15) ^ sw8(4 * ii + sub)) << 4),
+               __builtin_amdgcn_readfirstlane(st + (uint32_t)ii * 1024));
+    }
+  };
+
+  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
+  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
+  auto logit = [&](float sraw) -> float {
+    if (!CAP) return sraw * c1;
+    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
+  };
+
+  // K operand (tile tt, k-step j) at ka ^ (j << 5 | tt << 7) + tt * 16 rows:
+  // key tt*16 + lane%16, dims 8(g + 4j) .. +7 = half g&1 of raw column 2j + g/2.
+  const int km = lane & 15;
+  const uint32_t ka = (uint32_t)(km * kRawKeyBytes + (((lane >> 5) ^ km) << 4) + 8 * (g & 1));
+  // V^T operand of dims 16dt.. at va ^ (dt << 4): lanes 2r, 2r+1 of group g
+  // name key slot r, i.e. key 4g + r (r < 4) or 16 + 4g + r - 4.
+  const int vslot = (lane & 15) >> 1;
+  const int vkey = vslot < 4 ? 4 * g + vslot : 16 + 4 * g + (vslot - 4);
+  const uint32_t va = (uint32_t)(vkey * kRawKeyBytes + ((8 ^ sw8(vkey)) << 4) + 8 * (lane & 1));
+
+  drain_vmem_before_loop();
+  if (nblk > 0) issue(0);
+  for (int b = 0; b < nblk; ++b) {
+    if (b + 1 < nblk) issue(b + 1);
+    wait_blocks_ahead<kIPW8>(min(1, nblk - 1 - b));
+    wg_barrier();
+    const uint32_t cur = sbase + (uint32_t)(b % kStages8) * kRaw8Stage +
+                         (uint32_t)wave * (kWaveKeys8 * kRawKeyBytes);
+    const int kw = kb0 + b * kBN8 + kWaveKeys8 * wave;  // first key of this wave's share
+    u32x2 kr[2][4], vr[8];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        kr[tt][j] = lds_read_b64(cur + (ka ^ (uint32_t)((j << 5) | (tt << 7))) +
+                                 (uint32_t)(tt * 16 * kRawKeyBytes));
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) vr[dt] = lds_read_tr8(cur + (va ^ (uint32_t)(dt << 4)));
+    floatx4 sv[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sv[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[tt] = mfma_16x16x32(as_bf16x8(fp8x8_to_bf16x8(kr[tt][j])), as_bf16x8(qv[j]), sv[tt]);
+    }
+    // sv[tt][i] of lane group g is key kw + 16tt + 4g + i of row lane%16.
+    float mblk = -INFINITY;
+    const bool all_vis =
+        __builtin_amdgcn_ballot_w64(row_ok && !(kw >= t.lo && kw + kWaveKeys8 <= t.hi &&
+                                                kw + kWaveKeys8 - 1 <= qpos &&
+                                                (W <= 0 || kw > qpos - W))) == 0;
+    if (all_vis) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[tt][i] = logit(sv[tt][i]);
+          mblk = fmaxf(mblk, sv[tt][i]);
+        }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kw + 16 * tt + 4 * g + i;
+          const bool vis =
+              key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
+          sv[tt][i] = vis ? logit(sv[tt][i]) : -INFINITY;
+          mblk = fmaxf(mblk, sv[tt][i]);
+        }
+    }
+    mblk = wave_max_xor<16>(mblk);
+    mblk = wave_max_xor<32>(mblk);
+    const bool need = mblk > m_run + kLazyTau;
+    if (wave_any(need)) {
+      const float m_new = need ? mblk : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;  // rows not moving keep scale 1
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        acc[dt][0] *= alpha;
+        acc[dt][1] *= alpha;
+        acc[dt][2] *= alpha;
+        acc[dt][3] *= alpha;
+      }
+      m_run = m_new;
+    }
+    u32x4 pb = {0u, 0u, 0u, 0u};
+    if (m_run != -INFINITY) {
+      float psum = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sv[tt][i] = fast_exp2(sv[tt][i] - m_run);
+          psum += sv[tt][i];
+        }
+      l_run += psum;
+      pb[0] = pack_bf16x2(sv[0][0], sv[0][1]);
+      pb[1] = pack_bf16x2(sv[0][2], sv[0][3]);
+      pb[2] = pack_bf16x2(sv[1][0], sv[1][1]);
+      pb[3] = pack_bf16x2(sv[1][2], sv[1][3]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      acc[dt] = mfma_16x16x32(as_bf16x8(fp8x8_to_bf16x8(vr[dt])), as_bf16x8(pb), acc[dt]);
+    wg_barrier();
+  }
+
+  finish_tile(a, tile, t, s, acc, m_run, l_run, true, true, row_ok, r,
+              reinterpret_cast<float*>(sm.stage));
+}
+
+template <bool CAP>
+__global__ void __launch_bounds__(kThreads) gqa_decode8_kernel(GqaArgs a, int ps_log2) {
+  __shared__ __attribute__((aligned(1024))) Dec8Smem sm;
+  const int count = a.counters[0];
+  for (;;) {
+    if (threadIdx.x == 0) sm.tile = atomicAdd(&a.counters[1], 1);
+    __syncthreads();
+    const int ti = sm.tile;
+    __syncthreads();
+    if (ti >= count) break;
+    const Tile tile = a.tiles[ti];
+    process_decode8<CAP>(a, tile, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -980,6 +1246,14 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
       RPA_TILE_LAUNCH(DT_BF16, true);
     else
       RPA_TILE_LAUNCH(DT_BF16, false);
+  } else if (a.pre_kernel) {
+    // Only decode-class tiles are left for this launch: the fp8 decode kernel.
+    if (cap)
+      hipLaunchKernelGGL(gqa_decode8_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a,
+                         ps_log2);
+    else
+      hipLaunchKernelGGL(gqa_decode8_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a,
+                         ps_log2);
   } else {
     if (cap)
       RPA_TILE_LAUNCH(DT_FP8, true);

@@ -246,6 +246,21 @@ __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
       (__attribute__((address_space(3))) char*)(uintptr_t)addr);
 }
 
+__device__ __forceinline__ u32x2 lds_read_b64(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x2*>(
+      (__attribute__((address_space(3))) char*)(uintptr_t)addr);
+}
+
+// ds_read_b64_tr_b8: within each 16-lane group, lanes 2r and 2r+1 name the two
+// 8-byte halves of a 16-byte row r (r = 0..7); lane j of the group receives
+// byte j of rows 0..7, in row order.
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t addr) {
+  typedef int intx2 __attribute__((ext_vector_type(2)));
+  intx2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) intx2*)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // ds_read_b64_tr_b16: within each 16-lane group the four lanes 4r..4r+3 name
 // row r (4 consecutive b16 each); lane j of the group receives column j of the
 // 4x16 block, i.e. element j of rows 0..3.

@@ -90,6 +90,21 @@ def test_ragged_bf16(idx):
     _check(c, _run_gpu(c), _run_oracle(c), "bf16")
 
 
+@pytest.mark.parametrize("idx", range(len(RAGGED)), ids=[r[-1] for r in RAGGED])
+def test_ragged_fp8(idx):
+    """The ragged cases over an fp8 pool with k/v scales: decode-class tiles go
+    to the fp8 decode kernel (128-key raw blocks) whenever the prefill kernel
+    takes the prefill-class tiles, and to the 64-key tile kernel otherwise
+    (page size 4)."""
+    seqs, Hq, Hkv, ps, window, cap, name = RAGGED[idx]
+    _say(f"ragged fp8 {name}")
+    c = wl.make_gqa(seqs, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=ps,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn, seed=200 + idx,
+                    device="cuda", kv_value_scale=2.0, sliding_window=window, soft_cap=cap,
+                    k_scale=0.5, v_scale=0.5, name=name + "-fp8")
+    _check(c, _run_gpu(c), _run_oracle(c), "fp8")
+
+
 @pytest.mark.parametrize("cap,qscale,ps", [(None, 1.0, 16), (50.0, 1.0, 16), (50.0, 16.0, 16),
                                             (None, 1.0, 8)])
 def test_ragged_fp8_scales(cap, qscale, ps):
