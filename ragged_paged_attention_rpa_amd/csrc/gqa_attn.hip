@@ -18,6 +18,8 @@
 //                        flash_attention (alpha = e^{m_i - m*}).
 // The per-row arithmetic follows the page: scale, optional soft cap, mask
 // (causal offset kv_len - q_len, optional sliding window), softmax, P V.
+#include <mutex>
+
 #include "rpa_device.h"
 #include "rpa_internal.h"
 
@@ -1217,6 +1219,56 @@ void gqa_bind_workspace(GqaArgs& a, void* ws) {
   a.part_acc = (float*)p;
 }
 
+// Library-owned side stream per device (default priority) with its fork and
+// join events. When the prefill kernel runs on a batch with room for a real
+// prefill share, the decode-class launch goes to the side stream, so its
+// workgroups take CUs as the prefill kernel's workgroups run out of tiles
+// instead of waiting for the last one. The fork and join cost ~20 us, more
+// than the prefill kernel's tail on a batch of decodes, so batches whose token
+// capacity leaves fewer than kOverlapMinTokens tokens beyond one per sequence
+// stay on one stream (the results are the same either way).
+constexpr int64_t kOverlapMinTokens = 2048;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+// Fork: work later enqueued on the returned stream starts after what `stream`
+// holds now. Returns nullptr (caller stays on one stream) if it cannot be set up.
+SideStream* side_fork(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
+      ss.s = nullptr;
+      return nullptr;
+    }
+    if (hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      (void)hipStreamDestroy(ss.s);
+      ss.s = nullptr;
+      return nullptr;
+    }
+  }
+  // Record and wait under the lock: another caller's fork cannot slip between.
+  if (hipEventRecord(ss.fork, stream) != hipSuccess ||
+      hipStreamWaitEvent(ss.s, ss.fork, 0) != hipSuccess)
+    return nullptr;
+  return &ss;
+}
+
+hipError_t side_join(SideStream* ss, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  hipError_t e = hipEventRecord(ss->join, ss->s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, ss->join, 0);
+  return e;
+}
+
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   int ps_log2 = 0;
   while ((1 << ps_log2) < a.page_size) ++ps_log2;
@@ -1229,18 +1281,22 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   // slower: the compute of a block is then exposed).
   const int grid = max(1, min(a.tile_capacity, num_cus() * 2));
   prof_begin(stream);
+  hipStream_t dstream = stream;
+  SideStream* side = nullptr;
   if (a.pre_kernel) {
-    // Prefill-class tiles first, on the eight-wave kernel (one workgroup per CU).
+    if ((int64_t)a.max_num_tokens - a.max_num_seqs >= kOverlapMinTokens) side = side_fork(stream);
+    if (side) dstream = side->s;
+    // Prefill-class tiles on the eight-wave kernel (one workgroup per CU).
     prof_kernel_begin(stream, 0);
     const hipError_t e = launch_gqa_prefill(a, ps_log2, num_cus(), stream);
     if (e != hipSuccess) return e;
     prof_kernel_end(stream, 0);
   }
-  prof_kernel_begin(stream, 1);
+  prof_kernel_begin(dstream, 1);
   const bool cap = a.soft_cap != 0.f;
 #define RPA_TILE_LAUNCH(DT, CAP)                                                         \
   hipLaunchKernelGGL((gqa_tile_kernel<DT, kStages, CAP>), dim3(grid), dim3(kThreads), 0, \
-                     stream, a, ps_log2)
+                     dstream, a, ps_log2)
   if (a.kv_dtype == DT_BF16) {
     if (cap)
       RPA_TILE_LAUNCH(DT_BF16, true);
@@ -1249,10 +1305,10 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   } else if (a.pre_kernel) {
     // Only decode-class tiles are left for this launch: the fp8 decode kernel.
     if (cap)
-      hipLaunchKernelGGL(gqa_decode8_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, a,
+      hipLaunchKernelGGL(gqa_decode8_kernel<true>, dim3(grid), dim3(kThreads), 0, dstream, a,
                          ps_log2);
     else
-      hipLaunchKernelGGL(gqa_decode8_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, a,
+      hipLaunchKernelGGL(gqa_decode8_kernel<false>, dim3(grid), dim3(kThreads), 0, dstream, a,
                          ps_log2);
   } else {
     if (cap)
@@ -1261,12 +1317,17 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
       RPA_TILE_LAUNCH(DT_FP8, false);
   }
 #undef RPA_TILE_LAUNCH
-  prof_kernel_end(stream, 1);
-  prof_end(stream);
+  prof_kernel_end(dstream, 1);
   if (a.geo.qdec > 0)
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(a.max_num_seqs * a.num_kv_heads), dim3(kThreads),
-                       0, stream, a);
-  return hipGetLastError();
+                       0, dstream, a);
+  hipError_t e = hipGetLastError();
+  if (side) {
+    const hipError_t j = side_join(side, stream);
+    if (e == hipSuccess) e = j;
+  }
+  prof_end(stream);
+  return e;
 }
 
 hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream) {

@@ -105,6 +105,38 @@ def test_ragged_fp8(idx):
     _check(c, _run_gpu(c), _run_oracle(c), "fp8")
 
 
+@pytest.mark.parametrize("idx,kv", [(1, "bf16"), (4, "fp8"), (6, "fp8")])
+def test_side_stream_launch(idx, kv):
+    """Batches whose token capacity leaves room for a prefill share run the
+    decode-class launch on the library's side stream, concurrently with the
+    prefill kernel: parity, and three back-to-back calls on one workspace give
+    identical outputs (each call's planner waits for the previous call's side
+    work)."""
+    seqs, Hq, Hkv, ps, window, cap, name = RAGGED[idx]
+    _say(f"side stream {name} {kv}")
+    kvd = torch.bfloat16 if kv == "bf16" else torch.float8_e4m3fn
+    extra = dict(kv_value_scale=2.0, k_scale=0.5, v_scale=0.5) if kv == "fp8" else {}
+    c = wl.make_gqa(seqs, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=ps,
+                    q_dtype=torch.bfloat16, kv_dtype=kvd, seed=300 + idx, device="cuda",
+                    sliding_window=window, soft_cap=cap, extra_tokens=4096,
+                    name=f"{name}-side-{kv}", **extra)
+    kl, pi, cu, ns = _dev_meta(c)
+    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], Hq, Hkv, 128, ps)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.zeros_like(c.q)
+        rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, sm_scale=c.sm_scale,
+                        sliding_window=c.sliding_window, soft_cap=c.soft_cap,
+                        k_scale=c.k_scale, v_scale=c.v_scale, out=out, workspace=ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    T = int(c.cu_q_lens[c.num_seqs])
+    for o in outs[1:]:
+        assert torch.equal(o[:T], outs[0][:T])
+    _check(c, outs[0], _run_oracle(c), kv)
+
+
 @pytest.mark.parametrize("cap,qscale,ps", [(None, 1.0, 16), (50.0, 1.0, 16), (50.0, 16.0, 16),
                                             (None, 1.0, 8)])
 def test_ragged_fp8_scales(cap, qscale, ps):
