@@ -589,7 +589,12 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     if (b + NST - 1 < nblk) issue(b + NST - 1);
     // Blocks issued after block b: min(NST-1, nblk-1-b).
     wait_blocks_ahead<kIPW>(min(NST - 1, nblk - 1 - b));
-    wg_barrier();
+    // bf16 decode tiles: each wave moves and reads only its own 16 keys of a
+    // block (its own 8 KB of the stage), so its vmcnt wait is all it needs.
+    // Prefill-class tiles share every key, and fp8 blocks are widened by all
+    // waves together: those synchronise the workgroup.
+    const bool shared = !keysplit || KV_DT != DT_BF16;
+    if (shared) wg_barrier();
     uint32_t cur = sbase + (uint32_t)(b % NST) * dma_stride;
     if (KV_DT == DT_FP8) {
       // Widen the raw block: thread tid takes raw column tid/16 (16 fp8
@@ -744,7 +749,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
         sched_fence();
       }
     }
-    wg_barrier();
+    if (shared) wg_barrier();
   }
 
   finish_tile(a, tile, t, s, acc, m_run, l_run, keysplit, wave_active, row_ok, r,
@@ -778,8 +783,9 @@ __global__ void __launch_bounds__(kThreads) gqa_tile_kernel(GqaArgs a, int ps_lo
 // score tiles leave keys 4g..4g+3 and 16+4g..16+4g+3 in lane group g, which is
 // exactly the B operand (P^T) of one 16x16x32 PV MFMA per 16 value dims, and
 // V^T for it comes from the raw rows through ds_read_b64_tr_b8 (eight keys of
-// one dim per lane). Against the 64-key path this doubles the bytes in flight
-// per workgroup and drops the widening pass with its two extra barriers.
+// one dim per lane). Each wave moves and reads only its own keys, so the
+// waves run without workgroup barriers. Against the 64-key path this doubles
+// the bytes in flight per workgroup and drops the widening pass.
 constexpr int kBN8 = 128;                          // keys per block
 constexpr int kRaw8Stage = kBN8 * kRawKeyBytes;    // 32768
 constexpr int kStages8 = 2;
@@ -911,8 +917,9 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
   if (nblk > 0) issue(0);
   for (int b = 0; b < nblk; ++b) {
     if (b + 1 < nblk) issue(b + 1);
+    // Each wave moves and reads only its own 32 keys (its 8 KB of the stage),
+    // so its own vmcnt wait suffices: no workgroup barrier per block.
     wait_blocks_ahead<kIPW8>(min(1, nblk - 1 - b));
-    wg_barrier();
     const uint32_t cur = sbase + (uint32_t)(b % kStages8) * kRaw8Stage +
                          (uint32_t)wave * (kWaveKeys8 * kRawKeyBytes);
     const int kw = kb0 + b * kBN8 + kWaveKeys8 * wave;  // first key of this wave's share
@@ -994,7 +1001,6 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       acc[dt] = mfma_16x16x32(as_bf16x8(fp8x8_to_bf16x8(vr[dt])), as_bf16x8(pb), acc[dt]);
-    wg_barrier();
   }
 
   finish_tile(a, tile, t, s, acc, m_run, l_run, true, true, row_ok, r,
