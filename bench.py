@@ -45,6 +45,8 @@ KERNEL_SOURCES = {
     "tiny_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
     "mla_decode": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
     "sparse_mla": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
+    # the mixed batch's decode subset (--decode-subset only): the fp8 decode kernel
+    "mixed_gqa_decode": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
 }
 KERNEL_NAMES = {
     "decode_gqa": "gqa_tile_kernel",
@@ -52,6 +54,7 @@ KERNEL_NAMES = {
     "tiny_gqa": "gqa_generic_kernel",
     "mla_decode": "mla_tile_kernel",
     "sparse_mla": "sparse_mla_kernel",
+    "mixed_gqa_decode": "gqa_decode8_kernel",
 }
 
 
@@ -289,9 +292,19 @@ def load_traffic(config):
     return d.get("hbm_bytes_per_launch")
 
 
+def _leading_decodes(case):
+    """Number of leading decode-class sequences (q_len * G <= 16) of a batch."""
+    G = case.num_q_heads // case.num_kv_heads
+    big = np.diff(case.cu_q_lens[:case.num_seqs + 1]) * G > 16
+    return int(np.argmax(big)) if np.any(big) else case.num_seqs
+
+
 def bench_gqa(args, torch, rpa, wl):
     case, fn = setup_gqa(torch, rpa, wl, args.config)
     work = gqa_work(case)
+    subset = getattr(args, "decode_subset", "on")
+    if args.config == "mixed_gqa" and subset == "only":
+        fn.ns.fill_(_leading_decodes(case))
     ms, kern_mean, kern_med, parts = timed_loop(torch, rpa, fn, args.steps, args.warmup, split=True)
     step_s = ms / 1e3
     res = {"ms_per_step": ms, "attention_kernels_ms_mean": kern_mean,
@@ -311,6 +324,18 @@ def bench_gqa(args, torch, rpa, wl):
                            "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                            "algorithmic_bytes_per_launch": work["kv_bytes"],
                            "kernel": "gqa_tile_kernel"}
+    elif subset == "only":
+        # Profiling aid: the mixed batch's leading decode sequences alone.
+        kern_s = parts["decode_kernel_ms"] / 1e3
+        res["kernel_ms_mean"] = parts["decode_kernel_ms"]
+        gbs = work["decode_kv_bytes"] / step_s / 1e9
+        res.update(value=gbs, unit="GB/s", pct_hbm_peak=100 * gbs / HBM_PEAK_GBS,
+                   decode_seqs=_leading_decodes(case))
+        ach = work["decode_kv_bytes"] / kern_s / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBS, "traffic": load_traffic("mixed_gqa_decode"),
+                           "algorithmic_bytes_per_launch": work["decode_kv_bytes"],
+                           "kernel": "gqa_decode8_kernel"}
     else:  # mixed: prefill TFLOP/s on the prefill-tile kernel, decode GB/s on the decode-tile kernel
         pre_s = parts["prefill_kernel_ms"] / 1e3
         res["kernel_ms_mean"] = parts["prefill_kernel_ms"]
@@ -327,18 +352,18 @@ def bench_gqa(args, torch, rpa, wl):
         # for CUs; its rate is taken on the batch's decode subset (the leading
         # decode sequences alone, same kernel, same inputs).
         res["decode_kernel_span_in_batch_ms"] = res.pop("decode_kernel_ms")
-        G = case.num_q_heads // case.num_kv_heads
-        q_lens = np.diff(case.cu_q_lens[:case.num_seqs + 1])
-        n_dec = int(np.argmax(q_lens * G > 16)) if np.any(q_lens * G > 16) else case.num_seqs
-        fn.ns.fill_(n_dec)
-        _, _, _, dparts = timed_loop(torch, rpa, fn, args.steps, args.warmup, split=True)
-        fn.ns.fill_(case.num_seqs)
-        dec_s = dparts["decode_kernel_ms"] / 1e3
-        dgb = work["decode_kv_bytes"] / dec_s / 1e9
-        res["decode_part"] = {"kernel": "gqa_decode8_kernel", "decode_seqs": n_dec,
-                              "kernel_ms": dparts["decode_kernel_ms"], "achieved_GBs": dgb,
-                              "frac_hbm": dgb / HBM_PEAK_GBS,
-                              "algorithmic_bytes_per_launch": work["decode_kv_bytes"]}
+        if subset == "on":
+            n_dec = _leading_decodes(case)
+            fn.ns.fill_(n_dec)
+            _, _, _, dparts = timed_loop(torch, rpa, fn, args.steps, args.warmup, split=True)
+            fn.ns.fill_(case.num_seqs)
+            dec_s = dparts["decode_kernel_ms"] / 1e3
+            dgb = work["decode_kv_bytes"] / dec_s / 1e9
+            res["decode_part"] = {"kernel": "gqa_decode8_kernel", "decode_seqs": n_dec,
+                                  "kernel_ms": dparts["decode_kernel_ms"], "achieved_GBs": dgb,
+                                  "frac_hbm": dgb / HBM_PEAK_GBS,
+                                  "traffic": load_traffic("mixed_gqa_decode"),
+                                  "algorithmic_bytes_per_launch": work["decode_kv_bytes"]}
         roof_s = max(work["flops"] / (BF16_PEAK_TFLOPS * 1e12),
                      work["kv_bytes"] / (HBM_PEAK_GBS * 1e9))
         res["combined_roof_us"] = roof_s * 1e6
@@ -482,6 +507,9 @@ def main():
     ap.add_argument("--config", default="decode_gqa",
                     choices=["decode_gqa", "mixed_gqa", "tiny_gqa", "mla_decode", "sparse_mla"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-subset", choices=("on", "off", "only"), default="on",
+                    help="mixed_gqa: also time the batch's decode subset alone (on), skip it "
+                         "(off), or time only the subset (only; for profiling that kernel)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="target seconds of oracle CPU work for cpu_baseline")
     ap.add_argument("--copy-bytes", type=int, default=0,
