@@ -180,13 +180,32 @@ class HipEvents:
         self.pairs = []
 
 
-def timed_loop(torch, rpa, fn, steps, warmup, split=False):
+FLUSH_BYTES = 512 << 20
+_flush_buf = []
+
+
+def cache_flush(torch):
+    """Reads a 512 MB scratch buffer on the current stream, which evicts the
+    L2s and the 256 MB MALL: the step after it reads its inputs from HBM. A
+    read, not a write: a written buffer leaves dirty lines whose write-back
+    then competes with the next step's reads (measured: the decode batch's
+    kernel 14% slower after a 512 MB fill than after this read)."""
+    if not _flush_buf:
+        _flush_buf.append(torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda"))
+        _flush_buf.append(torch.zeros((), dtype=torch.int64, device="cuda"))
+    torch.sum(_flush_buf[0], dim=0, dtype=torch.int64, out=_flush_buf[1])
+
+
+def timed_loop(torch, rpa, fn, steps, warmup, split=False, flush=None):
     """Runs `warmup` untimed steps, then exactly `steps` steps between two
     device synchronisations; returns (wall ms/step, mean and median duration
-    of the dominant kernel(s) in ms from the library's event hook, and with
-    `split` the mean durations of rpa_forward's prefill-tile and decode-tile
-    kernels in ms)."""
+    of the dominant kernel(s) in ms from the library's event hook, and a dict
+    with their minimum and, with `split`, the mean and minimum durations of
+    rpa_forward's prefill-tile and decode-tile kernels in ms). With `flush`,
+    it runs before every step (cold caches; the wall time then includes it)."""
     for _ in range(warmup):
+        if flush:
+            flush()
         fn()
     torch.cuda.synchronize()
     ev = HipEvents(steps)
@@ -194,6 +213,8 @@ def timed_loop(torch, rpa, fn, steps, warmup, split=False):
     lib = rpa.load_library()
     t0 = time.perf_counter()
     for k in range(steps):
+        if flush:
+            flush()
         lib.rpa_set_profile_events(ev.pairs[k][0], ev.pairs[k][1])
         if split:
             lib.rpa_set_profile_events_split(evs.pairs[2 * k][0], evs.pairs[2 * k][1],
@@ -204,14 +225,46 @@ def timed_loop(torch, rpa, fn, steps, warmup, split=False):
     lib.rpa_set_profile_events(None, None)
     kern = [ev.elapsed_ms(k) for k in range(steps)]
     ev.close()
-    parts = None
+    parts = {"kernel_ms_min": float(np.min(kern))}
     if split:
         lib.rpa_set_profile_events_split(None, None, None, None)
         pre = [evs.elapsed_ms(2 * k) for k in range(steps)]
         dec = [evs.elapsed_ms(2 * k + 1) for k in range(steps)]
         evs.close()
-        parts = {"prefill_kernel_ms": float(np.mean(pre)), "decode_kernel_ms": float(np.mean(dec))}
+        parts.update(prefill_kernel_ms=float(np.mean(pre)), decode_kernel_ms=float(np.mean(dec)),
+                     prefill_kernel_ms_min=float(np.min(pre)),
+                     decode_kernel_ms_min=float(np.min(dec)))
     return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), float(np.median(kern)), parts
+
+
+def measure(args, torch, rpa, fn, split=False):
+    """The warm loop (back-to-back steps: the timed region behind `value` and
+    the roofline) and the cold loop (a read of a 512 MB buffer before each step
+    evicts L2 and MALL, so each step reads its inputs from HBM; reported beside
+    the warm figures). --cache warm runs only the warm loop (profiling runs, so
+    a trace holds exactly the launches the roofline averages); --cache cold
+    only the cold one. Returns (primary, cold or None)."""
+    mode = getattr(args, "cache", "both")
+    cold = None
+    if mode != "warm":
+        cold = timed_loop(torch, rpa, fn, args.steps, max(1, args.warmup // 2), split,
+                          flush=lambda: cache_flush(torch))
+    warm = timed_loop(torch, rpa, fn, args.steps, args.warmup, split) if mode != "cold" else None
+    return (warm or cold), cold
+
+
+def cold_summary(cold, key="kernel"):
+    """Cold-start kernel durations (ms) from a measure() result."""
+    if cold is None:
+        return None
+    _, kmean, kmed, parts = cold
+    out = {"flush": "512 MB read before each step", "kernel_ms_mean": kmean,
+           "kernel_ms_median": kmed, "kernel_ms_min": parts["kernel_ms_min"]}
+    for k in ("prefill_kernel_ms", "decode_kernel_ms"):
+        if k in parts:
+            out[k] = parts[k]
+            out[k + "_min"] = parts[k + "_min"]
+    return out
 
 
 def setup_gqa(torch, rpa, wl, config):
@@ -305,12 +358,14 @@ def bench_gqa(args, torch, rpa, wl):
     subset = getattr(args, "decode_subset", "on")
     if args.config == "mixed_gqa" and subset == "only":
         fn.ns.fill_(_leading_decodes(case))
-    ms, kern_mean, kern_med, parts = timed_loop(torch, rpa, fn, args.steps, args.warmup, split=True)
+    (ms, kern_mean, kern_med, parts), cold = measure(args, torch, rpa, fn, split=True)
     step_s = ms / 1e3
     res = {"ms_per_step": ms, "attention_kernels_ms_mean": kern_mean,
            "attention_kernels_ms_median": kern_med, "q_tokens": work["q_tokens"],
            "tokens_per_s": work["q_tokens"] / step_s}
     res.update(parts)
+    if cold is not None:
+        res["cold"] = cold_summary(cold)
     traffic = load_traffic(args.config)
     if args.config == "decode_gqa" or args.config == "tiny_gqa":
         # Dominant kernel: the decode-tile kernel (a batch of decodes has no
@@ -355,7 +410,7 @@ def bench_gqa(args, torch, rpa, wl):
         if subset == "on":
             n_dec = _leading_decodes(case)
             fn.ns.fill_(n_dec)
-            _, _, _, dparts = timed_loop(torch, rpa, fn, args.steps, args.warmup, split=True)
+            (_, _, _, dparts), dcold = measure(args, torch, rpa, fn, split=True)
             fn.ns.fill_(case.num_seqs)
             dec_s = dparts["decode_kernel_ms"] / 1e3
             dgb = work["decode_kv_bytes"] / dec_s / 1e9
@@ -364,6 +419,10 @@ def bench_gqa(args, torch, rpa, wl):
                                   "frac_hbm": dgb / HBM_PEAK_GBS,
                                   "traffic": load_traffic("mixed_gqa_decode"),
                                   "algorithmic_bytes_per_launch": work["decode_kv_bytes"]}
+            if dcold is not None:
+                dc = dcold[3]["decode_kernel_ms"]
+                res["decode_part"]["cold"] = {"kernel_ms": dc,
+                                              "achieved_GBs": work["decode_kv_bytes"] / dc / 1e6}
         roof_s = max(work["flops"] / (BF16_PEAK_TFLOPS * 1e12),
                      work["kv_bytes"] / (HBM_PEAK_GBS * 1e9))
         res["combined_roof_us"] = roof_s * 1e6
@@ -417,12 +476,14 @@ def bench_latent(args, torch, rpa, wl):
                                 case.cache_k_pe, kl, pi, cu, ns, sm_scale=case.sm_scale, out=out,
                                 workspace=ws)
         work = mla_work(case, H)
-        ms, kmean, kmed, _ = timed_loop(torch, rpa, fn, args.steps, args.warmup)
-        ms_attn, _, _, _ = timed_loop(torch, rpa, lambda: fn(False), args.steps, args.warmup)
+        (ms, kmean, kmed, kparts), cold = measure(args, torch, rpa, fn)
+        ms_attn = timed_loop(torch, rpa, lambda: fn(False), args.steps, args.warmup)[0] \
+            if getattr(args, "cache", "both") == "both" else None
         gbs = work["kv_bytes"] / (ms / 1e3) / 1e9
         ach = work["kv_bytes"] / (kmean / 1e3) / 1e9
         res = {"value": gbs, "unit": "GB/s", "ms_per_step": ms, "kernel_ms_mean": kmean,
-               "kernel_ms_median": kmed, "ms_per_step_attention_only": ms_attn,
+               "kernel_ms_median": kmed, "kernel_ms_min": kparts["kernel_ms_min"],
+               "cold": cold_summary(cold), "ms_per_step_attention_only": ms_attn,
                "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
                "tokens_per_s": work["q_tokens"] / (ms / 1e3),
                "mfma_tflops_in_kernel": work["flops"] / (kmean / 1e3) / 1e12,
@@ -464,11 +525,13 @@ def bench_latent(args, torch, rpa, wl):
         rpa.sparse_mla_forward(case.q, case.kv_cache, pt, idx, pos, seq_len=case.seq_len,
                                read_block=case.read_block, sm_scale=case.sm_scale, out=out)
     work = sparse_work(case)
-    ms, kmean, kmed, _ = timed_loop(torch, rpa, fn, args.steps, args.warmup)
+    (ms, kmean, kmed, kparts), cold = measure(args, torch, rpa, fn)
     tf = work["flops"] / (ms / 1e3) / 1e12
     ach = work["flops"] / (kmean / 1e3) / 1e12
     res = {"value": tf, "unit": "TFLOP/s", "ms_per_step": ms, "kernel_ms_mean": kmean,
-           "kernel_ms_median": kmed, "pct_mfma_peak": 100 * tf / BF16_PEAK_TFLOPS,
+           "kernel_ms_median": kmed, "kernel_ms_min": kparts["kernel_ms_min"],
+           "cold": cold_summary(cold),
+           "pct_mfma_peak": 100 * tf / BF16_PEAK_TFLOPS,
            "gathered_gbs_in_kernel": work["gathered_bytes"] / (kmean / 1e3) / 1e9,
            "tokens_per_s": work["q_tokens"] / (ms / 1e3),
            "roofline": {"bound": "mfma", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
@@ -507,6 +570,10 @@ def main():
     ap.add_argument("--config", default="decode_gqa",
                     choices=["decode_gqa", "mixed_gqa", "tiny_gqa", "mla_decode", "sparse_mla"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cache", choices=("both", "warm", "cold"), default="both",
+                    help="both: the warm timed region (value, roofline) plus a cold pass (a "
+                         "512 MB read evicts L2 and MALL before each step); warm / cold: only "
+                         "that loop (warm for profiling runs)")
     ap.add_argument("--decode-subset", choices=("on", "off", "only"), default="on",
                     help="mixed_gqa: also time the batch's decode subset alone (on), skip it "
                          "(off), or time only the subset (only; for profiling that kernel)")
