@@ -105,6 +105,22 @@ def test_ragged_fp8(idx):
     _check(c, _run_gpu(c), _run_oracle(c), "fp8")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_decode_page_window_refill(kv):
+    """Decode splits longer than the 512 page ids a workgroup caches in LDS:
+    at page size 8, sequences of 66k-70k keys hit the 16-split cap, so each
+    split spans ~550 pages and the decode kernels refill their page window
+    mid-tile (bf16: gqa_tile_kernel; fp8: gqa_decode8_kernel)."""
+    _say(f"decode page-window refill {kv}")
+    kvd = torch.bfloat16 if kv == "bf16" else torch.float8_e4m3fn
+    extra = dict(kv_value_scale=2.0, k_scale=0.5, v_scale=0.5) if kv == "fp8" else {}
+    c = wl.make_gqa([(1, 70000), (2, 66001), (1, 9000)], num_q_heads=8, num_kv_heads=2,
+                    head_dim=128, page_size=8, q_dtype=torch.bfloat16, kv_dtype=kvd, seed=77,
+                    device="cuda", sliding_window=None, soft_cap=None, name=f"refill-{kv}",
+                    **extra)
+    _check(c, _run_gpu(c), _run_oracle(c), kv)
+
+
 @pytest.mark.parametrize("idx,kv", [(1, "bf16"), (4, "fp8"), (6, "fp8")])
 def test_side_stream_launch(idx, kv):
     """Batches whose token capacity leaves room for a prefill share run the
