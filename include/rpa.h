@@ -29,6 +29,12 @@
  *    are given by rpa_dtype (bf16 = upper half of binary32; fp8 = OCP E4M3FN).
  *  - Calls are asynchronous on `stream` (NULL = the default stream). Unless
  *    rpa_opts.debug_validate is set, no call synchronises with the host.
+ *  - rpa_forward on a batch whose token capacity leaves room for a prefill
+ *    share runs its decode-class launch on a library-owned stream of the
+ *    current device (created on first use, default priority, kept until the
+ *    process ends), forked from `stream` with an event and joined back into it
+ *    before the call returns: to the caller all of the call's work is ordered
+ *    on `stream`, and the call can be captured into a graph like any other.
  *  - On any error the call returns a non-zero rpa_status, launches nothing,
  *    and rpa_last_error() describes the first problem found (thread-local).
  *  - Outputs are written in the query dtype for rpa_forward/mla_rpa_forward
