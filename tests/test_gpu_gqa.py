@@ -153,6 +153,49 @@ def test_side_stream_launch(idx, kv):
     _check(c, outs[0], _run_oracle(c), kv)
 
 
+def test_graph_capture_with_side_stream():
+    """rpa_forward captured into a HIP graph (through torch) on a batch that
+    takes the side-stream path: the fork and join events pull the side stream
+    into the capture. Replays, with eager work between them, match the eager
+    call bit for bit (the planner resets its counters with a kernel, so no
+    memset node is recorded)."""
+    _say("graph capture, side stream")
+    seqs, Hq, Hkv, ps, window, cap, name = RAGGED[4]
+    c = wl.make_gqa(seqs, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=ps,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn, seed=400,
+                    device="cuda", kv_value_scale=2.0, sliding_window=window, soft_cap=cap,
+                    k_scale=0.5, v_scale=0.5, extra_tokens=4096, name="graph-side")
+    kl, pi, cu, ns = _dev_meta(c)
+    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], Hq, Hkv, 128, ps)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    out = torch.zeros_like(c.q)
+
+    def call():
+        rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, sm_scale=c.sm_scale,
+                        sliding_window=c.sliding_window, soft_cap=c.soft_cap,
+                        k_scale=c.k_scale, v_scale=c.v_scale, out=out, workspace=ws)
+    call()  # eager first: creates the library's side stream outside the capture
+    torch.cuda.synchronize()
+    T = int(c.cu_q_lens[c.num_seqs])
+    eager = out[:T].clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for k in range(3):
+        out.zero_()
+        ws.fill_(0xFF)  # eager work between replays; the planner must reset what it needs
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out[:T], eager), f"replay {k} differs from the eager call"
+    _check(c, eager, _run_oracle(c), "fp8")
+
+
 @pytest.mark.parametrize("cap,qscale,ps", [(None, 1.0, 16), (50.0, 1.0, 16), (50.0, 16.0, 16),
                                             (None, 1.0, 8)])
 def test_ragged_fp8_scales(cap, qscale, ps):
