@@ -572,11 +572,18 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
     l_row = wave_sum_xor<32>(l_row);
     if (head >= a.num_heads) continue;
     if (split >= 0 && nsplit > 1) {
+      // The split's output normalised by its own row sum (a convex combination
+      // of value rows, so fp16 keeps it to 2^-11 relative), with (m, l) in
+      // fp32: half the bytes of unnormalised fp32 partials, written here and
+      // read again by the merge.
       const int64_t pidx = (int64_t)seq * kMlaMaxSplits + split;
-      float* pa = a.part_acc + (pidx * a.num_heads + head) * kDl;
+      uint16_t* pa = a.part_acc + (pidx * a.num_heads + head) * kDl;
+      const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
       for (int dt = 0; dt < kDvTiles; ++dt)
-        *reinterpret_cast<floatx4*>(pa + 16 * dt + 4 * g) = acc[h][dt];
+        *reinterpret_cast<u32x2*>(pa + 16 * dt + 4 * g) =
+            u32x2{pack_f16x2(acc[h][dt][0] * inv_l, acc[h][dt][1] * inv_l),
+                  pack_f16x2(acc[h][dt][2] * inv_l, acc[h][dt][3] * inv_l)};
       if (g == 0) {
         float* pm = a.part_ml + (pidx * a.num_heads + head) * 2;
         pm[0] = m_run[h];
@@ -634,21 +641,23 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
     mv[sp] = sp < nsplit ? a.part_ml[((pbase + sp) * a.num_heads + head) * 2] : -INFINITY;
     M = fmaxf(M, mv[sp]);
   }
+  // Split sp contributes weight l_sp * 2^(m_sp - M) times its normalised output.
   float L = 0.f;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (M != -INFINITY) {
 #pragma unroll
     for (int sp = 0; sp < kMlaMaxSplits; ++sp) {
       if (sp >= nsplit) break;
-      const float w = fast_exp2(mv[sp] - M);
-      L += w * a.part_ml[((pbase + sp) * a.num_heads + head) * 2 + 1];
-      const float* pa = a.part_acc + ((pbase + sp) * a.num_heads + head) * kDl + d0;
-      const floatx4 x0 = *reinterpret_cast<const floatx4*>(pa);
-      const floatx4 x1 = *reinterpret_cast<const floatx4*>(pa + 4);
+      const float w = fast_exp2(mv[sp] - M) * a.part_ml[((pbase + sp) * a.num_heads + head) * 2 + 1];
+      L += w;
+      const uint16_t* pa = a.part_acc + ((pbase + sp) * a.num_heads + head) * kDl + d0;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(pa);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o[i] += w * x0[i];
-        o[4 + i] += w * x1[i];
+        float lo, hi;
+        unpack_f16x2(x[i], lo, hi);
+        o[2 * i] += w * lo;
+        o[2 * i + 1] += w * hi;
       }
     }
   }
@@ -894,7 +903,7 @@ size_t mla_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_heads, 
   size_t bytes = align256((64 + (size_t)max_num_seqs + 1) * sizeof(int32_t));
   bytes += align256((size_t)cap * 16);
   bytes += align256((size_t)nparts * num_heads * 2 * sizeof(float));
-  bytes += align256((size_t)nparts * num_heads * (size_t)lkv_dim * sizeof(float));
+  bytes += align256((size_t)nparts * num_heads * (size_t)lkv_dim * sizeof(uint16_t));
   return bytes;
 }
 
@@ -911,7 +920,7 @@ void mla_bind_workspace(MlaArgs& a, void* ws) {
   const int64_t nparts = (int64_t)a.max_num_seqs * kMlaMaxSplits;
   a.part_ml = (float*)p;
   p += align256((size_t)nparts * a.num_heads * 2 * sizeof(float));
-  a.part_acc = (float*)p;
+  a.part_acc = (uint16_t*)p;
 }
 
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {

@@ -63,6 +63,19 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
   return r;
 }
 
+// Two fp32 -> packed pair of IEEE half (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+  const floatx2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, halfx2));
+}
+__device__ __forceinline__ void unpack_f16x2(uint32_t w, float& a, float& b) {
+  typedef _Float16 halfx2 __attribute__((ext_vector_type(2)));
+  const halfx2 h = __builtin_bit_cast(halfx2, w);
+  a = (float)h[0];
+  b = (float)h[1];
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh from its definition, tanh(x) = 1 - 2 / (exp(2x) + 1), evaluated with

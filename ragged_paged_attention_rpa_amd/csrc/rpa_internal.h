@@ -118,7 +118,7 @@ struct MlaArgs {
   // workspace
   int32_t* tiles;     // [capacity][4]
   int32_t* counters;  // [0] count, [1] cursor
-  float* part_acc;    // [capacity][num_heads][lkv_dim]
+  uint16_t* part_acc; // [capacity][num_heads][lkv_dim] fp16: acc / l of the split
   float* part_ml;     // [capacity][num_heads][2]
   int tile_capacity;
 };
