@@ -429,10 +429,15 @@ __device__ __forceinline__ void finish_tile(const GqaArgs& a, const Tile& tile, 
   if (tile.split >= 0 && t.nsplit > 1) {
     const int64_t pidx = ((int64_t)t.seq * a.num_kv_heads + t.kvh) * a.geo.max_splits + tile.split;
     if (row_ok) {
-      float* pa = a.part_acc + (pidx * kPartRows + r) * kD;
+      // The split's output normalised by its own row sum, in fp16 (a convex
+      // combination of value rows: 2^-11 relative), with (m, l) in fp32.
+      uint16_t* pa = a.part_acc + (pidx * kPartRows + r) * kD;
+      const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<floatx4*>(pa + 16 * dt + 4 * g) = acc[dt];
+        *reinterpret_cast<u32x2*>(pa + 16 * dt + 4 * g) =
+            u32x2{pack_f16x2(acc[dt][0] * inv_l, acc[dt][1] * inv_l),
+                  pack_f16x2(acc[dt][2] * inv_l, acc[dt][3] * inv_l)};
       if (g == 0) {
         float* pm = a.part_ml + (pidx * kPartRows + r) * 2;
         pm[0] = m_row;
@@ -1052,15 +1057,17 @@ __global__ void __launch_bounds__(kThreads) gqa_merge_kernel(GqaArgs a) {
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp) {
       if (sp < nsplit) {
-        const float w = fast_exp2(mv[sp] - M);
-        L += w * a.part_ml[((pbase + sp) * kPartRows + r) * 2 + 1];
-        const float* pa = a.part_acc + ((pbase + sp) * kPartRows + r) * kD + d0;
-        const floatx4 x0 = *reinterpret_cast<const floatx4*>(pa);
-        const floatx4 x1 = *reinterpret_cast<const floatx4*>(pa + 4);
+        // Weight l_sp * 2^(m_sp - M) on the split's normalised output.
+        const float w = fast_exp2(mv[sp] - M) * a.part_ml[((pbase + sp) * kPartRows + r) * 2 + 1];
+        L += w;
+        const uint16_t* pa = a.part_acc + ((pbase + sp) * kPartRows + r) * kD + d0;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(pa);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          o[i] += w * x0[i];
-          o[4 + i] += w * x1[i];
+          float lo, hi;
+          unpack_f16x2(x[i], lo, hi);
+          o[2 * i] += w * lo;
+          o[2 * i + 1] += w * hi;
         }
       }
     }
@@ -1205,7 +1212,7 @@ size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads
   bytes += align256((64 + 2 * ((size_t)max_num_seqs + 1)) * sizeof(int32_t));  // counters + offsets
   bytes += align256((size_t)cap * sizeof(Tile));
   bytes += align256((size_t)nparts * kPartRows * 2 * sizeof(float));
-  bytes += align256((size_t)nparts * kPartRows * (size_t)head_dim * sizeof(float));
+  bytes += align256((size_t)nparts * kPartRows * (size_t)head_dim * sizeof(uint16_t));
   return bytes;
 }
 
@@ -1222,7 +1229,7 @@ void gqa_bind_workspace(GqaArgs& a, void* ws) {
   const int64_t nparts = (int64_t)a.max_num_seqs * a.num_kv_heads * a.geo.max_splits;
   a.part_ml = (float*)p;
   p += align256((size_t)nparts * kPartRows * 2 * sizeof(float));
-  a.part_acc = (float*)p;
+  a.part_acc = (uint16_t*)p;
 }
 
 // Library-owned side stream per device (default priority) with its fork and

@@ -76,7 +76,7 @@ struct GqaArgs {
   int32_t* counters;  // [0] tile count, [1] decode-kernel cursor (starts past the prefill
                       // tiles when pre_kernel), [3] prefill tiles, [16 .. 23] prefill
                       // cursors (one per XCD)
-  float* part_acc;    // [max_num_seqs*Hkv*max_splits][16][D]
+  uint16_t* part_acc; // [max_num_seqs*Hkv*max_splits][16][D] fp16: acc / l of the split
   float* part_ml;     // [max_num_seqs*Hkv*max_splits][16][2]
   int tile_capacity;
 };
