@@ -1,21 +1,30 @@
 // GQA ragged paged attention on gfx950 [RPA v2 page: ragged_paged_attention,
 // ref_ragged_paged_attention, flash_attention].
 //
-// Three launches on one stream, no host synchronisation:
+// Launches, with no host synchronisation:
 //   1. gqa_plan_kernel   turns the ragged metadata into a work list of tiles
 //                        (prefill-class tiles first, then decode-class
-//                        splits) and resets the work cursor;
-//   2. gqa_tile_kernel   a persistent grid pops tiles off the list. A tile is
+//                        splits) and resets the work cursors;
+//   2. gqa_prefill_kernel (gqa_prefill.hip) takes the prefill-class tiles
+//                        when it applies (page size >= 8, positive scale);
+//   3. gqa_tile_kernel   a persistent grid pops the remaining tiles. A tile is
 //                        (sequence, kv head, block of query tokens, key range);
 //                        its rows are (query token, q head of the kv head's
 //                        group) pairs, 16 per wave. Keys stream through LDS in
 //                        blocks of 64 straight from the pages named by the page
 //                        table; S^T = K Q^T and O^T += V^T P^T run on
 //                        v_mfma_f32_16x16x32_bf16 with an online softmax in
-//                        the exp2 domain;
-//   3. gqa_merge_kernel  combines the (m, l, acc) partials of split decode
+//                        the exp2 domain. For an fp8 pool whose prefill-class
+//                        tiles went to the prefill kernel, gqa_decode8_kernel
+//                        takes its place (128-key raw blocks widened in
+//                        registers);
+//   4. gqa_merge_kernel  combines the (m, l, output) partials of split decode
 //                        sequences with the rescaling algebra of the page's
 //                        flash_attention (alpha = e^{m_i - m*}).
+// Launches 3 and 4 go to a library-owned side stream, forked after 1 and
+// joined before the call returns, when the batch has room for a prefill share
+// (they then run beside launch 2); otherwise everything is on the caller's
+// stream.
 // The per-row arithmetic follows the page: scale, optional soft cap, mask
 // (causal offset kv_len - q_len, optional sliding window), softmax, P V.
 #include <mutex>
