@@ -134,7 +134,8 @@ __device__ int block_excl_scan(int v, int* sh, int* total) {
   return before + x - v;
 }
 
-// seq_off layout in the workspace: [0, ns] prefill offsets, then [0, ns] decode offsets.
+// seq_off layout in the workspace: [0, ns] prefill offsets, then [0, ns] offsets of the
+// decode splits but the last, then [0, ns] offsets of the last splits.
 __device__ __forceinline__ int* seq_offsets(const GqaArgs& a) { return a.counters + 64; }
 
 __device__ __forceinline__ int upper_bound_seq(const int* off, int n, int t) {
@@ -156,35 +157,45 @@ constexpr int kPlanWgs = 32;
 
 __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
   __shared__ int sh[kThreads];
-  __shared__ int off_lds[2 * (kPlanLdsSeqs + 1)];
+  __shared__ int off_lds[3 * (kPlanLdsSeqs + 1)];
   const int tid = threadIdx.x;
   const int ns = num_seqs_clamped(a);
   const bool in_lds = ns <= kPlanLdsSeqs;
+  const int H = a.num_kv_heads;
+  // Tile order: prefill-class tiles, then every decode split but the last of
+  // its sequence (full length), then the last splits (the remainders, mostly
+  // shorter), so a persistent grid ends on short tiles.
   int* pre_off = in_lds ? off_lds : seq_offsets(a);
-  int* dec_off = pre_off + (in_lds ? kPlanLdsSeqs + 1 : a.max_num_seqs + 1);
-  int run_pre = 0, run_dec = 0;
+  const int stride = in_lds ? kPlanLdsSeqs + 1 : a.max_num_seqs + 1;
+  int* full_off = pre_off + stride;
+  int* last_off = full_off + stride;
+  int run_pre = 0, run_full = 0, run_last = 0;
   for (int c0 = 0; c0 < ns; c0 += kThreads) {
     const int i = c0 + tid;
     int np = 0, nd = 0;
     if (i < ns) seq_tile_counts(a, i, &np, &nd);
-    int tp, td;
+    const int nl = nd > 0 ? H : 0;
+    int tp, tf, tl;
     const int op = block_excl_scan(np, sh, &tp);
-    const int od = block_excl_scan(nd, sh, &td);
+    const int of = block_excl_scan(nd - nl, sh, &tf);
+    const int ol = block_excl_scan(nl, sh, &tl);
     if (i < ns) {
       pre_off[i] = run_pre + op;
-      dec_off[i] = run_dec + od;
+      full_off[i] = run_full + of;
+      last_off[i] = run_last + ol;
     }
     run_pre += tp;
-    run_dec += td;
+    run_full += tf;
+    run_last += tl;
   }
   if (tid == 0) {
     pre_off[ns] = run_pre;
-    dec_off[ns] = run_dec;
+    full_off[ns] = run_full;
+    last_off[ns] = run_last;
   }
   if (!in_lds) __threadfence();
   __syncthreads();
-  const int total = min(run_pre + run_dec, a.tile_capacity);
-  const int H = a.num_kv_heads;
+  const int total = min(run_pre + run_full + run_last, a.tile_capacity);
   // With the offsets in LDS every workgroup has computed them and writes its
   // share of the tiles; otherwise workgroup 0 writes them all. Each thread
   // writes one contiguous range: one search for its first tile, then the
@@ -217,18 +228,32 @@ __global__ void __launch_bounds__(kThreads) gqa_plan_kernel(GqaArgs a) {
         // workgroup picks up are the short ones.
         tl.qtok0 = (nqb - 1 - local % nqb) * a.geo.bq;
         tl.split = -1;
-      } else {
+      } else if (t < run_pre + run_full) {
         const int u = t - run_pre;
-        if (seq < 0 || t == run_pre || u >= seq_end) {  // first decode tile or next sequence
-          seq = upper_bound_seq(dec_off, ns, u);
-          seq_begin = dec_off[seq];
-          seq_end = dec_off[seq + 1];
+        if (seq < 0 || t == run_pre || u >= seq_end) {  // first full split or next sequence
+          seq = upper_bound_seq(full_off, ns, u);
+          seq_begin = full_off[seq];
+          seq_end = full_off[seq + 1];
         }
         const int local = u - seq_begin;
         tl.seq = seq;
         tl.kvh = local % H;
         tl.qtok0 = 0;
         tl.split = local / H;
+      } else {
+        const int u = t - run_pre - run_full;
+        if (seq < 0 || t == run_pre + run_full || u >= seq_end) {  // first last split or next sequence
+          seq = upper_bound_seq(last_off, ns, u);
+          seq_begin = last_off[seq];
+          seq_end = last_off[seq + 1];
+          int lo, hi, ch;
+          decode_range(a, seq_info(a, seq), &lo, &hi);
+          split_plan(hi - lo, a.geo.split_keys, a.geo.max_splits, &nqb, &ch);
+        }
+        tl.seq = seq;
+        tl.kvh = u - seq_begin;
+        tl.qtok0 = 0;
+        tl.split = nqb - 1;  // nqb holds the sequence's split count here
       }
       a.tiles[t] = tl;
     }
@@ -1193,12 +1218,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window) {
+GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int kv_dtype) {
   GqaGeometry g;
   g.group = num_q_heads / num_kv_heads;
   g.qdec = g.group <= 16 ? 16 / g.group : 0;
   g.bq = g.group <= 64 ? 64 / g.group : 1;
-  g.split_keys = 1024;
+  // Decode splits of about 512 KB of K and V per kv head (1024 bf16 keys,
+  // 2048 fp8 keys); measured against 512/1024/2048 keys on the decode batches.
+  g.split_keys = kv_dtype == DT_FP8 ? 2048 : 1024;
   g.max_splits = kMaxSplits;
   g.window = window;
   return g;
@@ -1211,14 +1238,14 @@ bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
 
 size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads,
                            int num_kv_heads, int head_dim, int window, int* tile_capacity) {
-  const GqaGeometry g = gqa_geometry(num_q_heads, num_kv_heads, window);
+  const GqaGeometry g = gqa_geometry(num_q_heads, num_kv_heads, window, DT_BF16);  // size: split count only
   const int64_t cap = (int64_t)num_kv_heads *
                       ((int64_t)max_num_tokens / g.bq + max_num_seqs +
                        (int64_t)max_num_seqs * g.max_splits);
   if (tile_capacity) *tile_capacity = (int)cap;
   const int64_t nparts = (int64_t)max_num_seqs * num_kv_heads * g.max_splits;
   size_t bytes = 0;
-  bytes += align256((64 + 2 * ((size_t)max_num_seqs + 1)) * sizeof(int32_t));  // counters + offsets
+  bytes += align256((64 + 3 * ((size_t)max_num_seqs + 1)) * sizeof(int32_t));  // counters + offsets
   bytes += align256((size_t)cap * sizeof(Tile));
   bytes += align256((size_t)nparts * kPartRows * 2 * sizeof(float));
   bytes += align256((size_t)nparts * kPartRows * (size_t)head_dim * sizeof(uint16_t));
@@ -1232,7 +1259,7 @@ void gqa_bind_workspace(GqaArgs& a, void* ws) {
   a.tile_capacity = cap;
   char* p = (char*)ws;
   a.counters = (int32_t*)p;
-  p += align256((64 + 2 * ((size_t)a.max_num_seqs + 1)) * sizeof(int32_t));
+  p += align256((64 + 3 * ((size_t)a.max_num_seqs + 1)) * sizeof(int32_t));
   a.tiles = (Tile*)p;
   p += align256((size_t)cap * sizeof(Tile));
   const int64_t nparts = (int64_t)a.max_num_seqs * a.num_kv_heads * a.geo.max_splits;

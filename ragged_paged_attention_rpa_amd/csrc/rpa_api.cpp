@@ -240,7 +240,7 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   a.score_scale = opts->sm_scale * opts->k_scale;
   a.soft_cap = opts->soft_cap;
   a.v_scale = opts->v_scale;
-  a.geo = rpa::gqa_geometry(num_q_heads, num_kv_heads, opts->sliding_window);
+  a.geo = rpa::gqa_geometry(num_q_heads, num_kv_heads, opts->sliding_window, a.kv_dtype);
 
   const bool mfma = rpa::gqa_mfma_supported(a.q_dtype, a.kv_dtype, head_dim,
                                             num_q_heads / num_kv_heads) &&

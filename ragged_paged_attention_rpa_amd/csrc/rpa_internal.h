@@ -84,7 +84,7 @@ struct GqaArgs {
 constexpr int kXcdCursor0 = 16;  // first per-XCD prefill cursor in GqaArgs::counters
 constexpr int kXcds = 8;         // XCDs of an MI355X (one prefill cursor each)
 
-GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window);
+GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int kv_dtype);
 size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads,
                            int num_kv_heads, int head_dim, int window, int* tile_capacity);
 // Carves the workspace into tiles/counters/partials of GqaArgs.
