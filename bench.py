@@ -585,7 +585,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the path has no multi-GPU part; see the sharding notes in DESIGN.md)",
+              "(the path has no multi-GPU part: tiles are independent, so each GPU would run its own sequences or kv heads)",
               file=sys.stderr)
         sys.exit(2)
     import torch
