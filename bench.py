@@ -584,7 +584,7 @@ def main():
                          "(calibration run for the PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path has no multi-GPU part: tiles are independent, so each GPU would run its own sequences or kv heads)",
               file=sys.stderr)
         sys.exit(2)

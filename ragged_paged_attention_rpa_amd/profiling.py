@@ -36,7 +36,7 @@ def trace_summary(stats_csv: str, title: str, command: str) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     out = [f"# rocprofv3 kernel summary — {title}",
-           "# command (from the repo root on the GPU box):",
+           "# command (run from the repo root):",
            f"#   {command}",
            f"{'kernel':72s} {'calls':>6s} {'mean_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_us':>11s}"]
     for r in rows:
