@@ -73,3 +73,38 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_mla_work_matches_brute_force():
+    seqs = [(1, 40), (1, 1), (3, 70)]
+    c = wl.make_mla(seqs, num_heads=16, page_size=16, seed=4)
+    got = bench.mla_work(c, 16)
+    pairs = rows = 0
+    for i, (ql, L) in enumerate(seqs):
+        seen = set()
+        for r in range(ql):
+            p = L - ql + r
+            for t in range(L):
+                if t <= p:
+                    pairs += 1
+                    seen.add(t)
+        rows += len(seen)
+    assert got["kv_bytes"] == rows * (512 + 64) * 2
+    assert got["flops"] == pairs * 16 * (2 * 576 + 2 * 512)
+
+
+def test_sparse_work_matches_brute_force():
+    c = wl.make_sparse(T=640, S=6, H=16, K=4, page_size=64, read_block=64, seed=5)
+    got = bench.sparse_work(c)
+    keys = 0
+    for s in range(c.q.shape[0]):
+        for u in c.indices[s]:
+            if u < 0:
+                continue
+            for r in range(c.read_block):
+                kp = int(u) * c.read_block + r
+                if kp <= int(c.positions[s]) and kp < c.seq_len:
+                    keys += 1
+    assert keys > 0
+    assert got["gathered_bytes"] == keys * 576 * 2
+    assert got["flops"] == keys * 16 * 2 * (576 + 512)
