@@ -1290,6 +1290,10 @@ std::mutex g_side_mu;
 SideStream* side_fork(hipStream_t stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  // A caller's stream of another device keeps everything on that stream.
+  hipDevice_t sdev = dev;
+  if (stream != nullptr && (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev))
+    return nullptr;
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream& ss = g_side[dev];
   if (!ss.s) {
