@@ -46,9 +46,14 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB)
+        # RPA_ORACLE_LIB names another build of this oracle (the mutation test
+        # loads deliberately broken copies through it); default: the in-tree one.
+        path = os.environ.get("RPA_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        lib = ctypes.CDLL(path)
         c_void_p, c_int, c_double = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
         lib.oracle_rpa.restype = c_int
         lib.oracle_rpa.argtypes = [c_void_p, c_int, c_int, c_int, c_int,

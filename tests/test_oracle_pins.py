@@ -489,3 +489,161 @@ def test_sparse_seq_len_bound_cuts_keys():
         Q = torch.from_numpy(q[s].astype(np.float64))[:, None, :]
         want = _sdpa(Q, K, V, torch.ones((1, 22), dtype=torch.bool), c.sm_scale)[:, 0, :].numpy()
         np.testing.assert_allclose(got[s], want, atol=1e-10)
+
+
+# ---------------------------------------------- MLA window and soft cap --
+
+GOLDEN_MLA = os.path.join(os.path.dirname(__file__), "golden", "hand_derived_mla.json")
+
+
+def _mla_expr(tok):
+    if isinstance(tok, (int, float)):
+        return float(tok)
+    if tok == "(2ln2+3ln3)/6":
+        return (2 * math.log(2.0) + 3 * math.log(3.0)) / 6
+    return _coord(tok)
+
+
+def _mla_golden_cases():
+    with open(GOLDEN_MLA) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _mla_golden_cases(), ids=lambda c: c["name"])
+def test_mla_hand_derived(case):
+    """One sequence, latent width 2 (the value), rope width 1, page size 2,
+    pages in reverse physical order, unused rows NaN [MLA v1 page:
+    ref_mla_ragged_paged_attention]."""
+    kv_len, q_len = case["kv_len"], case["q_len"]
+    ps, Dl, Dr = 2, 2, 1
+    n_pages = -(-kv_len // ps)
+    P = n_pages + 1
+    ckv = np.full((P, ps, Dl), np.nan, dtype=np.float32)
+    ckp = np.full((P, ps, Dr), np.nan, dtype=np.float32)
+    table = np.array([[P - 1 - lp for lp in range(n_pages)]], dtype=np.int32)
+    for t in range(kv_len):
+        page, row = table[0, t // ps], t % ps
+        score = _coord(case["key_score"][t])
+        vals = case["values"][t]
+        if case["score_from"] == "rope":
+            ckv[page, row] = vals
+            ckp[page, row, 0] = score
+        else:
+            ckv[page, row] = [score, vals[1]]
+            ckp[page, row, 0] = 0.0
+    ql = np.zeros((q_len, 1, Dl), dtype=np.float32)
+    qp = np.zeros((q_len, 1, Dr), dtype=np.float32)
+    if case["score_from"] == "rope":
+        qp[:, 0, 0] = 1.0
+    else:
+        ql[:, 0, 0] = 1.0
+    cap = case["soft_cap"]
+    cap = 3 * math.log(3.0) if cap == "3ln3" else float(cap)
+    out = oracle.mla(ql, qp, oracle.F32, ckv, ckp, [kv_len], table, [0, q_len], 1, sm_scale=1.0,
+                     sliding_window=case["window"] or None, soft_cap=cap or None)
+    want = np.array([[_mla_expr(x) for x in row] for row in case["expected"]])
+    np.testing.assert_allclose(out[:, 0, :], want, rtol=0, atol=2e-6)
+
+
+def _mla_dense(c, ql, qp, ckv, ckp, window, scale_q=1.0):
+    """fp64 SDPA over each sequence's unpaged latent with an explicit
+    causal + window mask."""
+    H, Dl, Dr = ql.shape[1], ql.shape[2], qp.shape[2]
+    ps = ckv.shape[1]
+    want = np.zeros(ql.shape, np.float64)
+    for i in range(c.num_seqs):
+        L, ql_i = int(c.kv_lens[i]), int(c.cu_q_lens[i + 1] - c.cu_q_lens[i])
+        rows = [c.page_indices[i, t // ps] * ps + t % ps for t in range(L)]
+        kvc = ckv.reshape(-1, ckv.shape[2])[rows, :Dl].astype(np.float64)
+        kpe = ckp.reshape(-1, ckp.shape[2])[rows, :Dr].astype(np.float64)
+        K = torch.from_numpy(np.concatenate([kvc, kpe], 1))[None].expand(H, -1, -1)
+        V = torch.from_numpy(kvc)[None].expand(H, -1, -1)
+        sl = slice(c.cu_q_lens[i], c.cu_q_lens[i + 1])
+        Q = torch.from_numpy(np.concatenate([ql[sl], qp[sl]], 2).astype(np.float64) * scale_q)
+        qpos = L - ql_i + np.arange(ql_i)
+        kpos = np.arange(L)
+        mask = kpos[None, :] <= qpos[:, None]
+        if window:
+            mask &= kpos[None, :] > qpos[:, None] - window
+        want[sl] = _sdpa(Q.transpose(0, 1), K, V, torch.from_numpy(mask),
+                         c.sm_scale).transpose(0, 1).numpy()
+    return want
+
+
+@pytest.mark.parametrize("window", [1, 5, 33])
+def test_mla_window_matches_dense_sdpa(window):
+    c = wl.make_mla([(1, 70), (3, 3), (5, 129), (2, 40)], num_heads=4, lkv_dim=32, r_dim=8,
+                    page_size=16, dtype=torch.float32, seed=30 + window)
+    ql, d = storage(c.ql_nope)
+    qp, _ = storage(c.q_pe)
+    ckv, _ = storage(c.cache_kv_c)
+    ckp, _ = storage(c.cache_k_pe)
+    got = oracle.mla(ql, qp, d, ckv, ckp, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
+                     sm_scale=c.sm_scale, sliding_window=window)
+    np.testing.assert_allclose(got, _mla_dense(c, ql, qp, ckv, ckp, window), atol=1e-10)
+
+
+def test_mla_huge_cap_is_no_cap_and_engaged_cap_moves_output():
+    c = wl.make_mla([(1, 70), (4, 90)], num_heads=4, lkv_dim=32, r_dim=8, page_size=16,
+                    dtype=torch.float32, seed=40)
+    ql, d = storage(c.ql_nope)
+    qp, _ = storage(c.q_pe)
+    ckv, _ = storage(c.cache_kv_c)
+    ckp, _ = storage(c.cache_k_pe)
+    args = (d, ckv, ckp, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs)
+    base = oracle.mla(ql, qp, *args, sm_scale=c.sm_scale)
+    np.testing.assert_allclose(oracle.mla(ql, qp, *args, sm_scale=c.sm_scale, soft_cap=1e9), base,
+                               atol=1e-12)
+    # Queries x16 push |score| well past a cap of 2: the capped output differs.
+    ql16, qp16 = ql * 16, qp * 16
+    capped = oracle.mla(ql16, qp16, *args, sm_scale=c.sm_scale, soft_cap=2.0)
+    uncapped = oracle.mla(ql16, qp16, *args, sm_scale=c.sm_scale)
+    assert np.abs(capped - uncapped).max() > 0.1
+
+
+# ------------------------------------------------------ row-subset paths --
+
+def test_rpa_token_subset_equals_full_rows():
+    c = wl.make_gqa([(3, 20), (1, 7), (6, 40), (1, 1)], num_q_heads=8, num_kv_heads=2,
+                    head_dim=16, page_size=4, q_dtype=torch.float32, kv_dtype=torch.float32,
+                    seed=50)
+    q, qd = storage(c.q)
+    kv, kd = storage(c.kv_pages)
+    kw = dict(sm_scale=0.3, sliding_window=5, soft_cap=3.0)
+    full = oracle.rpa(q, qd, kv, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs, **kw)
+    toks = np.array([10, 0, 4, 9, 5], np.int32)
+    sub = oracle.rpa(q, qd, kv, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
+                     tokens=toks, **kw)
+    assert np.array_equal(sub[toks], full[toks])
+    rest = np.setdiff1d(np.arange(q.shape[0]), toks)
+    assert np.isnan(sub[rest]).all()
+
+
+def test_mla_token_subset_equals_full_rows():
+    c = wl.make_mla([(1, 70), (3, 3), (5, 129)], num_heads=4, lkv_dim=32, r_dim=8,
+                    page_size=16, dtype=torch.float32, seed=51)
+    ql, d = storage(c.ql_nope)
+    qp, _ = storage(c.q_pe)
+    ckv, _ = storage(c.cache_kv_c)
+    ckp, _ = storage(c.cache_k_pe)
+    args = (ql, qp, d, ckv, ckp, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs)
+    kw = dict(sm_scale=c.sm_scale, sliding_window=7, soft_cap=4.0)
+    full = oracle.mla(*args, **kw)
+    toks = np.array([8, 1, 0, 3], np.int32)
+    sub = oracle.mla(*args, tokens=toks, **kw)
+    assert np.array_equal(sub[toks], full[toks])
+    rest = np.setdiff1d(np.arange(ql.shape[0]), toks)
+    assert np.isnan(sub[rest]).all()
+
+
+def test_sparse_query_subset_equals_full_rows():
+    c = _sparse_small(seed=52, pad_frac=0.3)
+    q, d = storage(c.q)
+    kv, _ = storage(c.kv_cache)
+    kw = dict(seq_len=c.seq_len, read_block=c.read_block, sm_scale=c.sm_scale, dv=32)
+    full = oracle.sparse_mla(q, d, kv, c.page_table, c.indices, c.positions, **kw)
+    qs = np.array([5, 2, 0], np.int32)
+    sub = oracle.sparse_mla(q, d, kv, c.page_table, c.indices, c.positions, queries=qs, **kw)
+    assert np.array_equal(sub[qs], full[qs])
+    rest = np.setdiff1d(np.arange(q.shape[0]), qs)
+    assert np.isnan(sub[rest]).all()
