@@ -31,10 +31,15 @@
  *    rpa_opts.debug_validate is set, no call synchronises with the host.
  *  - rpa_forward on a batch whose token capacity leaves room for a prefill
  *    share runs its decode-class launch on a library-owned stream of the
- *    current device (created on first use, default priority, kept until the
- *    process ends), forked from `stream` with an event and joined back into it
- *    before the call returns: to the caller all of the call's work is ordered
- *    on `stream`, and the call can be captured into a graph like any other.
+ *    current device (created on the first such call made outside a stream
+ *    capture, default priority, kept until the process ends), forked from
+ *    `stream` with an event and joined back into it before the call returns:
+ *    to the caller all of the call's work is ordered on `stream`, and the call
+ *    can be captured into a graph like any other (a call captured before the
+ *    side stream exists stays on `stream`). The side stream is shared by all
+ *    callers and threads of a device: calls from several host threads are
+ *    serialised on it, and capturing on one thread while another thread
+ *    issues eager calls on the same device is not supported.
  *  - On any error the call returns a non-zero rpa_status, launches nothing,
  *    and rpa_last_error() describes the first problem found (thread-local).
  *  - Outputs are written in the query dtype for rpa_forward/mla_rpa_forward
@@ -128,6 +133,19 @@ void rpa_opts_init(rpa_opts* opts);
 
 /* Thread-local description of the last error (empty string after success). */
 const char* rpa_last_error(void);
+
+/*
+ * Thread-local name of the kernel path the last successful rpa_forward call on
+ * this thread took (empty before the first call):
+ *   "gqa_mfma"          work-list planner, MFMA tile kernel(s), split merge;
+ *   "gqa_mfma_prefill"  as gqa_mfma, with prefill-class tiles on the
+ *                       eight-wave prefill kernel;
+ *   "gqa_generic"       one wave per (query token, q head) on plain vector
+ *                       ALU, no MFMA: taken for fp32 queries, head_dim != 128,
+ *                       page sizes that are not powers of two and pointers not
+ *                       16-byte aligned. Correct, but far slower.
+ */
+const char* rpa_last_path(void);
 
 /*
  * Profiling hook for benchmarks. `start` and `stop` are hipEvent_t handles

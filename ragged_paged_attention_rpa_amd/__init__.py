@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librpa.so")
 
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
-EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_set_profile_events",
+EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_last_path", "rpa_set_profile_events",
                     "rpa_set_profile_events_split",
                     "rpa_workspace_size", "rpa_forward",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
@@ -79,6 +79,8 @@ def load_library():
     lib.rpa_opts_init.restype = None
     lib.rpa_last_error.argtypes = []
     lib.rpa_last_error.restype = ctypes.c_char_p
+    lib.rpa_last_path.argtypes = []
+    lib.rpa_last_path.restype = ctypes.c_char_p
     lib.rpa_set_profile_events.argtypes = [P, P]
     lib.rpa_set_profile_events.restype = None
     lib.rpa_set_profile_events_split.argtypes = [P, P, P, P]
@@ -174,6 +176,12 @@ def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_valid
     o.v_scale = float(1.0 if v_scale is None else v_scale)
     o.debug_validate = 1 if debug_validate else 0
     return o
+
+
+def last_path() -> str:
+    """Kernel path of this thread's last successful rpa_forward call
+    ("gqa_mfma", "gqa_mfma_prefill" or "gqa_generic")."""
+    return load_library().rpa_last_path().decode()
 
 
 def set_profile_events(start, stop):

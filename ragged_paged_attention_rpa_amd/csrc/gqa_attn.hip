@@ -463,15 +463,16 @@ __device__ __forceinline__ void finish_tile(const GqaArgs& a, const Tile& tile, 
   if (tile.split >= 0 && t.nsplit > 1) {
     const int64_t pidx = ((int64_t)t.seq * a.num_kv_heads + t.kvh) * a.geo.max_splits + tile.split;
     if (row_ok) {
-      // The split's output normalised by its own row sum, in fp16 (a convex
-      // combination of value rows: 2^-11 relative), with (m, l) in fp32.
+      // The split's output normalised by its own row sum (pack_part: fp16
+      // for fp8 pools, bf16 for bf16 pools), with (m, l) in fp32.
       uint16_t* pa = a.part_acc + (pidx * kPartRows + r) * kD;
       const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
+      const bool f16 = a.kv_dtype == DT_FP8;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         *reinterpret_cast<u32x2*>(pa + 16 * dt + 4 * g) =
-            u32x2{pack_f16x2(acc[dt][0] * inv_l, acc[dt][1] * inv_l),
-                  pack_f16x2(acc[dt][2] * inv_l, acc[dt][3] * inv_l)};
+            u32x2{pack_part(acc[dt][0] * inv_l, acc[dt][1] * inv_l, f16),
+                  pack_part(acc[dt][2] * inv_l, acc[dt][3] * inv_l, f16)};
       if (g == 0) {
         float* pm = a.part_ml + (pidx * kPartRows + r) * 2;
         pm[0] = m_row;
@@ -1099,7 +1100,7 @@ __global__ void __launch_bounds__(kThreads) gqa_merge_kernel(GqaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float lo, hi;
-          unpack_f16x2(x[i], lo, hi);
+          unpack_part(x[i], lo, hi, a.kv_dtype == DT_FP8);
           o[2 * i] += w * lo;
           o[2 * i + 1] += w * hi;
         }
@@ -1297,6 +1298,13 @@ SideStream* side_fork(hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideStream& ss = g_side[dev];
   if (!ss.s) {
+    // Never create the stream while the caller's stream is being captured
+    // (creating a stream mid-capture is not a capturable operation): such a
+    // call stays on one stream; the side stream appears on the first call
+    // made outside a capture.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (stream != nullptr && hipStreamIsCapturing(stream, &cs) != hipSuccess) return nullptr;
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
     if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
       ss.s = nullptr;
       return nullptr;
@@ -1342,7 +1350,12 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
     // Prefill-class tiles on the eight-wave kernel (one workgroup per CU).
     prof_kernel_begin(stream, 0);
     const hipError_t e = launch_gqa_prefill(a, ps_log2, num_cus(), stream);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      // Join the fork even on failure: a capture with an unjoined fork
+      // cannot end.
+      if (side) (void)side_join(side, stream);
+      return e;
+    }
     prof_kernel_end(stream, 0);
   }
   prof_kernel_begin(dstream, 1);

@@ -572,18 +572,18 @@ __device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int p
     l_row = wave_sum_xor<32>(l_row);
     if (head >= a.num_heads) continue;
     if (split >= 0 && nsplit > 1) {
-      // The split's output normalised by its own row sum (a convex combination
-      // of value rows, so fp16 keeps it to 2^-11 relative), with (m, l) in
-      // fp32: half the bytes of unnormalised fp32 partials, written here and
-      // read again by the merge.
+      // The split's output normalised by its own row sum, in bf16 (a convex
+      // combination of bf16 value rows, whose range half precision might not
+      // hold), with (m, l) in fp32: half the bytes of unnormalised fp32
+      // partials, written here and read again by the merge.
       const int64_t pidx = (int64_t)seq * kMlaMaxSplits + split;
       uint16_t* pa = a.part_acc + (pidx * a.num_heads + head) * kDl;
       const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
       for (int dt = 0; dt < kDvTiles; ++dt)
         *reinterpret_cast<u32x2*>(pa + 16 * dt + 4 * g) =
-            u32x2{pack_f16x2(acc[h][dt][0] * inv_l, acc[h][dt][1] * inv_l),
-                  pack_f16x2(acc[h][dt][2] * inv_l, acc[h][dt][3] * inv_l)};
+            u32x2{pack_bf16x2(acc[h][dt][0] * inv_l, acc[h][dt][1] * inv_l),
+                  pack_bf16x2(acc[h][dt][2] * inv_l, acc[h][dt][3] * inv_l)};
       if (g == 0) {
         float* pm = a.part_ml + (pidx * a.num_heads + head) * 2;
         pm[0] = m_run[h];
@@ -655,7 +655,7 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float lo, hi;
-        unpack_f16x2(x[i], lo, hi);
+        unpack_part(x[i], lo, hi, false);
         o[2 * i] += w * lo;
         o[2 * i + 1] += w * hi;
       }

@@ -21,6 +21,7 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local const char* g_last_path = "";
 thread_local hipEvent_t g_prof_start = nullptr;
 thread_local hipEvent_t g_prof_stop = nullptr;
 thread_local hipEvent_t g_prof_k[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
@@ -188,6 +189,8 @@ void rpa_opts_init(rpa_opts* o) {
 
 const char* rpa_last_error(void) { return g_last_error.c_str(); }
 
+const char* rpa_last_path(void) { return g_last_path; }
+
 size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t page_size) {
   (void)page_size;
@@ -269,9 +272,13 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
       a.pre_kernel = 1;
       a.geo.bq = rpa::gqa_prefill_rows() / a.geo.group;
     }
-    return hip_status(rpa::launch_gqa(a, stream), "rpa_forward launch");
+    const rpa_status st = hip_status(rpa::launch_gqa(a, stream), "rpa_forward launch");
+    if (st == RPA_OK) g_last_path = a.pre_kernel ? "gqa_mfma_prefill" : "gqa_mfma";
+    return st;
   }
-  return hip_status(rpa::launch_gqa_generic(a, stream), "rpa_forward launch");
+  const rpa_status st = hip_status(rpa::launch_gqa_generic(a, stream), "rpa_forward launch");
+  if (st == RPA_OK) g_last_path = "gqa_generic";
+  return st;
 }
 
 rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const void* new_b,

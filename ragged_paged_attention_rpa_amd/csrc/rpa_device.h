@@ -76,6 +76,23 @@ __device__ __forceinline__ void unpack_f16x2(uint32_t w, float& a, float& b) {
   b = (float)h[1];
 }
 
+// Split-KV partials hold a split's output normalised by its own row sum: a
+// convex combination of value rows, so |x| <= max |V|. Pools whose values fit
+// IEEE half (fp8 E4M3FN: |V| <= 448) store them as fp16 (2^-11 relative);
+// bf16 pools, whose values may exceed half's range, store bf16 (2^-9, the same
+// rounding the final bf16 output takes anyway).
+__device__ __forceinline__ uint32_t pack_part(float a, float b, bool f16) {
+  return f16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
+}
+__device__ __forceinline__ void unpack_part(uint32_t w, float& a, float& b, bool f16) {
+  if (f16) {
+    unpack_f16x2(w, a, b);
+  } else {
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xffff0000u);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // tanh from its definition, tanh(x) = 1 - 2 / (exp(2x) + 1), evaluated with

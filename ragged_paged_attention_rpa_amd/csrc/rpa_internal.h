@@ -76,7 +76,8 @@ struct GqaArgs {
   int32_t* counters;  // [0] tile count, [1] decode-kernel cursor (starts past the prefill
                       // tiles when pre_kernel), [3] prefill tiles, [16 .. 23] prefill
                       // cursors (one per XCD)
-  uint16_t* part_acc; // [max_num_seqs*Hkv*max_splits][16][D] fp16: acc / l of the split
+  uint16_t* part_acc; // [max_num_seqs*Hkv*max_splits][16][D] acc / l of the split (fp16
+                      // for fp8 pools, bf16 for bf16 pools)
   float* part_ml;     // [max_num_seqs*Hkv*max_splits][16][2]
   int tile_capacity;
 };
@@ -118,7 +119,7 @@ struct MlaArgs {
   // workspace
   int32_t* tiles;     // [capacity][4]
   int32_t* counters;  // [0] count, [1] cursor
-  uint16_t* part_acc; // [capacity][num_heads][lkv_dim] fp16: acc / l of the split
+  uint16_t* part_acc; // [capacity][num_heads][lkv_dim] bf16: acc / l of the split
   float* part_ml;     // [capacity][num_heads][2]
   int tile_capacity;
 };

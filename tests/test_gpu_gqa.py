@@ -77,6 +77,13 @@ RAGGED = [
     # large groups: 16 and 32 rows per query token (16 and 8 tokens per tile)
     ([(33, 1000), (1, 500), (100, 100)], 32, 2, 16, None, 50.0, "g16"),
     ([(20, 700), (57, 640), (1, 64)], 32, 1, 32, 200, None, "g32-window"),
+    # groups that are not powers of two: 255 of the prefill kernel's 256 rows
+    # (G=3) or 252 (G=7) are live, decode tiles hold 15 or 14 rows
+    ([(1, 700), (3, 500), (300, 1200), (8, 8)], 16, 8, 16, 400, 30.0, "g2-window-cap"),
+    ([(5, 900), (1, 300), (170, 800), (4, 4), (2, 3000)], 24, 8, 16, 300, 25.0, "g3-window-cap"),
+    ([(2, 1000), (1, 64), (200, 700), (7, 7), (1, 5000)], 28, 4, 32, None, 40.0, "g7-cap"),
+    # page size 128 (256 KB of K and V per page for 8 kv heads)
+    ([(1, 3000), (200, 1500), (1, 129), (9, 700)], 32, 8, 128, None, None, "page128"),
 ]
 
 
@@ -323,14 +330,32 @@ def test_decode_gqa_full_size_sampled():
     _check(c, got, want, "bf16", tokens=tokens)
 
 
-def test_mixed_gqa_full_size_sampled():
-    _say("mixed_gqa full size (120 decodes + 8 prefill chunks), sampled rows")
-    c = wl.mixed_gqa(device="cuda")
+def _mixed_sample(c, block=64):
+    """Every decode token, plus the first and last token of every 64-token
+    query block of every prefill chunk (the prefill kernel's query-block size
+    at 32/8 heads), so each of its tiles has rows compared."""
+    toks = []
+    for i in range(c.num_seqs):
+        a, b = int(c.cu_q_lens[i]), int(c.cu_q_lens[i + 1])
+        if b - a == 1:
+            toks.append(a)
+            continue
+        for t0 in range(a, b, block):
+            toks += [t0, min(t0 + block, b) - 1]
+    return np.unique(np.array(toks, np.int32))
+
+
+@pytest.mark.parametrize("variant", ["ordered", "shuffled", "q_x16"])
+def test_mixed_gqa_full_size_sampled(variant):
+    """The mixed batch at full size (120 decodes + 8 prefill chunks, fp8 pool,
+    window 4096, cap 50), in the generator's order, in a shuffled sequence
+    order, and with queries x16 so the soft cap is engaged."""
+    _say(f"mixed_gqa full size {variant}, every decode + both ends of every prefill block")
+    c = wl.mixed_gqa(device="cuda", shuffle_order=variant == "shuffled",
+                     q_value_scale=16.0 if variant == "q_x16" else 1.0)
     got = _run_gpu(c)
-    rng = np.random.default_rng(0)
-    T = int(c.cu_q_lens[c.num_seqs])
-    tokens = np.unique(np.concatenate([np.arange(0, 120, 7), rng.integers(120, T, 24),
-                                       c.cu_q_lens[121:129] - 1]))
+    tokens = _mixed_sample(c)
+    assert len(tokens) > 400
     want = _run_oracle(c, tokens=tokens)
     _check(c, got, want, "fp8", tokens=tokens)
 
@@ -412,3 +437,86 @@ def test_rows_whose_window_starts_in_a_later_block():
                         kv_dtype=torch.bfloat16, seed=102, device="cuda", sliding_window=100,
                         name=f"late-window-{Hq}-{Hkv}")
         _check(c, _run_gpu(c), _run_oracle(c), "bf16")
+
+
+def test_bf16_values_beyond_half_range_stay_finite():
+    """Split decodes of a bf16 pool whose values exceed IEEE half's range
+    (|V| up to ~4e5): the split partials must not saturate, so the output is
+    finite and matches the oracle to the bf16 tolerance scaled by |V|."""
+    _say("bf16 values beyond half range")
+    scale = 1.0e5
+    c = wl.make_gqa([(1, 9000), (1, 3000), (2, 5000)], num_q_heads=32, num_kv_heads=8,
+                    head_dim=128, page_size=16, q_dtype=torch.bfloat16,
+                    kv_dtype=torch.bfloat16, seed=90, device="cuda", name="big-v")
+    c.kv_pages[:, :, 1::2] *= scale
+    got = _run_gpu(c)
+    n = int(c.cu_q_lens[c.num_seqs])
+    assert torch.isfinite(got[:n].float()).all()
+    want = _run_oracle(c)
+    assert_close(as_f64(got)[:n] / scale, want[:n] / scale, *TOL["bf16"], what="big-v")
+
+
+_CAPTURE_FIRST = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import ragged_paged_attention_rpa_amd as rpa
+from ragged_paged_attention_rpa_amd import workloads as wl
+c = wl.make_gqa([(4, 4), (2, 1025), (24, 900)], num_q_heads=16, num_kv_heads=2, head_dim=128,
+                page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=401,
+                device="cuda", extra_tokens=4096, name="capture-first")
+d = "cuda"
+kl, pi = torch.from_numpy(c.kv_lens).to(d), torch.from_numpy(c.page_indices).to(d)
+cu, ns = torch.from_numpy(c.cu_q_lens).to(d), torch.tensor([c.num_seqs], dtype=torch.int32, device=d)
+ws = torch.empty(rpa.rpa_workspace_size(kl, pi, c.q.shape[0], 16, 2, 128, 16), dtype=torch.uint8,
+                 device=d)
+out = torch.zeros_like(c.q)
+def call():
+    rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, sm_scale=c.sm_scale, out=out, workspace=ws)
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+with torch.cuda.stream(s):
+    with torch.cuda.graph(g, stream=s):
+        call()                  # the process's first rpa_forward: under capture
+torch.cuda.current_stream().wait_stream(s)
+torch.cuda.synchronize()
+T = int(c.cu_q_lens[c.num_seqs])
+g.replay(); torch.cuda.synchronize()
+captured = out[:T].clone()
+out.zero_(); call(); torch.cuda.synchronize()   # eager: creates the side stream
+assert torch.equal(out[:T], captured), "capture-first replay differs from eager"
+out.zero_(); g.replay(); torch.cuda.synchronize()
+assert torch.equal(out[:T], captured), "second replay differs"
+print("capture-first ok", rpa.last_path())
+"""
+
+
+def test_first_call_under_capture_stays_on_one_stream():
+    """A process whose very first rpa_forward is captured: the library must not
+    create its side stream mid-capture (it stays on the caller's stream), and
+    the replays equal the later eager call (run in a fresh process so no
+    earlier call has created the side stream)."""
+    import os
+    import subprocess
+    import sys
+    _say("first call under capture (fresh process)")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _CAPTURE_FIRST, root], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-4000:]
+    assert "capture-first ok" in r.stdout
+
+
+def test_last_path_names_the_kernel_path():
+    _say("rpa_last_path")
+    c = wl.make_gqa([(1, 100), (40, 200)], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=91,
+                    device="cuda")
+    _run_gpu(c)
+    assert rpa.last_path() == "gqa_mfma_prefill"
+    c = wl.make_gqa([(1, 100), (3, 200)], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=92,
+                    device="cuda")
+    _check(c, _run_gpu(c), _run_oracle(c), "bf16")
+    assert rpa.last_path() == "gqa_generic"

@@ -58,6 +58,9 @@ MLA_CASES = [
     ([(1, 5000), (4, 1300), (1, 129)], 128, 16, 700, None, "page16-window"),
     ([(2, 400), (1, 3000)], 40, 32, None, 30.0, "h40-cap"),
     ([(1, 900), (2, 150)], 130, 64, None, None, "h130-two-groups"),
+    # page 16 and 20000 keys: the query tiles span 1250 pages, past the 1024
+    # page ids a workgroup caches, so the page window refills mid-tile
+    ([(2, 20000), (1, 300)], 128, 16, None, None, "page16-refill"),
 ]
 
 
