@@ -196,6 +196,28 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
                        rpa_stream_t stream);
 
 /*
+ * rpa_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory or create streams (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments and results are those of rpa_forward. The scratch space (work
+ * list, counters, split partials) is a static array in the library, one per
+ * device, of rpa_noalloc_scratch_bytes() bytes (96 MiB), held until the
+ * process ends. Capacities whose rpa_workspace_size exceeds it are rejected
+ * with RPA_E_WORKSPACE before any launch. All launches stay on `stream` (no
+ * side stream). Every call on a device shares that device's array and leaves
+ * its contents behind (the planner resets what must start at zero on each
+ * call): calls that overlap in time on one device race, so serialise them.
+ */
+rpa_status rpa_forward_noalloc(const void* q, rpa_dtype q_dtype, int32_t num_q_heads,
+                               int32_t head_dim, const void* kv_pages, rpa_dtype kv_dtype,
+                               int32_t total_num_pages, int32_t page_size, int32_t num_kv_heads,
+                               const rpa_ragged_meta* meta, const rpa_opts* opts, void* out,
+                               rpa_stream_t stream);
+
+/* Bytes of the static per-device scratch array of rpa_forward_noalloc. */
+size_t rpa_noalloc_scratch_bytes(void);
+
+/*
  * Scatter new tokens into a paged cache, in place [MLA v1 page: update_kv_cache;
  * Sparse page: prefill_write_and_attend self-write].
  *   Page-table mode (slot_loc == NULL, meta required): new token j of

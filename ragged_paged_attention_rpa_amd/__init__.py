@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(_HERE, "librpa.so")
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
 EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_last_path", "rpa_set_profile_events",
                     "rpa_set_profile_events_split",
-                    "rpa_workspace_size", "rpa_forward",
+                    "rpa_workspace_size", "rpa_forward", "rpa_forward_noalloc",
+                    "rpa_noalloc_scratch_bytes",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
                     "sparse_mla_workspace_size", "sparse_mla_forward")
 
@@ -89,6 +90,10 @@ def load_library():
     lib.rpa_workspace_size.restype = SZ
     lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P, SZ, P]
     lib.rpa_forward.restype = I32
+    lib.rpa_forward_noalloc.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P]
+    lib.rpa_forward_noalloc.restype = I32
+    lib.rpa_noalloc_scratch_bytes.argtypes = []
+    lib.rpa_noalloc_scratch_bytes.restype = SZ
     lib.kv_cache_update.argtypes = [I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
                                     MP, P, I32, P]
     lib.kv_cache_update.restype = I32
@@ -235,6 +240,30 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
                          _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(lib, st)
     return out
+
+
+def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, out,
+                        sm_scale=1.0, sliding_window=None, soft_cap=None, k_scale=None,
+                        v_scale=None, debug_validate=False, stream=None):
+    """rpa_forward on the library's static scratch (see ``rpa_forward_noalloc``
+    in include/rpa.h): no workspace and no allocation; ``out`` must be given."""
+    lib = load_library()
+    _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out)
+    T, Hq, D = q.shape
+    P, ps, ch, D2 = kv_pages.shape
+    if D2 != D or ch % 2:
+        raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
+    meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate)
+    st = lib.rpa_forward_noalloc(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages),
+                                 _dtype_code(kv_pages), P, ps, ch // 2, ctypes.byref(meta),
+                                 ctypes.byref(opts), _ptr(out), _stream(stream))
+    _raise(lib, st)
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().rpa_noalloc_scratch_bytes())
 
 
 def kv_cache_update(layout, new_a, new_b, cache_a, cache_b=None, *, kv_lens=None,

@@ -1345,7 +1345,8 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   hipStream_t dstream = stream;
   SideStream* side = nullptr;
   if (a.pre_kernel) {
-    if ((int64_t)a.max_num_tokens - a.max_num_seqs >= kOverlapMinTokens) side = side_fork(stream);
+    if (!a.single_stream && (int64_t)a.max_num_tokens - a.max_num_seqs >= kOverlapMinTokens)
+      side = side_fork(stream);
     if (side) dstream = side->s;
     // Prefill-class tiles on the eight-wave kernel (one workgroup per CU).
     prof_kernel_begin(stream, 0);
@@ -1394,6 +1395,36 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   }
   prof_end(stream);
   return e;
+}
+
+// Scratch of rpa_forward_noalloc: the work list, counters and split partials
+// of callers that cannot allocate. Every device the library runs on holds its
+// own copy until the process ends, and every call on a device shares it (the
+// planner rewrites the counters each call; calls that overlap on one device
+// race). In host code `scratch` is only a host-side stand-in for the symbol:
+// its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = (size_t)96 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream) {

@@ -199,11 +199,18 @@ size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int3
                                   num_kv_heads, head_dim, 0, nullptr);
 }
 
-rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
+}  // extern "C"
+
+namespace {
+
+// rpa_forward with its scratch either from the caller (workspace) or, for
+// rpa_forward_noalloc, from the library's static per-device scratch array
+// (noalloc: no stream is created, every launch stays on `stream`).
+rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
                        const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
                        int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
                        const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
-                       rpa_stream_t stream_) {
+                       bool noalloc, rpa_stream_t stream_) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   RPA_TRY(check_meta(meta, true));
   RPA_TRY(check_opts(opts));
@@ -250,6 +257,15 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
                     is_pow2(page_size) && aligned16(q) && aligned16(kv_pages) && aligned16(out);
   if (mfma) {
     const size_t need = rpa_workspace_size(meta, num_q_heads, num_kv_heads, head_dim, page_size);
+    if (noalloc) {
+      if (need > rpa::noalloc_scratch_bytes())
+        return fail(RPA_E_WORKSPACE,
+                    "these capacities need %zu bytes of scratch; rpa_forward_noalloc holds at "
+                    "most %zu (use rpa_forward with a workspace)",
+                    need, rpa::noalloc_scratch_bytes());
+      RPA_TRY(hip_status(rpa::noalloc_scratch(&workspace), "rpa_forward_noalloc scratch"));
+      workspace_bytes = rpa::noalloc_scratch_bytes();
+    }
     if (!workspace || workspace_bytes < need)
       return fail(RPA_E_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -265,6 +281,7 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
     rpa::gqa_bind_workspace(a, workspace);
     // The prefill kernel takes row maxima on raw scores, which needs an
     // increasing logit map: a positive score scale.
+    a.single_stream = noalloc ? 1 : 0;
     if (a.score_scale > 0.f &&
         rpa::gqa_prefill_supported(a.q_dtype, a.kv_dtype, head_dim, a.geo.group, page_size)) {
       // Prefill-class tiles of 256 rows for the eight-wave kernel (fewer tiles
@@ -280,6 +297,31 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   if (st == RPA_OK) g_last_path = "gqa_generic";
   return st;
 }
+
+}  // namespace
+
+extern "C" {
+
+rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
+                       const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
+                       int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
+                       const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
+                       rpa_stream_t stream) {
+  return gqa_forward(q, q_dtype, num_q_heads, head_dim, kv_pages, kv_dtype, total_num_pages,
+                     page_size, num_kv_heads, meta, opts, out, workspace, workspace_bytes, false,
+                     stream);
+}
+
+rpa_status rpa_forward_noalloc(const void* q, rpa_dtype q_dtype, int32_t num_q_heads,
+                               int32_t head_dim, const void* kv_pages, rpa_dtype kv_dtype,
+                               int32_t total_num_pages, int32_t page_size, int32_t num_kv_heads,
+                               const rpa_ragged_meta* meta, const rpa_opts* opts, void* out,
+                               rpa_stream_t stream) {
+  return gqa_forward(q, q_dtype, num_q_heads, head_dim, kv_pages, kv_dtype, total_num_pages,
+                     page_size, num_kv_heads, meta, opts, out, nullptr, 0, true, stream);
+}
+
+size_t rpa_noalloc_scratch_bytes(void) { return rpa::noalloc_scratch_bytes(); }
 
 rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const void* new_b,
                            void* cache_a, void* cache_b, rpa_dtype dtype, int32_t total_num_pages,

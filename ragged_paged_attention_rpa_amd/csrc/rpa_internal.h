@@ -71,6 +71,7 @@ struct GqaArgs {
   float v_scale;
   GqaGeometry geo;
   int pre_kernel;     // 1: prefill-class tiles go to gqa_prefill_kernel (geo.bq = its rows / group)
+  int single_stream;  // 1: every launch on the caller's stream (no library side stream)
   // workspace
   Tile* tiles;
   int32_t* counters;  // [0] tile count, [1] decode-kernel cursor (starts past the prefill
@@ -93,6 +94,10 @@ void gqa_bind_workspace(GqaArgs& a, void* ws);
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group);
 hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream);
 hipError_t launch_gqa_generic(const GqaArgs& a, hipStream_t stream);
+// The static per-device scratch array of rpa_forward_noalloc: its size, and
+// its device address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 // Prefill-class tiles on eight waves (gqa_prefill.hip). Requires
 // a.score_scale > 0 (the kernel takes row maxima on raw scores).
 int gqa_prefill_rows();

@@ -139,3 +139,18 @@ def test_sparse_static_rejections(lib):
     assert call(ps=96) == RPA_E_INVALID        # page_size % read_block
     assert call(C=512) == RPA_E_SHAPE          # cache narrower than the latent
     assert call(kl=256) == RPA_E_UNSUPPORTED
+
+
+def test_noalloc_rejects_capacities_beyond_its_scratch_before_any_launch(lib):
+    """rpa_forward_noalloc checks the capacities against its static scratch
+    array on the host and returns RPA_E_WORKSPACE without touching the GPU."""
+    cap = lib.rpa_noalloc_scratch_bytes()
+    assert cap == 96 << 20
+    big = _meta(S=4096, pps=512, T=4096)
+    assert lib.rpa_workspace_size(ctypes.byref(big), 32, 8, 128, 16) > cap
+    st = lib.rpa_forward_noalloc(FAKE, 1, 32, 128, FAKE, 1, 64, 16, 8, ctypes.byref(big),
+                                 ctypes.byref(_opts(lib)), FAKE, None)
+    assert st == RPA_E_WORKSPACE
+    assert "rpa_forward_noalloc holds at most" in lib.rpa_last_error().decode()
+    small = _meta(S=128, pps=512, T=128)
+    assert lib.rpa_workspace_size(ctypes.byref(small), 32, 8, 128, 16) <= cap

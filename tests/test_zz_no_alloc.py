@@ -1,0 +1,79 @@
+"""rpa_forward_noalloc: the allocation-free variant of rpa_forward, whose work
+list, counters and split partials live in the library's static per-device
+scratch array. Called through the C ABI and checked against rpa_forward on
+the same inputs (bit for bit: the kernels are shared) and against the oracle,
+on two calls in a row, the second with a smaller input."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ragged_paged_attention_rpa_amd as rpa
+from ragged_paged_attention_rpa_amd import workloads as wl
+from tests.helpers import as_f64, assert_close, storage
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _meta(c):
+    d = "cuda"
+    return (torch.from_numpy(c.kv_lens).to(d), torch.from_numpy(c.page_indices).to(d),
+            torch.from_numpy(c.cu_q_lens).to(d),
+            torch.tensor([c.num_seqs], dtype=torch.int32, device=d))
+
+
+def _kw(c):
+    return dict(sm_scale=c.sm_scale, sliding_window=c.sliding_window, soft_cap=c.soft_cap,
+                k_scale=c.k_scale, v_scale=c.v_scale)
+
+
+def test_noalloc_matches_rpa_forward_on_two_calls():
+    cases = [
+        # a prefill+decode batch with long split decodes (prefill kernel, decode
+        # kernel, merge: every scratch region is used) ...
+        wl.make_gqa([(1, 9000), (200, 1500), (1, 700), (3, 4000), (64, 64)], num_q_heads=32,
+                    num_kv_heads=8, head_dim=128, page_size=16, q_dtype=torch.bfloat16,
+                    kv_dtype=torch.bfloat16, seed=500, device="cuda", sliding_window=2000,
+                    soft_cap=40.0, name="noalloc-big"),
+        # ... then a smaller fp8 batch over the same scratch
+        wl.make_gqa([(1, 3000), (2, 300)], num_q_heads=16, num_kv_heads=4, head_dim=128,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.float8_e4m3fn,
+                    seed=501, device="cuda", kv_value_scale=2.0, k_scale=0.5, v_scale=0.5,
+                    name="noalloc-small"),
+    ]
+    for c in cases:
+        _say(f"rpa_forward_noalloc {c.name}")
+        kl, pi, cu, ns = _meta(c)
+        ref = rpa.rpa_forward(c.q, c.kv_pages, kl, pi, cu, ns, **_kw(c))
+        out = torch.full_like(c.q, 7.0)
+        rpa.rpa_forward_noalloc(c.q, c.kv_pages, kl, pi, cu, ns, out=out, **_kw(c))
+        torch.cuda.synchronize()
+        n = int(c.cu_q_lens[c.num_seqs])
+        assert torch.equal(out[:n], ref[:n]), f"{c.name}: noalloc differs from rpa_forward"
+        assert torch.equal(out[n:], torch.full_like(out[n:], 7.0))
+        q, qd = storage(c.q)
+        kv, kd = storage(c.kv_pages)
+        want = oracle.rpa(q, qd, kv, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
+                          **_kw(c))
+        tol = (5e-2, 5e-3) if c.kv_pages.dtype == torch.float8_e4m3fn else (2e-2, 2e-3)
+        assert_close(as_f64(out)[:n], want[:n], *tol, what=c.name)
+
+
+def test_noalloc_rejects_capacities_beyond_its_scratch():
+    _say("rpa_forward_noalloc capacity limit")
+    c = wl.make_gqa([(1, 100)], num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=502, device="cuda")
+    d = "cuda"
+    S = 4096  # capacity of 4096 sequences: split partials alone exceed the array
+    kl = torch.zeros(S, dtype=torch.int32, device=d)
+    pi = torch.zeros((S, c.page_indices.shape[1]), dtype=torch.int32, device=d)
+    cu = torch.zeros(S + 1, dtype=torch.int32, device=d)
+    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], 32, 8, 128, 16)
+    assert need > rpa.noalloc_scratch_bytes()
+    with pytest.raises(rpa.RpaError, match="rpa_forward_noalloc holds at most"):
+        rpa.rpa_forward_noalloc(c.q, c.kv_pages, kl, pi, cu, torch.ones(1, dtype=torch.int32,
+                                device=d), out=torch.empty_like(c.q))
