@@ -290,14 +290,20 @@ def setup_gqa(torch, rpa, wl, config):
     return case, fn
 
 
-def cpu_baseline_gqa(case, work, budget_s=15.0):
-    """Times the CPU oracle on a bounded sample of the workload's query tokens."""
+def cpu_baseline_gqa(case, work, budget_s=15.0, prefill_only=False):
+    """Times the CPU oracle on a bounded sample of the workload's query tokens
+    (with prefill_only, of the tokens of its prefill chunks)."""
     import oracle
     q, qd = _storage(case.q)
     kv, kd = _storage(case.kv_pages)
     T = int(case.cu_q_lens[case.num_seqs])
     rng = np.random.default_rng(0)
-    order = rng.permutation(T)
+    pool = np.arange(T)
+    if prefill_only:
+        ql = np.diff(case.cu_q_lens[:case.num_seqs + 1])
+        pool = np.concatenate([np.arange(case.cu_q_lens[i], case.cu_q_lens[i + 1])
+                               for i in range(case.num_seqs) if ql[i] > 1])
+    order = pool[rng.permutation(len(pool))]
 
     def run(tokens):
         t0 = time.perf_counter()
@@ -307,9 +313,9 @@ def cpu_baseline_gqa(case, work, budget_s=15.0):
                    tokens=tokens)
         return time.perf_counter() - t0
 
-    probe = np.sort(order[:max(1, min(T, 8))])
+    probe = np.sort(order[:max(1, min(len(order), 8))])
     dt = run(probe)
-    n = int(min(T, max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
+    n = int(min(len(order), max(len(probe), len(probe) * budget_s / max(dt, 1e-3))))
     tokens = np.sort(order[:n])
     dt = run(tokens)
     # Work of the sampled tokens: their visible keys (bytes of K/V rows read,
@@ -325,9 +331,10 @@ def cpu_baseline_gqa(case, work, budget_s=15.0):
     eb = case.kv_pages.element_size()
     kv_bytes = rows * 2 * case.num_kv_heads * case.head_dim * eb
     flops = rows * case.num_q_heads * 4 * case.head_dim
+    what = "prefill-chunk query tokens" if prefill_only else "query tokens"
     return {"seconds": dt, "tokens": len(tokens), "kv_bytes": kv_bytes, "flops": flops,
             "cores": oracle.num_threads(),
-            "sample": f"{len(tokens)} of {T} query tokens (all q heads), drawn with seed 0"}
+            "sample": f"{len(tokens)} of {len(pool)} {what} (all q heads), drawn with seed 0"}
 
 
 def load_traffic(config):
@@ -429,7 +436,8 @@ def bench_gqa(args, torch, rpa, wl):
         res["frac_of_combined_roof"] = roof_s / (kern_mean / 1e3)
     res["work"] = work
     if not args.no_cpu_baseline:
-        cb = cpu_baseline_gqa(case, work, args.cpu_budget)
+        cb = cpu_baseline_gqa(case, work, args.cpu_budget,
+                              prefill_only=args.config == "mixed_gqa" and subset != "only")
         if res["unit"] == "GB/s":
             v, unit = cb["kv_bytes"] / cb["seconds"] / 1e9, "GB/s"
         else:
@@ -579,6 +587,13 @@ def main():
                          "(off), or time only the subset (only; for profiling that kernel)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="target seconds of oracle CPU work for cpu_baseline")
+    ap.add_argument("--extras", choices=("on", "off"), default="on",
+                    help="decode_gqa only: also measure the other full-size workloads (the mixed "
+                         "batch's prefill kernel and decode subset, MLA decode, sparse MLA) and "
+                         "attach each, with its own roofline and cpu_baseline, to the line "
+                         "(off for profiling runs of the decode kernel alone)")
+    ap.add_argument("--extras-cpu-budget", type=float, default=8.0,
+                    help="target seconds of oracle CPU work for each extra workload")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many bytes "
                          "(calibration run for the PMC byte counters)")
@@ -601,17 +616,35 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n * 4}))
         return
-    if args.config in ("decode_gqa", "mixed_gqa", "tiny_gqa"):
-        res, cfg = bench_gqa(args, torch, rpa, wl)
-    else:
-        res, cfg = bench_latent(args, torch, rpa, wl)
+    res, cfg = run_config(args, torch, rpa, wl)
     line = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16" if args.config != "tiny_gqa" else "f32", "data": "synthetic",
             "config": cfg}
     line.update(res)
+    if args.config == "decode_gqa" and args.extras == "on":
+        # The metric's other half and the other full-size workloads, each timed
+        # the same way (warm timed region + cold pass) on its own dominant
+        # kernel: "prefill" is the mixed batch (prefill kernel TFLOP/s, with its
+        # decode subset's GB/s under decode_part).
+        for key, config in (("prefill", "mixed_gqa"), ("mla_decode", "mla_decode"),
+                            ("sparse_mla", "sparse_mla")):
+            sub = argparse.Namespace(**vars(args))
+            sub.config = config
+            sub.cpu_budget = args.extras_cpu_budget
+            print(f"[bench] {config}", file=sys.stderr, flush=True)
+            r, c = run_config(sub, torch, rpa, wl)
+            r["config"] = c
+            line[key] = r
+            torch.cuda.empty_cache()
     print(json.dumps(line))
+
+
+def run_config(args, torch, rpa, wl):
+    if args.config in ("decode_gqa", "mixed_gqa", "tiny_gqa"):
+        return bench_gqa(args, torch, rpa, wl)
+    return bench_latent(args, torch, rpa, wl)
 
 
 if __name__ == "__main__":

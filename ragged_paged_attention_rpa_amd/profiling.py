@@ -12,8 +12,19 @@ Two text products, both computed from the CSV files rocprofv3 writes with
   The result is written as JSON keyed by a hash of the kernel's source, so
   ``bench.py`` reports it only while the kernel is unchanged.
 
+* ``mfma``: matrix-core use of one kernel from one ``--pmc`` run of
+  ``SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES
+  GRBM_GUI_ACTIVE``: MFMA-busy share of the SIMD cycles while the kernel ran
+  (busy cycles summed over SIMDs / (GPU-active cycles x 1024 SIMDs)) and the
+  bf16 MFMA flops executed (MOPS x 512) against the kernel's algorithmic flops.
+  rocprofv3's CSV gives GRBM_GUI_ACTIVE summed over the 8 XCDs (its value / 8
+  over the dispatch's own start-end span comes out at the shader clock), so
+  the active cycles of one XCD are that value / 8.
+
 Usage:
   python -m ragged_paged_attention_rpa_amd.profiling trace STATS_CSV OUT_TXT "TITLE" "COMMAND"
+  python -m ragged_paged_attention_rpa_amd.profiling mfma PMC_CSV KERNEL ALGO_FLOPS OUT_TXT \
+      "TITLE" "COMMAND"
   python -m ragged_paged_attention_rpa_amd.profiling traffic CONFIG KERNEL \\
       FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV COPY_BYTES "COMMAND"
 """
@@ -89,6 +100,53 @@ def traffic_summary(config, kernel, fetch_csv, write_csv, copy_fetch_csv, copy_w
     }
 
 
+SIMDS = 1024  # 256 CUs x 4 SIMDs on MI355X
+XCDS = 8
+
+
+def _per_dispatch(pmc_csv, kernel_substr, counter, spans=None):
+    """{dispatch id: [instance values]} of `counter` for the matching kernels;
+    fills `spans` with each dispatch's (start, end) timestamps in ns."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(pmc_csv)):
+        if kernel_substr in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[r["Dispatch_Id"]].append(float(r["Counter_Value"]))
+            if spans is not None:
+                spans[r["Dispatch_Id"]] = (int(r["Start_Timestamp"]), int(r["End_Timestamp"]))
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {kernel_substr!r} in {pmc_csv}")
+    return per
+
+
+def mfma_summary(pmc_csv, kernel, algo_flops, title, command):
+    busy = _per_dispatch(pmc_csv, kernel, "SQ_VALU_MFMA_BUSY_CYCLES")
+    mops = _per_dispatch(pmc_csv, kernel, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    sqb = _per_dispatch(pmc_csv, kernel, "SQ_BUSY_CYCLES")
+    spans = {}
+    gui = _per_dispatch(pmc_csv, kernel, "GRBM_GUI_ACTIVE", spans)
+    ids = sorted(set(busy) & set(mops) & set(gui), key=lambda x: int(x))
+    xcd_cyc = {i: sum(gui[i]) / XCDS for i in ids}
+    util = [sum(busy[i]) / (xcd_cyc[i] * SIMDS) for i in ids]
+    flops = [sum(mops[i]) * 512 for i in ids]
+    out = [f"# rocprofv3 MFMA counters — {title}",
+           "# command (run from the repo root):",
+           f"#   {command}",
+           f"# kernel: {kernel}; dispatches: {len(ids)}",
+           "# mfma_busy_pct = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/8 x 1024 SIMDs); "
+           "clock = GRBM_GUI_ACTIVE/8 / dispatch span",
+           f"{'dispatch':>9s} {'span_us':>9s} {'clock_GHz':>9s} {'mfma_busy_pct':>14s} "
+           f"{'mfma_bf16_flops':>16s} {'exec/algo':>10s} {'sq_busy_cyc':>12s}"]
+    for i, u, f in zip(ids, util, flops):
+        t0, t1 = spans[i]
+        span_ns = max(1, t1 - t0)
+        out.append(f"{i:>9s} {span_ns / 1e3:9.1f} {xcd_cyc[i] / span_ns:9.2f} {100 * u:14.1f} "
+                   f"{f:16.4e} {f / algo_flops:10.3f} {sum(sqb[i]):12.0f}")
+    mu, mf = sum(util) / len(util), sum(flops) / len(flops)
+    out.append(f"# mean: MFMA busy {100 * mu:.1f}% of SIMD cycles; executed bf16 MFMA flops "
+               f"{mf:.4e} = {mf / algo_flops:.3f} x the algorithmic {algo_flops:.4e}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "trace":
         stats, out, title, command = argv[1:5]
@@ -100,6 +158,12 @@ def main(argv):
         out = os.path.join(ROOT, "profiles", f"traffic_{config}.json")
         json.dump(d, open(out, "w"), indent=1)
         print(json.dumps(d))
+        return
+    if len(argv) >= 7 and argv[0] == "mfma":
+        pmc, kernel, flops, out, title, command = argv[1:7]
+        text = mfma_summary(pmc, kernel, float(flops), title, command)
+        open(out, "w").write(text)
+        print(text)
         return
     print(__doc__)
     raise SystemExit(2)
