@@ -43,7 +43,7 @@ KERNEL_SOURCES = {
     "decode_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
     "mixed_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_prefill.hip",
     "tiny_gqa": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",
-    "mla_decode": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
+    "mla_decode": "ragged_paged_attention_rpa_amd/csrc/mla_decode.hip",
     "sparse_mla": "ragged_paged_attention_rpa_amd/csrc/mla_attn.hip",
     # the mixed batch's decode subset (--decode-subset only): the fp8 decode kernel
     "mixed_gqa_decode": "ragged_paged_attention_rpa_amd/csrc/gqa_attn.hip",

@@ -258,7 +258,12 @@ size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, in
  *     (k_pe pad columns written as zeros).
  *   out [max_num_tokens, num_heads, lkv_dim] (BF16).
  * Every head attends the one latent per token: K_t = [kv_c_t || k_pe_t],
- * V_t = kv_c_t. Runs the scatter, then the attention, in stream order.
+ * V_t = kv_c_t. The result equals scattering the new tokens into the caches
+ * and then attending; one launch does both: keys at positions >= kv_len - q_len
+ * are read from new_kv_c / new_k_pe, and each token's row is written to its
+ * cache slot by the same work-group that finished attending for that token,
+ * so no read of the caches in this call depends on those writes. Two tokens of
+ * one call that map to the same cache slot are an error (debug_validate).
  * This build implements lkv_dim = 512, r_dim = 64, bf16.
  */
 rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* new_kv_c,

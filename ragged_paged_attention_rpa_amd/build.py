@@ -17,7 +17,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["rpa_api.cpp", "kv_update.hip", "gqa_attn.hip", "gqa_prefill.hip", "mla_attn.hip"]
+SOURCES = ["rpa_api.cpp", "kv_update.hip", "gqa_attn.hip", "gqa_prefill.hip", "mla_attn.hip",
+           "mla_decode.hip"]
 
 # Packed-fp32 VALU ops stay off: the compiler must not emit v_pk_{add,mul,fma}_f32.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -29,10 +30,16 @@ def _hipcc():
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
+# Per-file flags. mla_decode.hip keeps its QK^T accumulators in VGPRs (the
+# MFMA "VGPR form"): its 256 AGPRs hold the output accumulators.
+FILE_FLAGS = {"mla_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src):
     os.makedirs(BUILD, exist_ok=True)
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -1,10 +1,8 @@
-// MLA latent attention [MLA v1 page: mla_ragged_paged_attention,
-// ref_mla_ragged_paged_attention, flash_attention] and sparse MLA-latent
-// attention [Sparse page: sparse_mla_attention, _sparse_mla_kernel_chunked_hminor].
-//
-// Both attend one 576-wide latent row per key, shared by every head: the key
-// is the whole row [kv_c (512) || k_pe (64)], the value its first 512 columns.
-// Shared core:
+// Sparse MLA-latent attention [Sparse page: sparse_mla_attention,
+// _sparse_mla_kernel_chunked_hminor]: each query attends its own top-k set of
+// page units of a fused latent pool. The key is a whole latent row
+// [kv_c (512) || k_pe (64)], shared by every head; the value its first 512
+// columns.
 //  * keys stream through LDS in blocks of 64 rows, moved by
 //    global_load_lds_dwordx4 (no register staging) into two stages, so the
 //    next block's loads are in flight while the current one is multiplied.
@@ -17,13 +15,11 @@
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS, Q^T in VGPRs),
 //    V^T for O^T += V^T P^T read straight out of the same rows with
 //    ds_read_b64_tr_b16, so the value needs no second copy.
-// MLA: one workgroup of 8 waves takes 128 heads of one query token (16 heads
-// per wave) over a range of its keys; long decode ranges are split and merged
-// with the rescaling algebra of the page's flash_attention.
-// Sparse: one workgroup of 4 waves takes one query's 16 heads; each wave owns
-// one 16-key tile of every block; the four partial softmax states are merged
-// in LDS at the end. The key set is the query's selected units, each resolved
+// One workgroup of 4 waves takes one query's 16 heads; each wave owns one
+// 16-key tile of every block; the four partial softmax states are merged in
+// LDS at the end. The key set is the query's selected units, each resolved
 // through the page table [Sparse page: _src paged address computation].
+// (The dense MLA path is in mla_decode.hip.)
 #include "rpa_device.h"
 #include "rpa_internal.h"
 
@@ -180,494 +176,6 @@ __device__ __forceinline__ float score_log2(float s, float sc, float cap) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-int g_num_cus = 0;
-int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
-  }
-  return g_num_cus;
-}
-
-// =============================================================== MLA ========
-
-constexpr int kMlaWaves = 8;
-constexpr int kMlaThreads = kMlaWaves * 64;
-constexpr int kMlaHT = 1;                             // 16-head tiles per wave
-constexpr int kMlaHeads = kMlaWaves * 16 * kMlaHT;    // heads per workgroup (128)
-constexpr int kPageWin = 1024;                        // page ids cached in LDS
-constexpr int kMlaMaxSplits = 16;
-constexpr int kMlaMinChunk = 256;
-constexpr int kMlaAhead = 2;                          // K k-steps read ahead of their MFMAs
-
-struct MlaSeq {
-  int cu0, q_len, kv_len, kv_cap;
-};
-
-__device__ __forceinline__ MlaSeq mla_seq(const MlaArgs& a, int seq) {
-  MlaSeq s;
-  s.cu0 = a.cu_q_lens[seq];
-  s.q_len = a.cu_q_lens[seq + 1] - s.cu0;
-  s.kv_len = a.kv_lens[seq];
-  s.kv_cap = min(s.kv_len, a.pages_per_seq * a.page_size);
-  return s;
-}
-
-// Visible key range of query token tok_rel of a sequence (causal + window).
-__device__ __forceinline__ void mla_range(const MlaArgs& a, const MlaSeq& s, int tok_rel, int* lo,
-                                          int* hi) {
-  const int pos = s.kv_len - s.q_len + tok_rel;
-  *lo = a.window > 0 ? max(0, pos - a.window + 1) : 0;
-  *hi = min(pos + 1, s.kv_cap);
-}
-
-__device__ __forceinline__ int mla_num_seqs(const MlaArgs& a) {
-  return clampi(*a.num_seqs, 0, a.max_num_seqs);
-}
-
-__device__ __forceinline__ int mla_hgroups(const MlaArgs& a) {
-  return (a.num_heads + kMlaHeads - 1) / kMlaHeads;
-}
-
-__device__ __forceinline__ int mla_nsplit(int n, int chunk) {
-  return (n <= 0 || chunk <= 0) ? 1 : min(kMlaMaxSplits, (n + chunk - 1) / chunk);
-}
-
-// counters: [0] tile count, [1] work cursor, [2] split chunk, [64..] per-seq tile offsets
-__global__ void __launch_bounds__(256) mla_plan_kernel(MlaArgs a, int tile_target) {
-  __shared__ int sh[256];
-  __shared__ unsigned long long s_total;
-  __shared__ int s_max;
-  const int tid = threadIdx.x;
-  const int ns = mla_num_seqs(a);
-  const int HG = mla_hgroups(a);
-  if (tid == 0) {
-    s_total = 0;
-    s_max = 0;
-  }
-  __syncthreads();
-  // Pass 1: total and largest decode key range.
-  unsigned long long part = 0;
-  int mx = 0;
-  for (int i = tid; i < ns; i += 256) {
-    const MlaSeq s = mla_seq(a, i);
-    if (s.q_len == 1) {
-      int lo, hi;
-      mla_range(a, s, 0, &lo, &hi);
-      const int n = max(0, hi - lo);
-      part += n;
-      mx = max(mx, n);
-    }
-  }
-  atomicAdd(&s_total, part);
-  atomicMax(&s_max, mx);
-  __syncthreads();
-  const unsigned long long per = (s_total + tile_target - 1) / (unsigned long long)max(1, tile_target);
-  int chunk = (int)(per < (1ull << 30) ? per : (1ull << 30));
-  chunk = max(chunk, (s_max + kMlaMaxSplits - 1) / kMlaMaxSplits);
-  chunk = max(kMlaMinChunk, (chunk + kBlk - 1) / kBlk * kBlk);
-  // Pass 2: per-sequence tile counts and offsets.
-  int* off = a.counters + 64;
-  int run = 0;
-  for (int c0 = 0; c0 < ns; c0 += 256) {
-    const int i = c0 + tid;
-    int n = 0;
-    if (i < ns) {
-      const MlaSeq s = mla_seq(a, i);
-      if (s.q_len == 1) {
-        int lo, hi;
-        mla_range(a, s, 0, &lo, &hi);
-        n = mla_nsplit(hi - lo, chunk) * HG;
-      } else if (s.q_len > 1) {
-        n = s.q_len * HG;
-      }
-    }
-    sh[tid] = n;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-      const int x = tid >= o ? sh[tid - o] : 0;
-      __syncthreads();
-      sh[tid] += x;
-      __syncthreads();
-    }
-    if (i < ns) off[i] = run + sh[tid] - n;
-    run += sh[255];
-    __syncthreads();
-  }
-  if (tid == 0) off[ns] = run;
-  __threadfence();
-  __syncthreads();
-  const int total = min(run, a.tile_capacity);
-  // Each thread writes one contiguous range of tiles (one search, then the
-  // owning sequence advances as its offsets are passed).
-  const int span = (total + 255) / 256;
-  const int t0 = min(total, tid * span);
-  const int t1 = min(total, t0 + span);
-  int seq = -1, seq_begin = 0, seq_end = 0, q_len = 0;
-  for (int t = t0; t < t1; ++t) {
-    if (seq < 0 || t >= seq_end) {
-      int lo = 0, hi = ns - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= t)
-          lo = mid;
-        else
-          hi = mid - 1;
-      }
-      seq = lo;
-      seq_begin = off[seq];
-      seq_end = off[seq + 1];
-      q_len = a.cu_q_lens[seq + 1] - a.cu_q_lens[seq];
-    }
-    const int local = t - seq_begin;
-    int4 tl;
-    tl.x = seq;
-    tl.w = local % HG;
-    if (q_len == 1) {
-      tl.y = 0;
-      tl.z = local / HG;  // split
-    } else {
-      tl.y = local / HG;  // token
-      tl.z = -1;
-    }
-    reinterpret_cast<int4*>(a.tiles)[t] = tl;
-  }
-  if (tid == 0) {
-    a.counters[0] = total;
-    a.counters[1] = 0;
-    a.counters[2] = chunk;
-  }
-}
-
-struct MlaShared {
-  char stage[2][kStageBytes];
-  int pages[kPageWin];
-  int tile;
-};
-static_assert(sizeof(MlaShared) <= 160 * 1024, "MLA LDS budget");
-
-// One tile: 128 heads (16 per wave) of one query token over a key range; a
-// 64-key block is taken as two halves of 32 keys, each with its own softmax
-// step, which keeps the per-step registers small.
-__device__ void mla_process_tile(const MlaArgs& a, int4 tl, MlaShared& sm, int ps_log2, int chunk) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
-  const int g = lane >> 4;
-  const int seq = tl.x;
-  const MlaSeq s = mla_seq(a, seq);
-  const int tok_rel = tl.y;
-  const int split = tl.z;
-  int lo_all, hi_all;
-  mla_range(a, s, tok_rel, &lo_all, &hi_all);
-  int lo = lo_all, hi = hi_all, nsplit = 1;
-  if (split >= 0) {
-    nsplit = mla_nsplit(hi_all - lo_all, chunk);
-    lo = lo_all + split * chunk;
-    hi = (split == nsplit - 1) ? hi_all : min(hi_all, lo + chunk);
-  }
-  const int tok = s.cu0 + tok_rel;
-  const int head0 = tl.w * kMlaHeads + wave * 16 * kMlaHT;  // first head of this wave
-  const bool wave_active = head0 < a.num_heads;
-
-  u32x4 qv[kMlaHT][kQSteps];
-#pragma unroll
-  for (int h = 0; h < kMlaHT; ++h) {
-    const int head = head0 + 16 * h + (lane & 15);
-    load_q(qv[h], (const uint16_t*)a.ql_nope + ((int64_t)tok * a.num_heads + head) * a.lkv_dim,
-           (const uint16_t*)a.q_pe + ((int64_t)tok * a.num_heads + head) * a.r_dim,
-           head < a.num_heads);
-  }
-
-  floatx4 acc[kMlaHT][kDvTiles];
-#pragma unroll
-  for (int h = 0; h < kMlaHT; ++h)
-#pragma unroll
-    for (int dt = 0; dt < kDvTiles; ++dt) acc[h][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kMlaHT], l_run[kMlaHT];
-#pragma unroll
-  for (int h = 0; h < kMlaHT; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-  }
-
-  const int kb0 = (lo / kBlk) * kBlk;
-  const int nblk = hi > kb0 ? cdiv_i(hi - kb0, kBlk) : 0;
-  const int32_t* table = a.page_indices + (int64_t)seq * a.pages_per_seq;
-  const int ps_mask = (1 << ps_log2) - 1;
-  int pwin = kb0 >> ps_log2;
-  for (int i = tid; i < kPageWin; i += kMlaThreads) {
-    const int lp = pwin + i;
-    sm.pages[i] = lp < a.pages_per_seq ? table[lp] : -1;
-  }
-  __syncthreads();
-
-  RowSrc src;
-  src.a = (const char*)a.cache_kv_c;
-  src.b = (const char*)a.cache_k_pe;
-  src.sa = (int64_t)a.kvc_stride * 2;
-  src.sb = (int64_t)a.kpe_stride * 2;
-  const uint32_t st0 = lds_addr(sm.stage[0]);
-  const uint32_t st1 = lds_addr(sm.stage[1]);
-  const int P = a.total_num_pages;
-
-  // Row of this wave's key 8*wave + lane/8 of block b (the wave moves keys
-  // 8*wave .. +7 of every block). Called by all waves at the same point: a
-  // page-window refill synchronises the workgroup.
-  auto prep_rows = [&](int b) -> int {
-    const int kb = kb0 + b * kBlk;
-    if (((kb + kBlk - 1) >> ps_log2) - pwin >= kPageWin) {
-      wg_barrier();
-      pwin = kb >> ps_log2;
-      for (int i = tid; i < kPageWin; i += kMlaThreads) {
-        const int lp = pwin + i;
-        sm.pages[i] = lp < a.pages_per_seq ? table[lp] : -1;
-      }
-      __syncthreads();
-    }
-    const int key = kb + 8 * wave + (lane >> 3);
-    int row = -1;
-    if (key >= lo && key < hi) {
-      const int page = sm.pages[(key >> ps_log2) - pwin];
-      if (page >= 0 && page < P) row = (page << ps_log2) + (key & ps_mask);
-    }
-    return row;
-  };
-
-  // Log2-domain logit of a raw score: s * scale * log2(e), or with the soft
-  // cap c, c * tanh(s * scale / c) * log2(e) = c2 - c3 / (2^{s * c1} + 1).
-  const bool capped = a.soft_cap != 0.f;
-  const float c1 = capped ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
-  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
-  auto logit = [&](float sraw) -> float {
-    if (!capped) return sraw * c1;
-    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
-  };
-  const uint32_t klat = k_lat(), krope = k_rope(), vlat = v_lat();
-  drain_vmem_before_loop();
-  if (nblk > 0) {
-    const int row0 = prep_rows(0);
-#pragma unroll
-    for (int k = 0; k < kDmaPer8; ++k) issue_key_dma(src, st0, wave, row0, k);
-  }
-  for (int b = 0; b < nblk; ++b) {
-    const uint32_t cur = (b & 1) ? st1 : st0;
-    const uint32_t nxt = (b & 1) ? st0 : st1;
-    // Block b was issued during the previous block's work; the barrier also
-    // means every wave is done with stage nxt, which block b + 1 now fills.
-    wait_vmcnt<0>();
-    wg_barrier();
-    const bool more = b + 1 < nblk;
-    const int nrow = more ? prep_rows(b + 1) : -1;
-    if (!wave_active) {
-      if (more) {
-#pragma unroll
-        for (int k = 0; k < kDmaPer8; ++k) issue_key_dma(src, nxt, wave, nrow, k);
-      }
-      continue;
-    }
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      const int kb = kb0 + b * kBlk + 32 * half;
-      const uint32_t hc = cur + (uint32_t)(2 * half * kTileKvc);
-      u32x4 pb[kMlaHT];
-      floatx4 sv[2][kMlaHT];
-      // The first half's k-steps carry this wave's DMA of block b + 1.
-      const bool dma_here = more && half == 0;
-      score_tiles<2, kMlaHT, kMlaAhead>(sv, hc + klat, cur + (uint32_t)(2 * half * kTileKpe) + krope, qv,
-                             [&](int j) {
-                               if (j < kDmaPer8 && dma_here) issue_key_dma(src, nxt, wave, nrow, j);
-                             });
-#pragma unroll
-      for (int h = 0; h < kMlaHT; ++h) {
-        float mblk = -INFINITY;
-        if (kb >= lo && kb + 32 <= hi) {  // all 32 keys visible: no mask
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              sv[kt][h][i] = logit(sv[kt][h][i]);
-              mblk = fmaxf(mblk, sv[kt][h][i]);
-            }
-        } else {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kb + 16 * kt + 4 * g + i;
-              const float x = (key >= lo && key < hi) ? logit(sv[kt][h][i]) : -INFINITY;
-              sv[kt][h][i] = x;
-              mblk = fmaxf(mblk, x);
-            }
-        }
-        mblk = wave_max_xor<16>(mblk);
-        mblk = wave_max_xor<32>(mblk);
-        const bool need = mblk > m_run[h] + kLazyTau;
-        if (wave_any(need)) {
-          const float m_new = need ? mblk : m_run[h];
-          const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.f;  // rows not moving keep scale 1
-          l_run[h] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < kDvTiles; ++dt) {
-            acc[h][dt][0] *= alpha;
-            acc[h][dt][1] *= alpha;
-            acc[h][dt][2] *= alpha;
-            acc[h][dt][3] *= alpha;
-          }
-          m_run[h] = m_new;
-        }
-        pb[h] = u32x4{0u, 0u, 0u, 0u};
-        if (m_run[h] != -INFINITY) {
-          float psum = 0.f;
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              sv[kt][h][i] = fast_exp2(sv[kt][h][i] - m_run[h]);
-              psum += sv[kt][h][i];
-            }
-          l_run[h] += psum;
-          pb[h][0] = pack_bf16x2(sv[0][h][0], sv[0][h][1]);
-          pb[h][1] = pack_bf16x2(sv[0][h][2], sv[0][h][3]);
-          pb[h][2] = pack_bf16x2(sv[1][h][0], sv[1][h][1]);
-          pb[h][3] = pack_bf16x2(sv[1][h][2], sv[1][h][3]);
-        }
-      }
-      // O^T += V^T P^T over the 32 keys (one k-step: tiles 2*half and
-      // 2*half + 1). The V^T reads of tile dt + 1 are issued before the MFMA
-      // of tile dt, so one LDS round trip overlaps one MFMA.
-      const uint32_t vcur = hc + vlat;
-      u32x2 v0 = lds_read_tr16(vcur), v1 = lds_read_tr16(vcur + kTileKvc);
-#pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt) {
-        u32x2 n0 = {0u, 0u}, n1 = {0u, 0u};
-        if (dt + 1 < kDvTiles) {
-          const uint32_t va = xor_here(vcur, (uint32_t)((dt + 1) << 5));
-          n0 = lds_read_tr16(va);
-          n1 = lds_read_tr16(va + kTileKvc);
-        }
-        u32x4 vf = {v0[0], v0[1], v1[0], v1[1]};
-        pin_after(vf);  // the prefetch stays ahead of this tile's MFMA
-#pragma unroll
-        for (int h = 0; h < kMlaHT; ++h)
-          acc[h][dt] = mfma_16x16x32(as_bf16x8(vf), as_bf16x8(pb[h]), acc[h][dt]);
-        v0 = n0;
-        v1 = n1;
-      }
-    }
-  }
-
-  if (!wave_active) return;
-#pragma unroll
-  for (int h = 0; h < kMlaHT; ++h) {
-    const int head = head0 + 16 * h + (lane & 15);
-    float l_row = wave_sum_xor<16>(l_run[h]);
-    l_row = wave_sum_xor<32>(l_row);
-    if (head >= a.num_heads) continue;
-    if (split >= 0 && nsplit > 1) {
-      // The split's output normalised by its own row sum, in bf16 (a convex
-      // combination of bf16 value rows, whose range half precision might not
-      // hold), with (m, l) in fp32: half the bytes of unnormalised fp32
-      // partials, written here and read again by the merge.
-      const int64_t pidx = (int64_t)seq * kMlaMaxSplits + split;
-      uint16_t* pa = a.part_acc + (pidx * a.num_heads + head) * kDl;
-      const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
-#pragma unroll
-      for (int dt = 0; dt < kDvTiles; ++dt)
-        *reinterpret_cast<u32x2*>(pa + 16 * dt + 4 * g) =
-            u32x2{pack_bf16x2(acc[h][dt][0] * inv_l, acc[h][dt][1] * inv_l),
-                  pack_bf16x2(acc[h][dt][2] * inv_l, acc[h][dt][3] * inv_l)};
-      if (g == 0) {
-        float* pm = a.part_ml + (pidx * a.num_heads + head) * 2;
-        pm[0] = m_run[h];
-        pm[1] = l_row;
-      }
-      continue;
-    }
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    uint16_t* op = (uint16_t*)a.out + ((int64_t)tok * a.num_heads + head) * kDl;
-#pragma unroll
-    for (int dt = 0; dt < kDvTiles; ++dt) {
-      u32x2 w;
-      w[0] = pack_bf16x2(acc[h][dt][0] * inv, acc[h][dt][1] * inv);
-      w[1] = pack_bf16x2(acc[h][dt][2] * inv, acc[h][dt][3] * inv);
-      *reinterpret_cast<u32x2*>(op + 16 * dt + 4 * g) = w;
-    }
-  }
-}
-
-__global__ void __launch_bounds__(kMlaThreads) mla_tile_kernel(MlaArgs a, int ps_log2) {
-  __shared__ __attribute__((aligned(1024))) MlaShared sm;
-  const int count = a.counters[0];
-  const int chunk = a.counters[2];
-  for (;;) {
-    if (threadIdx.x == 0) sm.tile = atomicAdd(&a.counters[1], 1);
-    __syncthreads();
-    const int ti = sm.tile;
-    __syncthreads();
-    if (ti >= count) break;
-    const int4 tl = reinterpret_cast<const int4*>(a.tiles)[ti];
-    mla_process_tile(a, tl, sm, ps_log2, chunk);
-    __syncthreads();
-  }
-}
-
-// Combines the split partials of decode sequences: thread = (head, 8 dims).
-__global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
-  const int seq = blockIdx.x;
-  if (seq >= mla_num_seqs(a)) return;
-  const MlaSeq s = mla_seq(a, seq);
-  if (s.q_len != 1) return;
-  int lo, hi;
-  mla_range(a, s, 0, &lo, &hi);
-  const int nsplit = mla_nsplit(hi - lo, a.counters[2]);
-  if (nsplit <= 1) return;
-  const int t = blockIdx.y * 256 + threadIdx.x;
-  const int head = t >> 6;
-  const int d0 = (t & 63) * 8;
-  if (head >= a.num_heads) return;
-  const int64_t pbase = (int64_t)seq * kMlaMaxSplits;
-  float mv[kMlaMaxSplits];
-  float M = -INFINITY;
-#pragma unroll
-  for (int sp = 0; sp < kMlaMaxSplits; ++sp) {
-    mv[sp] = sp < nsplit ? a.part_ml[((pbase + sp) * a.num_heads + head) * 2] : -INFINITY;
-    M = fmaxf(M, mv[sp]);
-  }
-  // Split sp contributes weight l_sp * 2^(m_sp - M) times its normalised output.
-  float L = 0.f;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int sp = 0; sp < kMlaMaxSplits; ++sp) {
-      if (sp >= nsplit) break;
-      const float w = fast_exp2(mv[sp] - M) * a.part_ml[((pbase + sp) * a.num_heads + head) * 2 + 1];
-      L += w;
-      const uint16_t* pa = a.part_acc + ((pbase + sp) * a.num_heads + head) * kDl + d0;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(pa);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float lo, hi;
-        unpack_part(x[i], lo, hi, false);
-        o[2 * i] += w * lo;
-        o[2 * i + 1] += w * hi;
-      }
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* op = (uint16_t*)a.out + ((int64_t)s.cu0 * a.num_heads + head) * kDl + d0;
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
-  *reinterpret_cast<u32x4*>(op) = w;
-}
 
 // ============================================================ sparse ========
 
@@ -892,50 +400,6 @@ sparse_mla_kernel(SparseArgs a) {
 }
 
 }  // namespace
-
-size_t mla_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_heads, int lkv_dim,
-                           int* tile_capacity, int* max_splits) {
-  const int HG = (num_heads + kMlaHeads - 1) / kMlaHeads;
-  const int64_t cap = (int64_t)HG * ((int64_t)max_num_tokens + (int64_t)max_num_seqs * kMlaMaxSplits);
-  if (tile_capacity) *tile_capacity = (int)cap;
-  if (max_splits) *max_splits = kMlaMaxSplits;
-  const int64_t nparts = (int64_t)max_num_seqs * kMlaMaxSplits;
-  size_t bytes = align256((64 + (size_t)max_num_seqs + 1) * sizeof(int32_t));
-  bytes += align256((size_t)cap * 16);
-  bytes += align256((size_t)nparts * num_heads * 2 * sizeof(float));
-  bytes += align256((size_t)nparts * num_heads * (size_t)lkv_dim * sizeof(uint16_t));
-  return bytes;
-}
-
-void mla_bind_workspace(MlaArgs& a, void* ws) {
-  int cap = 0, ms = 0;
-  mla_workspace_bytes(a.max_num_seqs, a.max_num_tokens, a.num_heads, a.lkv_dim, &cap, &ms);
-  a.tile_capacity = cap;
-  a.max_splits = ms;
-  char* p = (char*)ws;
-  a.counters = (int32_t*)p;
-  p += align256((64 + (size_t)a.max_num_seqs + 1) * sizeof(int32_t));
-  a.tiles = (int32_t*)p;
-  p += align256((size_t)cap * 16);
-  const int64_t nparts = (int64_t)a.max_num_seqs * kMlaMaxSplits;
-  a.part_ml = (float*)p;
-  p += align256((size_t)nparts * a.num_heads * 2 * sizeof(float));
-  a.part_acc = (uint16_t*)p;
-}
-
-hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
-  int ps_log2 = 0;
-  while ((1 << ps_log2) < a.page_size) ++ps_log2;
-  const int target = 2 * num_cus();
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(256), 0, stream, a, target);
-  const int grid = max(1, min(a.tile_capacity, num_cus()));
-  prof_begin(stream);
-  hipLaunchKernelGGL(mla_tile_kernel, dim3(grid), dim3(kMlaThreads), 0, stream, a, ps_log2);
-  prof_end(stream);
-  const int ygrid = (a.num_heads * 64 + 255) / 256;
-  hipLaunchKernelGGL(mla_merge_kernel, dim3(a.max_num_seqs, ygrid), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t stream) {
   if (a.top_k > kSpMaxUnits) return hipErrorInvalidValue;

@@ -132,6 +132,26 @@ rpa_status validate_values(const rpa_ragged_meta* m, const HostMeta& h, int page
   return RPA_OK;
 }
 
+// No two new tokens of the batch may name one cache slot [MLA v1 page:
+// update_kv_cache visits them in order, so the later one would win; here the
+// scatter is parallel and such input is rejected].
+rpa_status check_update_slots(const rpa_ragged_meta* meta, const HostMeta& h, int page_size) {
+  std::set<int64_t> seen;
+  for (int i = 0; i < h.ns; ++i) {
+    const int q_len = h.cu[i + 1] - h.cu[i];
+    for (int j = 0; j < q_len; ++j) {
+      const int pos = h.kv[i] - q_len + j;
+      const int64_t slot =
+          (int64_t)h.pages[(size_t)i * meta->pages_per_seq + pos / page_size] * page_size +
+          pos % page_size;
+      if (!seen.insert(slot).second)
+        return fail(RPA_E_INVALID, "sequence %d token %d: slot %lld written twice", i, j,
+                    (long long)slot);
+    }
+  }
+  return RPA_OK;
+}
+
 #define RPA_TRY(x)                 \
   do {                             \
     rpa_status _s = (x);           \
@@ -375,17 +395,7 @@ rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const voi
       RPA_TRY(validate_values(meta, h, page_size, total_num_pages));
       if (h.cu[h.ns] > num_tokens)
         return fail(RPA_E_INVALID, "total new tokens %d exceed num_tokens=%d", h.cu[h.ns], num_tokens);
-      for (int i = 0; i < h.ns; ++i) {
-        const int q_len = h.cu[i + 1] - h.cu[i];
-        for (int j = 0; j < q_len; ++j) {
-          const int pos = h.kv[i] - q_len + j;
-          const int64_t slot = (int64_t)h.pages[(size_t)i * meta->pages_per_seq + pos / page_size] *
-                                   page_size + pos % page_size;
-          if (!seen.insert(slot).second)
-            return fail(RPA_E_INVALID, "sequence %d token %d: slot %lld written twice", i, j,
-                        (long long)slot);
-        }
-      }
+      RPA_TRY(check_update_slots(meta, h, page_size));
     }
   }
   rpa::KvUpdateArgs a{};
@@ -418,8 +428,7 @@ size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, in
                               int32_t page_size) {
   (void)page_size;
   if (!meta || meta->max_num_seqs <= 0 || num_heads <= 0 || lkv_dim <= 0) return 0;
-  return rpa::mla_workspace_bytes(meta->max_num_seqs, meta->max_num_tokens, num_heads, lkv_dim,
-                                  nullptr, nullptr);
+  return rpa::mla_workspace_bytes(meta->max_num_seqs, meta->max_num_tokens, num_heads, lkv_dim);
 }
 
 rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* new_kv_c,
@@ -463,18 +472,16 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
     HostMeta h;
     RPA_TRY(fetch_meta(meta, true, stream, &h));
     RPA_TRY(validate_values(meta, h, page_size, total_num_pages));
-  }
-  if (new_kv_c) {
-    rpa_status st = kv_cache_update(RPA_LAYOUT_MLA_SPLIT, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe,
-                                    dtype, total_num_pages, page_size, 0, lkv_dim, r_dim,
-                                    kvc_stride, kpe_stride, meta->max_num_tokens, meta, nullptr, 0,
-                                    stream_);
-    if (st != RPA_OK) return st;
+    if (new_kv_c) RPA_TRY(check_update_slots(meta, h, page_size));
   }
   if (meta->max_num_tokens == 0) return ok();
+  // The step's new rows go to their cache slots inside the attention launch
+  // (no separate scatter launch).
   rpa::MlaArgs a{};
   a.ql_nope = ql_nope;
   a.q_pe = q_pe;
+  a.new_kv_c = new_kv_c;
+  a.new_k_pe = new_k_pe;
   a.cache_kv_c = cache_kv_c;
   a.cache_k_pe = cache_k_pe;
   a.out = out;

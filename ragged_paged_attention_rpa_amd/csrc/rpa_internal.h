@@ -105,11 +105,15 @@ bool gqa_prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group, i
 hipError_t launch_gqa_prefill(const GqaArgs& a, int ps_log2, int grid, hipStream_t stream);
 
 // ------------------------------------------------------------------- MLA ----
+constexpr int kMlaGrid = 256;  // workgroups of the MLA tile kernel (one share of keys each)
+
 struct MlaArgs {
   const void* ql_nope;
   const void* q_pe;
-  const void* cache_kv_c;
-  const void* cache_k_pe;
+  const void* new_kv_c;  // [max_num_tokens, lkv_dim] or NULL: the step's new rows, scattered
+  const void* new_k_pe;  // [max_num_tokens, r_dim]    into the caches inside the attention launch
+  void* cache_kv_c;
+  void* cache_k_pe;
   void* out;
   const int32_t* cu_q_lens;
   const int32_t* kv_lens;
@@ -120,16 +124,17 @@ struct MlaArgs {
   float score_scale;
   float soft_cap;
   int window;
-  int split_keys, max_splits;
   // workspace
-  int32_t* tiles;     // [capacity][4]
-  int32_t* counters;  // [0] count, [1] cursor
-  uint16_t* part_acc; // [capacity][num_heads][lkv_dim] bf16: acc / l of the split
-  float* part_ml;     // [capacity][num_heads][2]
-  int tile_capacity;
+  int32_t* counters;  // [0] pieces, [1] partial slots used
+  int32_t* wg_start;  // [kMlaGrid + 1] first piece of each workgroup's share
+  long long* kpre;    // [max_num_tokens] inclusive prefix of visible keys per token
+  int32_t* tok_slot;  // [head groups * max_num_tokens][2]: first partial slot (-1: whole), pieces
+  int32_t* pieces;    // [piece_capacity][8]: {seq, token, lo, hi}, {head group, slot, writes, share}
+  uint16_t* part_acc; // [slot_capacity][num_heads][lkv_dim] bf16: acc / l of the piece
+  float* part_ml;     // [slot_capacity][num_heads][2]
+  int piece_capacity, slot_capacity;
 };
-size_t mla_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_heads, int lkv_dim,
-                           int* tile_capacity, int* max_splits);
+size_t mla_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_heads, int lkv_dim);
 void mla_bind_workspace(MlaArgs& a, void* ws);
 hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 

@@ -175,3 +175,20 @@ def test_sparse_full_size_sampled():
     qs = np.arange(0, 4096, 97)
     want = _sparse_oracle(c, queries=qs)
     assert_close(got[qs], want[qs], *TOL, what="sparse_mla")
+
+
+def test_mla_page_window_refill_page1():
+    """Decode pieces spanning more than the 1024 page ids a workgroup caches in
+    LDS: at page size 1, 16 sequences of 20000 keys give shares of ~1250 keys,
+    so the page window refills inside a piece; the step's new rows go through
+    the fused scatter at the same time."""
+    _say("mla page-window refill (page size 1)")
+    c = wl.make_mla([(1, 20000 - 7 * i) for i in range(16)], num_heads=32, page_size=1,
+                    seed=230, device="cuda", name="page1-refill")
+    ckv, ckp = _host_caches_after_update(c)
+    got = _mla_gpu(c)
+    assert np.array_equal(storage(c.cache_kv_c)[0], ckv)
+    assert np.array_equal(storage(c.cache_k_pe)[0], ckp)
+    tokens = np.array([0, 5, 15])
+    want = _mla_oracle(c, ckv, ckp, tokens=tokens)
+    assert_close(as_f64(got)[tokens], want[tokens], *TOL, what="page1-refill")
