@@ -19,9 +19,12 @@
 //      O^T += V^T P^T is split by value dims (wave w: dims 128w .. 128w+127
 //      of all 128 heads, O^T in AGPRs), so one transposed V read feeds four
 //      MFMAs. Keys move through a four-stage LDS ring of 32-key blocks (36 KB
-//      each) filled by global_load_lds_dwordx4: three blocks are in flight
-//      while one is multiplied. Pieces that cover a whole token write the
-//      output; the others write (m, l, O / l) partials.
+//      each) filled by global_load_lds_dwordx4. The block loop is software
+//      pipelined: while the matrix cores multiply the scores of block j + 1,
+//      the softmax of block j runs between those MFMAs; then block j's
+//      weights are exchanged and its PV products added. Blocks j + 2 and
+//      j + 3 are in flight meanwhile. Pieces that cover a whole token write
+//      the output; the others write (m, l, O / l) partials.
 //   3. mla_merge_kernel  combines the partials of each token that was cut,
 //      with the rescaling algebra of the page's flash_attention.
 // When the call brings the step's new tokens (new_kv_c, new_k_pe), the keys
@@ -31,6 +34,8 @@
 // piece reads a slot that is being written.
 #include "rpa_device.h"
 #include "rpa_internal.h"
+
+#include <type_traits>
 
 namespace rpa {
 
@@ -321,6 +326,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Fixes where a value is computed: the empty asm uses it and may change it,
+// and volatile asm statements keep their order, so the work that produces it
+// stays between the MFMAs around this point instead of being sunk to its use.
+template <typename T>
+__device__ __forceinline__ void pin_here(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
 // ------------------------------------------------------------------ tile ----
 struct MlaSmem {
   char stage[kStages][kStageBytes];
@@ -448,10 +461,10 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
   const uint32_t st_base = lds_addr(sm.stage[0]);
   auto stage_addr = [&](int j) -> uint32_t { return st_base + (uint32_t)((j & (kStages - 1)) * kStageBytes); };
 
-  // Prologue: the first three stages' loads go out before the queries'.
+  // Prologue: the first two stages' loads go out before the queries'.
   {
 #pragma unroll 1
-    for (int j = 0; j < kStages - 1; ++j) {
+    for (int j = 0; j < kStages - 2; ++j) {
       if (j >= nst) break;
       uint64_t kvc, kpe;
       prep(j, &kvc, &kpe);
@@ -510,96 +523,143 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
     vhi = (uint32_t)(k_hi * kKvcBytes + ((x ^ swz(k_hi)) << 4) + 8 * (jj & 1));
   }
 
-#pragma unroll 1
-  for (int j = 0; j < nst; ++j) {
-    // Stage j landed once this wave's loads issued after it are all that is
-    // outstanding; the barrier then makes every wave's part visible and
-    // frees stage j - 1's buffer, which stage j + 3 now fills.
-    const int after = min(kStages - 2, nst - 1 - j);
-    if (after >= 2)
-      wait_vmcnt<2 * kDmaPerWave>();
-    else if (after == 1)
+  // Software pipeline over the stages: iteration j (from -1) multiplies
+  // S^T(j+1) = K Q^T on the matrix cores while the VALU runs the online
+  // softmax of stage j (its scores came out of the previous iteration) between
+  // those MFMAs, then hands P(j) to the other waves and adds V^T P^T(j).
+  // Stage buffers in use during iteration j: j (PV), j + 1 (QK), j + 2 (in
+  // flight), j + 3 (loads issued during the QK).
+  floatx16 sc, sn;  // S^T of stage j (being softmaxed) and of stage j + 1
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+
+  auto kread = [&](uint32_t stb, int st) -> u32x4 {
+    return st < 32 ? lds_read_b128(stb + xor_here(klat, (uint32_t)(st << 4)))
+                   : lds_read_b128(stb + xor_here(krope, (uint32_t)((st - 32) << 5)));
+  };
+
+  // MODE 0: QK only (j = -1); 1: QK + softmax of a stage inside [lo, hi);
+  // 2: QK + softmax of a stage that needs the key mask; 3: masked softmax
+  // only (the last stage). The softmax work is spread over the 36 k-steps:
+  // logits and the block max at steps 0..15, the reference update at 16, the
+  // weights at 17..32, their bf16 packing at 33.
+  auto qk_soft = [&](auto MODE, uint32_t qst, uint32_t nxt, bool more, uint64_t nkvc,
+                     uint64_t nkpe, int kb, u32x4 (&pb)[2], float& alpha, int& moved) {
+    constexpr int mode = decltype(MODE)::value;
+    constexpr bool do_qk = mode != 3, do_soft = mode != 0, full = mode == 1;
+    // Register r holds key kb + 8(r/4) + 4c + r%4; the window relative to
+    // this lane's register-0 key.
+    const int lo_r = lo - (kb + 4 * c), hi_r = hi - (kb + 4 * c);
+    float mblk = -INFINITY, mref = 0.f, psum = 0.f;
+    constexpr int kAheadK = 4;  // K reads run four k-steps ahead of their MFMAs
+    u32x4 kr[kAheadK];
+    if constexpr (do_qk) {
+#pragma unroll
+      for (int i = 0; i < kAheadK; ++i) kr[i] = kread(qst, i);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[r] = 0.f;
+    }
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      if constexpr (do_qk) {
+        u32x4 kf = kr[st % kAheadK];
+        pin_after(kf);
+        sn = mfma_32x32x16(as_bf16x8(kf), as_bf16x8(qv[st]), sn);
+        if (st + kAheadK < kSteps) kr[st % kAheadK] = kread(qst, st + kAheadK);
+        // Stage j + 3's loads go out together after the first MFMA: their
+        // addresses then die at once (spreading them keeps them live across
+        // the k-steps, which the register budget does not allow).
+        if (more && st == 0) {
+#pragma unroll
+          for (int k = 0; k < kDmaPerWave; ++k) dma(nxt, nkvc, nkpe, k);
+        }
+      }
+      if constexpr (do_soft) {
+        if (st < 16) {
+          float x = logit(sc[st]);
+          if constexpr (!full) {
+            const int off = 8 * (st >> 2) + (st & 3);
+            x = (off >= lo_r && off < hi_r) ? x : -INFINITY;
+          }
+          pin_here(x);
+          sc[st] = x;
+          mblk = fmaxf(mblk, x);
+        } else if (st == 16) {
+          // Lane l ^ 32 holds the other 16 keys of the same head.
+          mblk = wave_max_xor<32>(mblk);
+          const bool need = mblk > m_run + kLazyTau;
+          moved = __builtin_amdgcn_readfirstlane(wave_any(need) ? 1 : 0);
+          alpha = need ? fast_exp2(m_run - mblk) : 1.f;  // rows not moving keep scale 1
+          l_run *= alpha;
+          m_run = need ? mblk : m_run;
+          mref = m_run == -INFINITY ? 0.f : m_run;  // no visible key yet: weights 0
+          pin_here(mref);
+        } else if (st <= 32) {
+          const int r = st - 17;
+          float e = fast_exp2(sc[r] - mref);
+          pin_here(e);
+          sc[r] = e;
+          psum += e;
+        } else if (st == 33) {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pb[u][i] = pack_bf16x2(sc[8 * u + 2 * i], sc[8 * u + 2 * i + 1]);
+          pin_here(pb[0]);
+          pin_here(pb[1]);
+        }
+      }
+    }
+    if constexpr (do_soft) l_run += psum;
+  };
+
+  // Iteration -1 (S^T of stage 0 only), then iterations 0 .. nst - 1.
+  auto pre_stage = [&](int j, bool has_qk, bool& more, uint64_t& nkvc, uint64_t& nkpe) {
+    // Stage j + 1 landed once this wave's loads of stage j + 2 are all that
+    // is outstanding (the last iteration has none left). The barrier makes
+    // every wave's part visible, and every wave is past PV(j - 1): stage
+    // j - 1's buffer is free for stage j + 3, and the weights, scales and
+    // flags of j - 1 in LDS may be overwritten.
+    if (has_qk && j + 2 < nst)
       wait_vmcnt<kDmaPerWave>();
     else
       wait_vmcnt<0>();
     wg_barrier();
-    const bool more = j + kStages - 1 < nst;
-    uint64_t nkvc = 0, nkpe = 0;
+    more = j + kStages - 1 < nst;
+    nkvc = 0;
+    nkpe = 0;
     if (more) prep(j + kStages - 1, &nkvc, &nkpe);
-    const uint32_t cur = stage_addr(j);
-    const uint32_t nxt = stage_addr(j + kStages - 1);
-
-    const int kb = kb0 + j * kBlk;
-
-    // ---- S^T = K Q^T over 36 k-steps; K read two steps ahead; one DMA
-    // instruction of stage j + 3 after every fourth k-step.
-    floatx16 sv;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = 0.f;
-    auto kread = [&](int st) -> u32x4 {
-      return st < 32 ? lds_read_b128(cur + xor_here(klat, (uint32_t)(st << 4)))
-                     : lds_read_b128(cur + xor_here(krope, (uint32_t)((st - 32) << 5)));
-    };
-    // K reads run kAheadK k-steps ahead of their MFMAs (an LDS round trip takes
-    // several MFMAs). One accumulation chain: back-to-back MFMAs on the same
-    // accumulator issue at the full rate.
-    constexpr int kAheadK = 4;
-    u32x4 kr[kAheadK];
-#pragma unroll
-    for (int i = 0; i < kAheadK; ++i) kr[i] = kread(i);
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      u32x4 kf = kr[st % kAheadK];
-      pin_after(kf);
-      sv = mfma_32x32x16(as_bf16x8(kf), as_bf16x8(qv[st]), sv);
-      if (st + kAheadK < kSteps) kr[st % kAheadK] = kread(st + kAheadK);
-      if (more && (st & 3) == 3) dma(nxt, nkvc, nkpe, st >> 2);
-    }
-
-    // ---- online softmax for head 32*wave + lane%32 (lazy reference max, exp2
-    // domain). Register r holds key kb + 8(r/4) + 4c + r%4; the other 16 keys
-    // of the stage are in lane l ^ 32.
-    float mblk = -INFINITY;
-    if (kb >= lo && kb + kBlk <= hi) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = logit(sv[r]);
-        mblk = fmaxf(mblk, sv[r]);
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb + 8 * (r >> 2) + 4 * c + (r & 3);
-        sv[r] = (key >= lo && key < hi) ? logit(sv[r]) : -INFINITY;
-        mblk = fmaxf(mblk, sv[r]);
-      }
-    }
-    mblk = wave_max_xor<32>(mblk);
-    const bool need = mblk > m_run + kLazyTau;
-    const int moved = __builtin_amdgcn_readfirstlane(wave_any(need) ? 1 : 0);
-    float alpha = 1.f;
-    if (need) {
-      alpha = fast_exp2(m_run - mblk);  // rows not moving keep scale 1
-      l_run *= alpha;
-      m_run = mblk;
-    }
+  };
+  if (nst > 0) {
+    bool more;
+    uint64_t nkvc, nkpe;
+    pre_stage(-1, true, more, nkvc, nkpe);
     u32x4 pb[2];
-    if (m_run != -INFINITY) {
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sv[r] = fast_exp2(sv[r] - m_run);
-        psum += sv[r];
-      }
-      l_run += psum;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pb[u][i] = pack_bf16x2(sv[8 * u + 2 * i], sv[8 * u + 2 * i + 1]);
-    } else {
-      pb[0] = u32x4{0u, 0u, 0u, 0u};
-      pb[1] = u32x4{0u, 0u, 0u, 0u};
-    }
+    float alpha = 1.f;
+    int moved = 0;
+    qk_soft(std::integral_constant<int, 0>{}, stage_addr(0), stage_addr(kStages - 2), more, nkvc,
+            nkpe, kb0 - kBlk, pb, alpha, moved);
+    sc = sn;
+  }
+#pragma unroll 1
+  for (int j = 0; j < nst; ++j) {
+    const bool has_qk = j + 1 < nst;
+    bool more;
+    uint64_t nkvc, nkpe;
+    pre_stage(j, has_qk, more, nkvc, nkpe);
+    const uint32_t qst = stage_addr(j + 1);
+    const uint32_t nxt = stage_addr(j + kStages - 1);
+    const int kb = kb0 + j * kBlk;
+    u32x4 pb[2];
+    float alpha = 1.f;
+    int moved = 0;
+    if (!has_qk)
+      qk_soft(std::integral_constant<int, 3>{}, qst, nxt, more, nkvc, nkpe, kb, pb, alpha, moved);
+    else if (kb >= lo && kb + kBlk <= hi)
+      qk_soft(std::integral_constant<int, 1>{}, qst, nxt, more, nkvc, nkpe, kb, pb, alpha, moved);
+    else
+      qk_soft(std::integral_constant<int, 2>{}, qst, nxt, more, nkvc, nkpe, kb, pb, alpha, moved);
+
     // Hand the weights (and rescale factors) of this wave's heads to every
     // wave: they are the B operands of the PV products of head tile `wave`.
     sm.pex[wave][0][lane] = pb[0];
@@ -608,29 +668,11 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
     if (lane == 0) sm.rescale[wave] = moved;
     lds_barrier();
 
-    // ---- rescale the accumulators of head tiles whose reference moved (one
-    // LDS read of the four flags; the common case skips it all).
-    const int4 flags = *reinterpret_cast<const int4*>(sm.rescale);
-    const int rs_any = __builtin_amdgcn_readfirstlane(flags.x | flags.y | flags.z | flags.w);
-#pragma unroll
-    for (int h = 0; h < kWaves; ++h) {
-      const int rs_h = h == 0 ? flags.x : h == 1 ? flags.y : h == 2 ? flags.z : flags.w;
-      if (rs_any && __builtin_amdgcn_readfirstlane(rs_h)) {
-        const float al = sm.alpha[h][lane & 31];
-#pragma unroll
-        for (int d = 0; d < kDtPerWave; ++d) {
-          floatx16 x = acc_read(d * kWaves + h, acc[d][h]);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] *= al;
-          acc_write(acc[d][h], x);
-        }
-        mfma_agpr_fence();
-      }
-    }
-
-    // ---- O^T += V^T P^T for dims 128*wave .. +127 of all 128 heads: k-step u
-    // takes keys 16u + 4c + {0..3, 8..11}; each V^T operand feeds the four
-    // head tiles.
+    // ---- O^T += V^T P^T(j) for dims 128*wave .. +127 of all 128 heads: k-step
+    // u takes keys 16u + 4c + {0..3, 8..11}; each V^T operand feeds the four
+    // head tiles. The flags, the first weights and the first V^T operand are
+    // read together.
+    const uint32_t cur = stage_addr(j);
     auto vread = [&](int u, int d) -> u32x4 {
       const uint32_t b = cur + (uint32_t)(u * 16 * kKvcBytes);
       const uint32_t dsel = (uint32_t)((kDtPerWave * wave + d) << 6);
@@ -638,12 +680,39 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
       const u32x2 v1 = lds_read_tr16(b + xor_here(vhi, dsel));
       return u32x4{v0[0], v0[1], v1[0], v1[1]};
     };
+    const int4 flags = *reinterpret_cast<const int4*>(sm.rescale);
+    u32x4 pbh[kWaves];
+#pragma unroll
+    for (int h = 0; h < kWaves; ++h) pbh[h] = sm.pex[h][0][lane];
     u32x4 vf = vread(0, 0);
+
+    // ---- rescale the accumulators of head tiles whose reference moved (the
+    // common case skips it all).
+    const int rs_any = __builtin_amdgcn_readfirstlane(flags.x | flags.y | flags.z | flags.w);
+    if (rs_any) {
+#pragma unroll
+      for (int h = 0; h < kWaves; ++h) {
+        const int rs_h = h == 0 ? flags.x : h == 1 ? flags.y : h == 2 ? flags.z : flags.w;
+        if (__builtin_amdgcn_readfirstlane(rs_h)) {
+          const float al = sm.alpha[h][lane & 31];
+#pragma unroll
+          for (int d = 0; d < kDtPerWave; ++d) {
+            floatx16 x = acc_read(d * kWaves + h, acc[d][h]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] *= al;
+            acc_write(acc[d][h], x);
+          }
+          mfma_agpr_fence();
+        }
+      }
+    }
+
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      u32x4 pbh[kWaves];
+      if (u == 1) {
 #pragma unroll
-      for (int h = 0; h < kWaves; ++h) pbh[h] = sm.pex[h][u][lane];
+        for (int h = 0; h < kWaves; ++h) pbh[h] = sm.pex[h][1][lane];
+      }
 #pragma unroll
       for (int d = 0; d < kDtPerWave; ++d) {
         const int n = u * kDtPerWave + d + 1;
@@ -655,6 +724,7 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
         vf = vn;
       }
     }
+    sc = sn;
   }
 
   // ---- end of piece: every wave needs the row sums of all 128 heads.
