@@ -70,7 +70,9 @@ def _load():
         lib.oracle_sparse_mla.argtypes = [c_void_p, c_int, c_int, c_int, c_int, c_int,
                                           c_void_p, c_int, c_int, c_int,
                                           c_void_p, c_int, c_void_p, c_int, c_int,
-                                          c_void_p, c_int, c_double, c_void_p, c_int, c_void_p]
+                                          c_void_p, c_int, c_double,
+                                          c_void_p, c_void_p, c_void_p, c_int,
+                                          c_void_p, c_int, c_void_p]
         lib.oracle_kv_update.restype = c_int
         lib.oracle_kv_update.argtypes = [c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                          c_int, c_int, c_int, c_int, c_int, c_int, c_int,
@@ -183,13 +185,19 @@ def mla(ql_nope, q_pe, dtype, cache_kv_c, cache_k_pe, kv_lens, page_indices, cu_
     return out
 
 
-def sparse_mla(q, dtype, kv_cache, page_table, indices, positions, *, seq_len, read_block,
-               sm_scale, dv=512, queries=None):
-    """Sparse MLA-latent attention, paged single-sequence mode
-    [Sparse page: sparse_mla_attention / _sparse_mla_kernel_chunked_hminor].
+def sparse_mla(q, dtype, kv_cache, page_table, indices, positions, *, seq_len=0, read_block,
+               sm_scale, dv=512, queries=None, cu_q_lens=None, seq_lens=None, cu_kv_lens=None):
+    """Sparse MLA-latent attention, paged single-sequence or packed-ragged mode
+    [Sparse page: sparse_mla_attention / _sparse_mla_kernel_chunked_hminor;
+    prefill_write_and_attend_ragged].
 
     q [S, H, Dk]; kv_cache [P, ps, C] fused latent pool; page_table [PTW];
     indices [S, K] unit ids (-1 = padding); positions [S].
+    Single-sequence mode: causal bound seq_len, page_table indexed from 0.
+    Ragged mode (cu_q_lens [R+1], seq_lens [R], cu_kv_lens [R+1] given): token s
+    belongs to request rid = min(searchsorted(cu_q_lens[1:], s, 'right'), R-1),
+    is bounded by seq_lens[rid], and its unit ids index page_table from
+    cu_kv_lens[rid] // page_size.
     Returns fp64 [S, H, dv]; an empty key set gives zeros.
     """
     q = _storage(q, dtype)
@@ -200,10 +208,17 @@ def sparse_mla(q, dtype, kv_cache, page_table, indices, positions, *, seq_len, r
     idx = _c(indices, np.int32)
     pos = _c(positions, np.int32)
     ql = None if queries is None else _c(queries, np.int32)
+    ragged = cu_q_lens is not None
+    if ragged and (seq_lens is None or cu_kv_lens is None):
+        raise ValueError("ragged mode needs cu_q_lens, seq_lens and cu_kv_lens")
+    cq = _c(cu_q_lens, np.int32) if ragged else None
+    sl = _c(seq_lens, np.int32) if ragged else None
+    ck = _c(cu_kv_lens, np.int32) if ragged else None
     out = np.full((S, H, dv), np.nan, dtype=np.float64)
     rc = _load().oracle_sparse_mla(
         _ptr(q), dtype, S, H, Dk, dv, _ptr(kv_cache), P, ps, C, _ptr(pt), pt.size,
         _ptr(idx), idx.shape[1], int(read_block), _ptr(pos), int(seq_len), float(sm_scale),
+        _ptr(cq), _ptr(sl), _ptr(ck), 0 if not ragged else sl.size,
         _ptr(ql), 0 if ql is None else ql.size, _ptr(out))
     _check(rc, "sparse_mla")
     return out

@@ -283,7 +283,8 @@ int oracle_mla(const void* ql_nope, const void* q_pe, int dtype, int num_tokens,
 /*
  * Sparse MLA-latent attention over a fused paged latent pool
  * [Sparse page: _sparse_mla_kernel_chunked_hminor, validity bias and online
- *  softmax; sparse_mla_attention, paged single-sequence mode].
+ *  softmax; sparse_mla_attention, paged single-sequence and packed-ragged
+ *  modes; prefill_write_and_attend_ragged for the token -> request map].
  *
  * q        [S, H, dk]  (dk = dv + rope, e.g. 512 + 64)
  * kv_cache [total_num_pages, page_size, cache_dim]; token (page P, offset o)
@@ -296,14 +297,25 @@ int oracle_mla(const void* ql_nope, const void* q_pe, int dtype, int num_tokens,
  *            u*RB + r <= positions[s], u*RB + r < seq_len };
  *          duplicate units count once per occurrence.
  * out [S, H, dv] fp64; an empty key set gives zeros.
+ *
+ * Packed-ragged mode (cu_q_lens != NULL): the S queries are the packed tokens
+ * of num_seqs requests. Token s belongs to request
+ *   rid = min(#{ j in 1..num_seqs : cu_q_lens[j] <= s }, num_seqs - 1)
+ * (a right-sided search of s in cu_q_lens[1:], clipped), its causal bound is
+ * seq_lens[rid] in place of seq_len, and its unit ids are local to the
+ * request: logical page lp is page_table[cu_kv_lens[rid] / page_size + lp],
+ * page_table being the packed table of ptw entries.
  */
 int oracle_sparse_mla(const void* q, int dtype, int S, int H, int dk, int dv,
                       const void* kv_cache, int total_num_pages, int page_size, int cache_dim,
                       const int32_t* page_table, int ptw, const int32_t* indices, int K,
                       int read_block, const int32_t* positions, int seq_len, double sm_scale,
+                      const int32_t* cu_q_lens, const int32_t* seq_lens,
+                      const int32_t* cu_kv_lens, int num_seqs,
                       const int32_t* query_list, int n_list, double* out) {
   if (read_block <= 0 || page_size % read_block != 0) return -1;
   if (dk > cache_dim || dv > dk) return -1;
+  if (cu_q_lens && (num_seqs <= 0 || !seq_lens || !cu_kv_lens)) return -1;
   const int n_q = query_list ? n_list : S;
   const int64_t max_keys = (int64_t)K * read_block;
   int bad = 0;
@@ -312,6 +324,14 @@ int oracle_sparse_mla(const void* q, int dtype, int S, int H, int dk, int dv,
     for (int h = 0; h < H; ++h) {
       const int si = query_list ? query_list[a] : a;
       const int64_t qpos = positions[si];
+      int64_t kv_bound = seq_len, table_base = 0;
+      if (cu_q_lens) {
+        int rid = 0;
+        for (int j = 1; j <= num_seqs; ++j) rid += cu_q_lens[j] <= si;
+        if (rid > num_seqs - 1) rid = num_seqs - 1;
+        kv_bound = seq_lens[rid];
+        table_base = cu_kv_lens[rid] / page_size;
+      }
       double* s = (double*)malloc(sizeof(double) * (size_t)(max_keys > 0 ? max_keys : 1));
       double* w = (double*)malloc(sizeof(double) * (size_t)(max_keys > 0 ? max_keys : 1));
       int64_t* key_row = (int64_t*)malloc(sizeof(int64_t) * (size_t)(max_keys > 0 ? max_keys : 1));
@@ -322,8 +342,8 @@ int oracle_sparse_mla(const void* q, int dtype, int S, int H, int dk, int dv,
         if (u < 0) continue;
         for (int r = 0; r < read_block; ++r) {
           const int64_t kp = (int64_t)u * read_block + r; /* logical token */
-          if (kp > qpos || kp >= seq_len) continue;
-          const int64_t lp = kp / page_size;
+          if (kp > qpos || kp >= kv_bound) continue;
+          const int64_t lp = table_base + kp / page_size;
           if (lp >= ptw) {
 #pragma omp atomic write
             bad = 1;

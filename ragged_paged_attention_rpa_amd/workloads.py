@@ -306,6 +306,67 @@ def make_sparse(*, T, S, H, K, page_size=64, read_block=64, dtype=torch.bfloat16
                       rope_dim=rope_dim)
 
 
+@dataclass
+class SparseRaggedCase:
+    """Packed tokens of several requests over one fused paged latent pool
+    (the sparse page's packed-ragged mode)."""
+    name: str
+    q: torch.Tensor            # [T, H, Dk] packed tokens (T may exceed cu_q_lens[-1]: padding)
+    kv_cache: torch.Tensor     # [P, ps, pad_cols]
+    page_indices: np.ndarray   # int32 [PTW] packed physical pages, request r's from cu_kv_lens[r]//ps
+    indices: np.ndarray        # int32 [T, K] request-local unit ids (-1 = padding)
+    positions: np.ndarray      # int32 [T]
+    cu_q_lens: np.ndarray      # int32 [R+1]
+    seq_lens: np.ndarray       # int32 [R]
+    cu_kv_lens: np.ndarray     # int32 [R+1] page-aligned
+    read_block: int
+    sm_scale: float
+    kv_lora_rank: int = 512
+    rope_dim: int = 64
+
+    @property
+    def page_size(self):
+        return self.kv_cache.shape[1]
+
+
+def make_sparse_ragged(*, seq_lens, q_lens, H, K, page_size=64, read_block=64,
+                       dtype=torch.bfloat16, seed=0, device="cpu", kv_lora_rank=512, rope_dim=64,
+                       pad_cols=640, pad_tokens=0, spare_pages=3, pad_frac=0.0,
+                       name="sparse_ragged"):
+    """Requests r = 0..R-1 with kv length seq_lens[r] whose last q_lens[r]
+    tokens are queries (positions seq_lens[r] - q_lens[r] .. seq_lens[r] - 1),
+    packed in request order, then pad_tokens extra tokens (positions of the
+    last request's last token). Each request owns ceil(seq_len / ps) pages of
+    the packed table, at page-aligned offsets cu_kv_lens; the physical pages
+    are a random permutation of the pool (plus spare_pages never referenced)."""
+    rng = np.random.default_rng(seed)
+    gen = _gen(device, seed)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    q_lens = np.asarray(q_lens, dtype=np.int32)
+    R = len(seq_lens)
+    dk = kv_lora_rank + rope_dim
+    pages = np.array([cdiv(int(L), page_size) for L in seq_lens], dtype=np.int64)
+    cu_kv_lens = np.zeros(R + 1, dtype=np.int32)
+    cu_kv_lens[1:] = np.cumsum(pages * page_size)
+    n_pages = int(pages.sum()) + spare_pages
+    page_indices = rng.permutation(n_pages)[: int(pages.sum())].astype(np.int32)
+    cu_q_lens = np.zeros(R + 1, dtype=np.int32)
+    cu_q_lens[1:] = np.cumsum(q_lens)
+    positions = np.concatenate(
+        [np.arange(L - ql, L, dtype=np.int32) for L, ql in zip(seq_lens, q_lens)]
+        + [np.full(pad_tokens, seq_lens[-1] - 1, dtype=np.int32)])
+    T = len(positions)
+    indices = sample_units(rng, positions, K, read_block, pad_frac)
+    q = randn((T, H, dk), dtype, gen, device)
+    kv = torch.zeros((n_pages, page_size, pad_cols), dtype=dtype, device=device)
+    kv[:, :, :dk] = randn((n_pages, page_size, dk), dtype, gen, device)
+    return SparseRaggedCase(name=name, q=q, kv_cache=kv, page_indices=page_indices,
+                            indices=indices, positions=positions, cu_q_lens=cu_q_lens,
+                            seq_lens=seq_lens, cu_kv_lens=cu_kv_lens, read_block=read_block,
+                            sm_scale=1.0 / math.sqrt(192), kv_lora_rank=kv_lora_rank,
+                            rope_dim=rope_dim)
+
+
 def sparse_mla(device="cpu", seed=1005):
     """T=65536 latent tokens, 4096 queries at T-4096..T-1, 16 heads,
     K=32 distinct causal units of 64 tokens (page-level selection)."""

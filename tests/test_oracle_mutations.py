@@ -57,8 +57,12 @@ MUTATIONS = [
     ("mla_value_column_shift", "o[d] += w[k] * load_elem(cache_kv_c, dtype, key_row[k] * kvc_stride + d);",
      "o[d] += w[k] * load_elem(cache_kv_c, dtype, key_row[k] * kvc_stride + d + 1);", None),
     ("mla_fused_rope_column_ignored", "row * kpe_stride + kpe_col + d", "row * kpe_stride + d", None),
-    ("sparse_seq_len_dropped", "if (kp > qpos || kp >= seq_len) continue;", "if (kp > qpos) continue;", None),
-    ("sparse_causal_dropped", "if (kp > qpos || kp >= seq_len) continue;", "if (kp >= seq_len) continue;", None),
+    ("sparse_seq_len_dropped", "if (kp > qpos || kp >= kv_bound) continue;", "if (kp > qpos) continue;", None),
+    ("sparse_causal_dropped", "if (kp > qpos || kp >= kv_bound) continue;", "if (kp >= kv_bound) continue;", None),
+    ("sparse_ragged_request_search_left", "rid += cu_q_lens[j] <= si;", "rid += cu_q_lens[j] < si;", None),
+    ("sparse_ragged_bound_not_per_request", "kv_bound = seq_lens[rid];", "kv_bound = seq_lens[0];", None),
+    ("sparse_ragged_table_base_dropped", "table_base = cu_kv_lens[rid] / page_size;", "table_base = 0;", None),
+    ("sparse_ragged_no_clip", "if (rid > num_seqs - 1) rid = num_seqs - 1;", "if (rid > num_seqs) rid = num_seqs;", None),
     ("sparse_padding_as_unit0", "if (u < 0) continue;", "if (u < -1) continue;", None),
     ("sparse_row_mod_read_block", "(int64_t)page * page_size + kp % page_size;",
      "(int64_t)page * page_size + kp % read_block;", None),

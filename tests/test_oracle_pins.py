@@ -407,6 +407,132 @@ def test_sparse_empty_selection_gives_zero_and_padding_is_ignored():
     assert np.array_equal(a[1], b[1])
 
 
+def _sparse_ragged(seed=60, seq_lens=(200, 75, 130), q_lens=(5, 1, 3), K=6, RB=16, ps=32, H=3,
+                   pad_tokens=0, pad_frac=0.3):
+    return wl.make_sparse_ragged(seq_lens=list(seq_lens), q_lens=list(q_lens), H=H, K=K,
+                                 page_size=ps, read_block=RB, dtype=torch.float32, seed=seed,
+                                 kv_lora_rank=32, rope_dim=8, pad_cols=48, pad_tokens=pad_tokens,
+                                 pad_frac=pad_frac)
+
+
+def _sparse_one_request(c, q, d, kv, r, rows):
+    """The single-sequence call for request r on the given packed rows: its own
+    page-table slice, its own kv length as the causal bound."""
+    ps = c.page_size
+    base = int(c.cu_kv_lens[r]) // ps
+    npg = (int(c.cu_kv_lens[r + 1]) - int(c.cu_kv_lens[r])) // ps
+    table = c.page_indices[base:base + npg].copy()
+    return oracle.sparse_mla(q[rows], d, kv, table, c.indices[rows], c.positions[rows],
+                             seq_len=int(c.seq_lens[r]), read_block=c.read_block,
+                             sm_scale=c.sm_scale, dv=32)
+
+
+def test_sparse_ragged_equals_each_request_alone():
+    """Packed-ragged mode [Sparse page: prefill_write_and_attend_ragged,
+    sparse_mla_attention ragged branch]: every token gives what the
+    single-sequence call of its own request gives (its pages, its bound),
+    bit for bit; one request has a single token (decode, S == 1)."""
+    c = _sparse_ragged()
+    q, d = storage(c.q)
+    kv, _ = storage(c.kv_cache)
+    got = oracle.sparse_mla(q, d, kv, c.page_indices, c.indices, c.positions, read_block=c.read_block,
+                            sm_scale=c.sm_scale, dv=32, cu_q_lens=c.cu_q_lens, seq_lens=c.seq_lens,
+                            cu_kv_lens=c.cu_kv_lens)
+    for r in range(len(c.seq_lens)):
+        rows = np.arange(c.cu_q_lens[r], c.cu_q_lens[r + 1])
+        want = _sparse_one_request(c, q, d, kv, r, rows)
+        assert np.array_equal(got[rows], want), r
+
+
+def test_sparse_ragged_bound_is_per_request():
+    """The causal bound of a token is its own request's kv length: with query
+    positions pushed past every request's length, keys stop at seq_lens[rid]
+    (the single-sequence call with that request's length as seq_len)."""
+    c = _sparse_ragged(seed=64, seq_lens=(200, 75, 130), q_lens=(3, 2, 2), K=8, pad_frac=0.0)
+    q, d = storage(c.q)
+    kv, _ = storage(c.kv_cache)
+    pos = c.positions.copy()
+    for r in range(len(c.seq_lens)):
+        pos[c.cu_q_lens[r]:c.cu_q_lens[r + 1]] = int(c.seq_lens[r]) + 40
+    idx = np.full_like(c.indices, -1)
+    for t in range(q.shape[0]):
+        r = int(np.searchsorted(c.cu_q_lens[1:], t, side="right"))
+        n = -(-int(c.seq_lens[r]) // 16)
+        idx[t, :min(8, n)] = np.arange(max(0, n - 8), n)
+    got = oracle.sparse_mla(q, d, kv, c.page_indices, idx, pos, read_block=16, sm_scale=c.sm_scale,
+                            dv=32, cu_q_lens=c.cu_q_lens, seq_lens=c.seq_lens, cu_kv_lens=c.cu_kv_lens)
+    for r in range(len(c.seq_lens)):
+        rows = np.arange(c.cu_q_lens[r], c.cu_q_lens[r + 1])
+        ps = c.page_size
+        base = int(c.cu_kv_lens[r]) // ps
+        npg = (int(c.cu_kv_lens[r + 1]) - int(c.cu_kv_lens[r])) // ps
+        want = oracle.sparse_mla(q[rows], d, kv, c.page_indices[base:base + npg].copy(), idx[rows],
+                                 pos[rows], seq_len=int(c.seq_lens[r]), read_block=16,
+                                 sm_scale=c.sm_scale, dv=32)
+        assert np.array_equal(got[rows], want), r
+        # the last unit is cut at the request's length, so the bound is engaged
+        assert int(c.seq_lens[r]) % 16 != 0
+
+
+def test_sparse_ragged_all_causal_units_equals_dense_causal_mla():
+    """Selecting every causal unit of its request turns each token's sparse
+    attention into dense causal MLA over that request's first position + 1
+    tokens, read through the request's own window of the packed table."""
+    c = _sparse_ragged(seed=61, seq_lens=(96, 160, 40), q_lens=(2, 3, 1), K=16, RB=16, pad_frac=0.0)
+    q, d = storage(c.q)
+    kv, _ = storage(c.kv_cache)
+    T = q.shape[0]
+    idx = np.full((T, 16), -1, np.int32)
+    for t in range(T):
+        n = int(c.positions[t]) // 16 + 1
+        idx[t, :n] = np.arange(n)
+    got = oracle.sparse_mla(q, d, kv, c.page_indices, idx, c.positions, read_block=16,
+                            sm_scale=c.sm_scale, dv=32, cu_q_lens=c.cu_q_lens, seq_lens=c.seq_lens,
+                            cu_kv_lens=c.cu_kv_lens)
+    ps = c.page_size
+    for r in range(len(c.seq_lens)):
+        base = int(c.cu_kv_lens[r]) // ps
+        npg = (int(c.cu_kv_lens[r + 1]) - int(c.cu_kv_lens[r])) // ps
+        table = c.page_indices[base:base + npg].reshape(1, npg).copy()
+        for t in range(c.cu_q_lens[r], c.cu_q_lens[r + 1]):
+            L = int(c.positions[t]) + 1
+            dense = oracle.mla(q[t:t + 1, :, :32].copy(), q[t:t + 1, :, 32:40].copy(), d, kv, None,
+                               [L], table, [0, 1], 1, sm_scale=c.sm_scale, fused=True)
+            np.testing.assert_allclose(got[t], dense[0], atol=1e-12)
+
+
+def test_sparse_ragged_padding_tokens_belong_to_the_last_request():
+    """Tokens past cu_q_lens[R] map to request R - 1 (the page's right-sided
+    search clipped to the last request). The per-request arrays are views of
+    longer buffers, so a missing clip would read the sentinel entries."""
+    c = _sparse_ragged(seed=62, pad_tokens=3)
+    q, d = storage(c.q)
+    kv, _ = storage(c.kv_cache)
+    R = len(c.seq_lens)
+    sl_buf = np.concatenate([c.seq_lens, [0]]).astype(np.int32)
+    got = oracle.sparse_mla(q, d, kv, c.page_indices, c.indices, c.positions, read_block=c.read_block,
+                            sm_scale=c.sm_scale, dv=32, cu_q_lens=c.cu_q_lens,
+                            seq_lens=sl_buf[:R], cu_kv_lens=c.cu_kv_lens)
+    pad_rows = np.arange(c.cu_q_lens[R], q.shape[0])
+    assert len(pad_rows) == 3
+    want = _sparse_one_request(c, q, d, kv, R - 1, pad_rows)
+    assert np.array_equal(got[pad_rows], want)
+    assert np.abs(want).sum() > 0
+
+
+def test_sparse_ragged_single_request_is_the_single_sequence_mode():
+    c = _sparse_small(seed=63, pad_frac=0.3)
+    q, d = storage(c.q)
+    kv, _ = storage(c.kv_cache)
+    S = q.shape[0]
+    a = oracle.sparse_mla(q, d, kv, c.page_table, c.indices, c.positions, seq_len=c.seq_len,
+                          read_block=c.read_block, sm_scale=c.sm_scale, dv=32)
+    b = oracle.sparse_mla(q, d, kv, c.page_table, c.indices, c.positions, read_block=c.read_block,
+                          sm_scale=c.sm_scale, dv=32, cu_q_lens=[0, S], seq_lens=[c.seq_len],
+                          cu_kv_lens=[0, len(c.page_table) * c.page_size])
+    assert np.array_equal(a, b)
+
+
 # -------------------------------------------------------------- kv update --
 
 def test_kv_update_combined_gqa_by_direct_assignment():
