@@ -304,6 +304,40 @@ rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t
                               int32_t rope_dim, float sm_scale, float* out, void* workspace,
                               size_t workspace_bytes, rpa_stream_t stream);
 
+/*
+ * Sparse MLA-latent attention, packed-ragged mode: the tokens of num_seqs
+ * requests packed along one axis, as the dense MLA path and the indexer lay
+ * them out [Sparse page: prefill_write_and_attend_ragged, sparse_mla_attention
+ * ragged branch]. One launch covers prefill chunks and decodes (a request
+ * with one token is the S == 1 case).
+ *   q          [num_tokens, num_heads, 576] (BF16), out [num_tokens, num_heads, 512] FP32.
+ *   kv_cache   [total_num_pages, page_size, cache_dim] (BF16), as in sparse_mla_forward.
+ *   page_indices [ptw]: the packed physical page list; request r's logical
+ *              page lp is page_indices[cu_kv_lens[r] / page_size + lp].
+ *   indices    [num_tokens, top_k] request-local unit ids (-1 = padding).
+ *   positions  [num_tokens] absolute query positions (causal bound).
+ *   cu_q_lens  [num_seqs + 1] non-decreasing token offsets; token t belongs to
+ *              request min(#{j in 1..num_seqs : cu_q_lens[j] <= t}, num_seqs - 1),
+ *              so tokens past cu_q_lens[num_seqs] count as the last request's.
+ *   seq_lens   [num_seqs] per-request kv length (keys at or past it are masked).
+ *   cu_kv_lens [num_seqs + 1] page-aligned kv offsets into page_indices.
+ * All arrays are device memory owned by the caller; num_seqs is a host value.
+ * Key set, duplicates and empty sets as in sparse_mla_forward; a logical page
+ * outside page_indices (index < 0 or >= ptw) or a physical page outside the
+ * pool is masked. No workspace. Same shape limits as sparse_mla_forward;
+ * RPA_E_SHAPE if num_seqs <= 0.
+ */
+rpa_status sparse_mla_forward_ragged(const void* q, const void* kv_cache,
+                                     const int32_t* page_indices, int32_t ptw,
+                                     const int32_t* indices, const int32_t* positions,
+                                     const int32_t* cu_q_lens, const int32_t* seq_lens,
+                                     const int32_t* cu_kv_lens, int32_t num_seqs,
+                                     int32_t num_tokens, int32_t num_heads, int32_t top_k,
+                                     int32_t read_block, int32_t page_size,
+                                     int32_t total_num_pages, int32_t cache_dim,
+                                     int32_t kv_lora_rank, int32_t rope_dim, float sm_scale,
+                                     float* out, rpa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -344,7 +344,7 @@ int oracle_sparse_mla(const void* q, int dtype, int S, int H, int dk, int dv,
           const int64_t kp = (int64_t)u * read_block + r; /* logical token */
           if (kp > qpos || kp >= kv_bound) continue;
           const int64_t lp = table_base + kp / page_size;
-          if (lp >= ptw) {
+          if (lp < 0 || lp >= ptw) {
 #pragma omp atomic write
             bad = 1;
             continue;

@@ -19,6 +19,7 @@ import ctypes
 import os
 
 __all__ = ["rpa_forward", "kv_cache_update", "mla_rpa_forward", "sparse_mla_forward",
+           "sparse_mla_forward_ragged",
            "rpa_workspace_size", "mla_rpa_workspace_size", "sparse_mla_workspace_size",
            "RpaError", "RpaLibraryMissing", "library_path", "load_library",
            "LAYOUT_COMBINED_GQA", "LAYOUT_MLA_SPLIT", "LAYOUT_MLA_FUSED", "EXPORTED_SYMBOLS"]
@@ -32,7 +33,8 @@ EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_last_path", "rpa_set
                     "rpa_workspace_size", "rpa_forward", "rpa_forward_noalloc",
                     "rpa_noalloc_scratch_bytes",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
-                    "sparse_mla_workspace_size", "sparse_mla_forward")
+                    "sparse_mla_workspace_size", "sparse_mla_forward",
+                    "sparse_mla_forward_ragged")
 
 
 class RpaLibraryMissing(RuntimeError):
@@ -107,6 +109,9 @@ def load_library():
     lib.sparse_mla_forward.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
                                        I32, I32, F32, P, P, SZ, P]
     lib.sparse_mla_forward.restype = I32
+    lib.sparse_mla_forward_ragged.argtypes = [P, P, P, I32, P, P, P, P, P, I32, I32, I32, I32, I32,
+                                              I32, I32, I32, I32, I32, F32, P, P]
+    lib.sparse_mla_forward_ragged.restype = I32
     _lib = lib
     return lib
 
@@ -374,5 +379,37 @@ def sparse_mla_forward(q, kv_cache, page_table, indices, positions, *, seq_len, 
                                 int(read_block), ps, P, C, page_table.numel(), kv_lora_rank,
                                 rope_dim, float(sm_scale), _ptr(out), _ptr(workspace),
                                 0 if workspace is None else workspace.numel(), _stream(stream))
+    _raise(lib, st)
+    return out
+
+
+def sparse_mla_forward_ragged(q, kv_cache, page_indices, indices, positions, cu_q_lens, seq_lens,
+                              cu_kv_lens, *, read_block, sm_scale, kv_lora_rank=512, rope_dim=64,
+                              out=None, stream=None):
+    """Sparse MLA-latent attention over packed tokens of several requests.
+
+    q [T, H, 576] bf16; kv_cache [P, ps, C] bf16; page_indices [PTW] packed page
+    list; indices [T, K] request-local unit ids (-1 = padding); positions [T];
+    cu_q_lens [R+1]; seq_lens [R]; cu_kv_lens [R+1] (all int32, on the device).
+    Returns out [T, H, 512] fp32.
+    """
+    torch = _torch()
+    lib = load_library()
+    _check_dev(q, kv_cache, page_indices, indices, positions, cu_q_lens, seq_lens, cu_kv_lens, out)
+    T, H, Dk = q.shape
+    if Dk != kv_lora_rank + rope_dim:
+        raise ValueError("q last dim must be kv_lora_rank + rope_dim")
+    P, ps, C = kv_cache.shape
+    K = indices.shape[1]
+    R = seq_lens.numel()
+    if cu_q_lens.numel() != R + 1 or cu_kv_lens.numel() != R + 1:
+        raise ValueError("cu_q_lens and cu_kv_lens need len(seq_lens) + 1 entries")
+    if out is None:
+        out = torch.empty((T, H, kv_lora_rank), dtype=torch.float32, device=q.device)
+    st = lib.sparse_mla_forward_ragged(
+        _ptr(q), _ptr(kv_cache), _ptr(_i32(page_indices)), page_indices.numel(), _ptr(_i32(indices)),
+        _ptr(_i32(positions)), _ptr(_i32(cu_q_lens)), _ptr(_i32(seq_lens)), _ptr(_i32(cu_kv_lens)), R,
+        T, H, K, int(read_block), ps, P, C, kv_lora_rank, rope_dim, float(sm_scale), _ptr(out),
+        _stream(stream))
     _raise(lib, st)
     return out

@@ -210,6 +210,26 @@ sparse_mla_kernel(SparseArgs a) {
   const int RB = a.read_block;
   const int ps = a.page_size;
 
+  // Causal bound and page-table base of this query: the call's seq_len and 0
+  // for one sequence; for packed requests those of request rid, the number
+  // of cu_q_lens[1..num_seqs] at or below qi clipped to the last request
+  // [Sparse page: prefill_write_and_attend_ragged, sparse_mla_attention].
+  int kv_bound = a.seq_len;
+  int64_t tbase = 0;
+  if (a.cu_q_lens != nullptr) {
+    int lo = 0, hi = a.num_seqs;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cu_q_lens[mid + 1] <= qi)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    const int rid = min(lo, a.num_seqs - 1);
+    kv_bound = a.seq_lens[rid];
+    tbase = a.cu_kv_lens[rid] / ps;
+  }
+
   // Unit table: physical first row of each selected unit (-1 = padding or
   // outside the page table) [Sparse page: _src, paged branch].
   for (int k = tid; k < K; k += kSpThreads) {
@@ -218,8 +238,9 @@ sparse_mla_kernel(SparseArgs a) {
     if (u >= 0) {
       const int64_t lt = (int64_t)u * RB;
       const int64_t lp = lt / ps;
-      if (lp < a.ptw) {
-        const int phys = a.page_table[lp];
+      const int64_t li = tbase + lp;
+      if (li >= 0 && li < a.ptw) {
+        const int phys = a.page_table[li];
         if (phys >= 0 && phys < a.total_num_pages) row = phys * ps + (int)(lt - lp * ps);
       }
     }
@@ -261,7 +282,7 @@ sparse_mla_kernel(SparseArgs a) {
         const int r = kk - unit * RB;
         const int base = sm.unit_row[unit];
         const int kp = sm.unit_id[unit] * RB + r;
-        if (base >= 0 && kp <= pos && kp < a.seq_len) row = base + r;
+        if (base >= 0 && kp <= pos && kp < kv_bound) row = base + r;
       }
       rows[gi] = row;
       vmask[gi] = __builtin_amdgcn_ballot_w64(row >= 0);

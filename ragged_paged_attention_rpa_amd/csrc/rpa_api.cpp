@@ -516,18 +516,20 @@ size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t
   return 0;
 }
 
-rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t* page_table,
-                              const int32_t* indices, const int32_t* positions, int32_t seq_len,
-                              int32_t num_queries, int32_t num_heads, int32_t top_k,
-                              int32_t read_block, int32_t page_size, int32_t total_num_pages,
-                              int32_t cache_dim, int32_t ptw, int32_t kv_lora_rank,
-                              int32_t rope_dim, float sm_scale, float* out, void* workspace,
-                              size_t workspace_bytes, rpa_stream_t stream_) {
-  (void)workspace;
-  (void)workspace_bytes;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both sparse entry points; fills everything but the
+// single-sequence / ragged fields.
+rpa_status sparse_prepare(rpa::SparseArgs& a, const void* q, const void* kv_cache,
+                          const int32_t* page_table, const int32_t* indices,
+                          const int32_t* positions, int32_t num_queries, int32_t num_heads,
+                          int32_t top_k, int32_t read_block, int32_t page_size,
+                          int32_t total_num_pages, int32_t cache_dim, int32_t ptw,
+                          int32_t kv_lora_rank, int32_t rope_dim, float sm_scale, float* out) {
   if (!q || !kv_cache || !page_table || !indices || !positions || !out)
-    return fail(RPA_E_INVALID, "q, kv_cache, page_table, indices, positions and out must be non-NULL");
+    return fail(RPA_E_INVALID, "q, kv_cache, page table, indices, positions and out must be non-NULL");
   // sm_scale has no safe default [Sparse page: sparse_mla_attention].
   if (!(sm_scale > 0.0f) || !std::isfinite(sm_scale))
     return fail(RPA_E_INVALID, "sm_scale is required and must be finite and > 0");
@@ -542,24 +544,21 @@ rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t
   if (page_size <= 0 || page_size % read_block != 0)
     return fail(RPA_E_INVALID, "page_size=%d must be a multiple of read_block=%d", page_size, read_block);
   if (kv_lora_rank != 512 || rope_dim != 64)
-    return fail(RPA_E_UNSUPPORTED, "sparse_mla_forward implements kv_lora_rank=512, rope_dim=64");
+    return fail(RPA_E_UNSUPPORTED, "sparse MLA implements kv_lora_rank=512, rope_dim=64");
   const int dk = kv_lora_rank + rope_dim;
   if (cache_dim < dk || cache_dim % 8 != 0)
     return fail(RPA_E_SHAPE, "cache_dim=%d must be >= %d and a multiple of 8", cache_dim, dk);
   if (total_num_pages <= 0 || ptw <= 0)
     return fail(RPA_E_SHAPE, "total_num_pages=%d and ptw=%d must be positive", total_num_pages, ptw);
-  if (seq_len < 0) return fail(RPA_E_INVALID, "seq_len=%d must be >= 0", seq_len);
   if (!aligned16(q) || !aligned16(kv_cache) || !aligned16(out))
     return fail(RPA_E_INVALID, "q, kv_cache and out must be 16-byte aligned");
-  if (num_queries == 0) return ok();
-  rpa::SparseArgs a{};
+  a = rpa::SparseArgs{};
   a.q = q;
   a.kv = kv_cache;
   a.page_table = page_table;
   a.indices = indices;
   a.positions = positions;
   a.out = out;
-  a.seq_len = seq_len;
   a.num_queries = num_queries;
   a.num_heads = num_heads;
   a.top_k = top_k;
@@ -571,7 +570,59 @@ rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t
   a.dv = kv_lora_rank;
   a.dk = dk;
   a.score_scale = sm_scale;
+  return RPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t* page_table,
+                              const int32_t* indices, const int32_t* positions, int32_t seq_len,
+                              int32_t num_queries, int32_t num_heads, int32_t top_k,
+                              int32_t read_block, int32_t page_size, int32_t total_num_pages,
+                              int32_t cache_dim, int32_t ptw, int32_t kv_lora_rank,
+                              int32_t rope_dim, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes, rpa_stream_t stream_) {
+  (void)workspace;
+  (void)workspace_bytes;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  rpa::SparseArgs a;
+  const rpa_status st = sparse_prepare(a, q, kv_cache, page_table, indices, positions, num_queries,
+                                       num_heads, top_k, read_block, page_size, total_num_pages,
+                                       cache_dim, ptw, kv_lora_rank, rope_dim, sm_scale, out);
+  if (st != RPA_OK) return st;
+  if (seq_len < 0) return fail(RPA_E_INVALID, "seq_len=%d must be >= 0", seq_len);
+  if (num_queries == 0) return ok();
+  a.seq_len = seq_len;
   return hip_status(rpa::launch_sparse_mla(a, stream), "sparse_mla_forward launch");
+}
+
+rpa_status sparse_mla_forward_ragged(const void* q, const void* kv_cache,
+                                     const int32_t* page_indices, int32_t ptw,
+                                     const int32_t* indices, const int32_t* positions,
+                                     const int32_t* cu_q_lens, const int32_t* seq_lens,
+                                     const int32_t* cu_kv_lens, int32_t num_seqs,
+                                     int32_t num_tokens, int32_t num_heads, int32_t top_k,
+                                     int32_t read_block, int32_t page_size,
+                                     int32_t total_num_pages, int32_t cache_dim,
+                                     int32_t kv_lora_rank, int32_t rope_dim, float sm_scale,
+                                     float* out, rpa_stream_t stream_) {
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+  rpa::SparseArgs a;
+  const rpa_status st = sparse_prepare(a, q, kv_cache, page_indices, indices, positions, num_tokens,
+                                       num_heads, top_k, read_block, page_size, total_num_pages,
+                                       cache_dim, ptw, kv_lora_rank, rope_dim, sm_scale, out);
+  if (st != RPA_OK) return st;
+  if (!cu_q_lens || !seq_lens || !cu_kv_lens)
+    return fail(RPA_E_INVALID, "cu_q_lens, seq_lens and cu_kv_lens must be non-NULL");
+  if (num_seqs <= 0) return fail(RPA_E_SHAPE, "num_seqs=%d must be positive", num_seqs);
+  if (num_tokens == 0) return ok();
+  a.cu_q_lens = cu_q_lens;
+  a.seq_lens = seq_lens;
+  a.cu_kv_lens = cu_kv_lens;
+  a.num_seqs = num_seqs;
+  return hip_status(rpa::launch_sparse_mla(a, stream), "sparse_mla_forward_ragged launch");
 }
 
 }  // extern "C"

@@ -142,11 +142,16 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream);
 struct SparseArgs {
   const void* q;
   const void* kv;
-  const int32_t* page_table;
+  const int32_t* page_table;  // single sequence: [ptw]; ragged: the packed table [ptw]
   const int32_t* indices;
   const int32_t* positions;
+  // Packed-ragged mode when cu_q_lens != nullptr: per-token request, bound
+  // seq_lens[rid] and table base cu_kv_lens[rid] / page_size.
+  const int32_t* cu_q_lens;
+  const int32_t* seq_lens;
+  const int32_t* cu_kv_lens;
   float* out;
-  int seq_len, num_queries, num_heads, top_k, read_block, page_size, total_num_pages,
+  int seq_len, num_seqs, num_queries, num_heads, top_k, read_block, page_size, total_num_pages,
       cache_dim, ptw, dv, dk;
   float score_scale;
 };

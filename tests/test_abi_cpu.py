@@ -141,6 +141,31 @@ def test_sparse_static_rejections(lib):
     assert call(kl=256) == RPA_E_UNSUPPORTED
 
 
+def test_sparse_ragged_static_rejections(lib):
+    """The packed-ragged sparse entry shares the single-sequence checks and
+    adds its own (request arrays present, at least one request); all of them
+    return before any launch."""
+    f = lib.sparse_mla_forward_ragged
+    base = dict(ptw=8, R=2, T=5, H=16, K=8, RB=64, ps=64, P=8, C=640, kl=512, rd=64, sc=0.07,
+                cu=FAKE, sl=FAKE, ck=FAKE)
+
+    def call(**k):
+        a = {**base, **k}
+        return f(FAKE, FAKE, FAKE, a["ptw"], FAKE, FAKE, a["cu"], a["sl"], a["ck"], a["R"], a["T"],
+                 a["H"], a["K"], a["RB"], a["ps"], a["P"], a["C"], a["kl"], a["rd"], a["sc"], FAKE,
+                 None)
+
+    assert call(sc=float("nan")) == RPA_E_INVALID
+    assert call(RB=24) == RPA_E_INVALID
+    assert call(C=512) == RPA_E_SHAPE
+    assert call(kl=256) == RPA_E_UNSUPPORTED
+    assert call(R=0) == RPA_E_SHAPE
+    assert call(cu=None) == RPA_E_INVALID
+    assert call(ck=None) == RPA_E_INVALID
+    assert call(K=300) == RPA_E_UNSUPPORTED
+    assert call(T=0) == 0                      # nothing to do, nothing launched
+
+
 def test_noalloc_rejects_capacities_beyond_its_scratch_before_any_launch(lib):
     """rpa_forward_noalloc checks the capacities against its static scratch
     array on the host and returns RPA_E_WORKSPACE without touching the GPU."""

@@ -177,6 +177,107 @@ def test_sparse_full_size_sampled():
     assert_close(got[qs], want[qs], *TOL, what="sparse_mla")
 
 
+# ----------------------------------------------------------- sparse ragged --
+
+def _sparse_ragged_gpu(c, indices=None, positions=None):
+    d = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(d)
+    out = rpa.sparse_mla_forward_ragged(
+        c.q, c.kv_cache, t(c.page_indices), t(c.indices if indices is None else indices),
+        t(c.positions if positions is None else positions), t(c.cu_q_lens), t(c.seq_lens),
+        t(c.cu_kv_lens), read_block=c.read_block, sm_scale=c.sm_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _sparse_ragged_oracle(c, indices=None, positions=None, queries=None):
+    return oracle.sparse_mla(storage(c.q)[0], oracle.BF16, storage(c.kv_cache)[0], c.page_indices,
+                             c.indices if indices is None else indices,
+                             c.positions if positions is None else positions,
+                             read_block=c.read_block, sm_scale=c.sm_scale, queries=queries,
+                             cu_q_lens=c.cu_q_lens, seq_lens=c.seq_lens, cu_kv_lens=c.cu_kv_lens)
+
+
+SPARSE_RAGGED_CASES = [
+    # (seq_lens, q_lens, H, K, ps, RB, pad_tokens, name)
+    ((3000, 700, 1900, 64), (24, 1, 9, 1), 16, 12, 64, 64, 2, "mixed-extend-decode"),
+    ((2500, 4000, 130), (1, 1, 1), 20, 20, 128, 32, 0, "decodes-rb32-ps128"),
+    ((5000,), (1,), 16, 32, 64, 64, 0, "single-decode"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SPARSE_RAGGED_CASES)),
+                         ids=[c[-1] for c in SPARSE_RAGGED_CASES])
+def test_sparse_ragged_small(idx):
+    seq_lens, q_lens, H, K, ps, RB, pad_tokens, name = SPARSE_RAGGED_CASES[idx]
+    _say(f"sparse ragged {name}")
+    c = wl.make_sparse_ragged(seq_lens=list(seq_lens), q_lens=list(q_lens), H=H, K=K, page_size=ps,
+                              read_block=RB, seed=340 + idx, device="cuda", pad_tokens=pad_tokens,
+                              pad_frac=0.3, name=name)
+    idx_arr = c.indices.copy()
+    if idx_arr.shape[0] > 2:
+        idx_arr[0, -1] = idx_arr[0, 0]     # a repeated unit counts twice
+        idx_arr[1, :] = -1                 # empty selection -> zeros
+    got = as_f64(_sparse_ragged_gpu(c, idx_arr))
+    want = _sparse_ragged_oracle(c, idx_arr)
+    if idx_arr.shape[0] > 2:
+        assert np.all(got[1] == 0.0)
+    assert_close(got, want, *TOL, what=name)
+
+
+def test_sparse_ragged_bound_is_per_request():
+    """Query positions past every request's kv length: keys stop at that
+    request's seq_lens entry (the last selected unit is cut there)."""
+    _say("sparse ragged per-request bound")
+    c = wl.make_sparse_ragged(seq_lens=[1000, 333, 2100], q_lens=[3, 2, 4], H=16, K=8, page_size=64,
+                              read_block=64, seed=350, device="cuda", name="bound")
+    pos = c.positions.copy()
+    idx = np.full_like(c.indices, -1)
+    for r in range(3):
+        rows = slice(c.cu_q_lens[r], c.cu_q_lens[r + 1])
+        pos[rows] = int(c.seq_lens[r]) + 100
+        n = -(-int(c.seq_lens[r]) // 64)
+        idx[rows, :min(8, n)] = np.arange(max(0, n - 8), n)
+    got = as_f64(_sparse_ragged_gpu(c, idx, pos))
+    want = _sparse_ragged_oracle(c, idx, pos)
+    assert_close(got, want, *TOL, what="bound")
+
+
+def test_sparse_ragged_matches_single_sequence_calls_bitwise():
+    """Each request's rows of a packed call equal the single-sequence call on
+    that request's page-table window and length, bit for bit."""
+    _say("sparse ragged vs single-sequence calls")
+    c = wl.make_sparse_ragged(seq_lens=[1500, 64, 2200], q_lens=[7, 1, 5], H=16, K=10, page_size=64,
+                              read_block=64, seed=351, device="cuda", pad_frac=0.2, name="vs-single")
+    got = _sparse_ragged_gpu(c)
+    ps = c.page_size
+    for r in range(3):
+        rows = slice(int(c.cu_q_lens[r]), int(c.cu_q_lens[r + 1]))
+        base = int(c.cu_kv_lens[r]) // ps
+        npg = (int(c.cu_kv_lens[r + 1]) - int(c.cu_kv_lens[r])) // ps
+        one = rpa.sparse_mla_forward(
+            c.q[rows].contiguous(), c.kv_cache, torch.from_numpy(c.page_indices[base:base + npg].copy()).cuda(),
+            torch.from_numpy(c.indices[rows].copy()).cuda(), torch.from_numpy(c.positions[rows].copy()).cuda(),
+            seq_len=int(c.seq_lens[r]), read_block=c.read_block, sm_scale=c.sm_scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got[rows], one), r
+
+
+def test_sparse_ragged_large_sampled():
+    """Four packed requests (64k, 32k, 16k and 8k keys; 1024, 512 and 256
+    extend tokens and one decode), 16 heads, 32 units of 64 tokens; sampled
+    tokens against the oracle, the decode token included."""
+    _say("sparse ragged large (4 requests, 1793 tokens), sampled tokens")
+    c = wl.make_sparse_ragged(seq_lens=[65536, 32768, 16384, 8192], q_lens=[1024, 512, 256, 1],
+                              H=16, K=32, page_size=64, read_block=64, seed=352, device="cuda",
+                              name="large")
+    got = as_f64(_sparse_ragged_gpu(c))
+    qs = np.unique(np.concatenate([np.arange(0, c.q.shape[0], 37), [c.q.shape[0] - 1],
+                                   c.cu_q_lens[1:-1], c.cu_q_lens[1:-1] - 1]))
+    want = _sparse_ragged_oracle(c, queries=qs)
+    assert_close(got[qs], want[qs], *TOL, what="sparse ragged large")
+
+
 def test_mla_page_window_refill_page1():
     """Decode pieces spanning more than the 1024 page ids a workgroup caches in
     LDS: at page size 1, 16 sequences of 20000 keys give shares of ~1250 keys,
