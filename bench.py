@@ -277,7 +277,7 @@ def setup_gqa(torch, rpa, wl, config):
     ns = torch.tensor([case.num_seqs], dtype=torch.int32, device=dev)
     out = torch.empty_like(case.q)
     need = rpa.rpa_workspace_size(kl, pi, case.q.shape[0], case.num_q_heads, case.num_kv_heads,
-                                  case.head_dim, case.page_size)
+                                  case.head_dim)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
     def fn():
@@ -475,7 +475,7 @@ def bench_latent(args, torch, rpa, wl):
         ns = torch.tensor([case.num_seqs], dtype=torch.int32, device=dev)
         out = torch.empty_like(case.ql_nope)
         H = case.ql_nope.shape[1]
-        need = rpa.mla_rpa_workspace_size(kl, pi, case.ql_nope.shape[0], H, 512, case.page_size)
+        need = rpa.mla_rpa_workspace_size(kl, pi, case.ql_nope.shape[0], H, 512)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
         def fn(update=True):

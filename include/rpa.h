@@ -172,10 +172,11 @@ void rpa_set_profile_events_split(void* pre_start, void* pre_stop, void* dec_sta
 
 /*
  * Workspace bytes rpa_forward needs for these capacities (host-only query;
- * depends only on capacities, never on device values).
+ * depends only on meta's capacities max_num_seqs and max_num_tokens and on
+ * the head counts and head_dim, never on device values or the page size).
  */
 size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int32_t num_kv_heads,
-                          int32_t head_dim, int32_t page_size);
+                          int32_t head_dim);
 
 /*
  * GQA ragged paged attention [RPA v2 page: ragged_paged_attention].
@@ -244,9 +245,9 @@ rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const voi
                            const rpa_ragged_meta* meta, const int32_t* slot_loc,
                            int32_t debug_validate, rpa_stream_t stream);
 
-/* Workspace bytes mla_rpa_forward needs for these capacities. */
-size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, int32_t lkv_dim,
-                              int32_t page_size);
+/* Workspace bytes mla_rpa_forward needs for these capacities (max_num_seqs,
+ * max_num_tokens, num_heads, lkv_dim; host-only). */
+size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, int32_t lkv_dim);
 
 /*
  * MLA ragged paged attention [MLA v1 page: mla_ragged_paged_attention].
@@ -274,10 +275,6 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
                            void* out, void* workspace, size_t workspace_bytes,
                            rpa_stream_t stream);
 
-/* Workspace bytes sparse_mla_forward needs. */
-size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t top_k,
-                                 int32_t read_block, int32_t kv_lora_rank);
-
 /*
  * Sparse MLA-latent attention, paged single-sequence mode [Sparse page:
  * sparse_mla_attention, _sparse_mla_kernel_chunked_hminor].
@@ -295,14 +292,14 @@ size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t
  * Requires read_block % 16 == 0 and page_size % read_block == 0; this build
  * handles top_k <= 256 units per query (RPA_E_UNSUPPORTED above).
  * Logical pages at or past ptw are clamped to ptw-1 for the address and masked.
+ * Needs no workspace.
  */
 rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t* page_table,
                               const int32_t* indices, const int32_t* positions, int32_t seq_len,
                               int32_t num_queries, int32_t num_heads, int32_t top_k,
                               int32_t read_block, int32_t page_size, int32_t total_num_pages,
                               int32_t cache_dim, int32_t ptw, int32_t kv_lora_rank,
-                              int32_t rope_dim, float sm_scale, float* out, void* workspace,
-                              size_t workspace_bytes, rpa_stream_t stream);
+                              int32_t rope_dim, float sm_scale, float* out, rpa_stream_t stream);
 
 /*
  * Sparse MLA-latent attention, packed-ragged mode: the tokens of num_seqs

@@ -20,7 +20,7 @@ import os
 
 __all__ = ["rpa_forward", "kv_cache_update", "mla_rpa_forward", "sparse_mla_forward",
            "sparse_mla_forward_ragged",
-           "rpa_workspace_size", "mla_rpa_workspace_size", "sparse_mla_workspace_size",
+           "rpa_workspace_size", "mla_rpa_workspace_size",
            "RpaError", "RpaLibraryMissing", "library_path", "load_library",
            "LAYOUT_COMBINED_GQA", "LAYOUT_MLA_SPLIT", "LAYOUT_MLA_FUSED", "EXPORTED_SYMBOLS"]
 
@@ -33,7 +33,7 @@ EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_last_path", "rpa_set
                     "rpa_workspace_size", "rpa_forward", "rpa_forward_noalloc",
                     "rpa_noalloc_scratch_bytes",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
-                    "sparse_mla_workspace_size", "sparse_mla_forward",
+                    "sparse_mla_forward",
                     "sparse_mla_forward_ragged")
 
 
@@ -88,7 +88,7 @@ def load_library():
     lib.rpa_set_profile_events.restype = None
     lib.rpa_set_profile_events_split.argtypes = [P, P, P, P]
     lib.rpa_set_profile_events_split.restype = None
-    lib.rpa_workspace_size.argtypes = [MP, I32, I32, I32, I32]
+    lib.rpa_workspace_size.argtypes = [MP, I32, I32, I32]
     lib.rpa_workspace_size.restype = SZ
     lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P, SZ, P]
     lib.rpa_forward.restype = I32
@@ -99,15 +99,13 @@ def load_library():
     lib.kv_cache_update.argtypes = [I32, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
                                     MP, P, I32, P]
     lib.kv_cache_update.restype = I32
-    lib.mla_rpa_workspace_size.argtypes = [MP, I32, I32, I32]
+    lib.mla_rpa_workspace_size.argtypes = [MP, I32, I32]
     lib.mla_rpa_workspace_size.restype = SZ
     lib.mla_rpa_forward.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, MP,
                                     OP, P, P, SZ, P]
     lib.mla_rpa_forward.restype = I32
-    lib.sparse_mla_workspace_size.argtypes = [I32, I32, I32, I32, I32]
-    lib.sparse_mla_workspace_size.restype = SZ
     lib.sparse_mla_forward.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, I32, I32, I32,
-                                       I32, I32, F32, P, P, SZ, P]
+                                       I32, I32, F32, P, P]
     lib.sparse_mla_forward.restype = I32
     lib.sparse_mla_forward_ragged.argtypes = [P, P, P, I32, P, P, P, P, P, I32, I32, I32, I32, I32,
                                               I32, I32, I32, I32, I32, F32, P, P]
@@ -207,14 +205,13 @@ def set_profile_events(start, stop):
 
 
 def rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_q_heads, num_kv_heads,
-                       head_dim, page_size):
+                       head_dim):
     lib = load_library()
     m = _Meta()
     m.max_num_seqs = kv_lens.numel()
     m.pages_per_seq = page_indices.numel() // max(1, kv_lens.numel())
     m.max_num_tokens = max_num_tokens
-    return int(lib.rpa_workspace_size(ctypes.byref(m), num_q_heads, num_kv_heads, head_dim,
-                                      page_size))
+    return int(lib.rpa_workspace_size(ctypes.byref(m), num_q_heads, num_kv_heads, head_dim))
 
 
 def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0,
@@ -237,7 +234,7 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
         out = torch.empty_like(q)
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
     opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate)
-    need = int(lib.rpa_workspace_size(ctypes.byref(meta), Hq, ch // 2, D, ps))
+    need = int(lib.rpa_workspace_size(ctypes.byref(meta), Hq, ch // 2, D))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib.rpa_forward(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages), _dtype_code(kv_pages), P,
@@ -307,14 +304,13 @@ def kv_cache_update(layout, new_a, new_b, cache_a, cache_b=None, *, kv_lens=None
     _raise(lib, st)
 
 
-def mla_rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_heads, lkv_dim,
-                           page_size):
+def mla_rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_heads, lkv_dim):
     lib = load_library()
     m = _Meta()
     m.max_num_seqs = kv_lens.numel()
     m.pages_per_seq = page_indices.numel() // max(1, kv_lens.numel())
     m.max_num_tokens = max_num_tokens
-    return int(lib.mla_rpa_workspace_size(ctypes.byref(m), num_heads, lkv_dim, page_size))
+    return int(lib.mla_rpa_workspace_size(ctypes.byref(m), num_heads, lkv_dim))
 
 
 def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, kv_lens,
@@ -337,7 +333,7 @@ def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, k
         out = torch.empty_like(ql_nope)
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
     opts = _opts(lib, sm_scale, sliding_window, soft_cap, None, None, debug_validate)
-    need = int(lib.mla_rpa_workspace_size(ctypes.byref(meta), H, Dl, ps))
+    need = int(lib.mla_rpa_workspace_size(ctypes.byref(meta), H, Dl))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ql_nope.device)
     st = lib.mla_rpa_forward(_ptr(ql_nope), _ptr(q_pe), _ptr(new_kv_c), _ptr(new_k_pe),
@@ -348,14 +344,8 @@ def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, k
     return out
 
 
-def sparse_mla_workspace_size(num_queries, num_heads, top_k, read_block, kv_lora_rank=512):
-    return int(load_library().sparse_mla_workspace_size(num_queries, num_heads, top_k,
-                                                        read_block, kv_lora_rank))
-
-
 def sparse_mla_forward(q, kv_cache, page_table, indices, positions, *, seq_len, read_block,
-                       sm_scale, kv_lora_rank=512, rope_dim=64, out=None, workspace=None,
-                       stream=None):
+                       sm_scale, kv_lora_rank=512, rope_dim=64, out=None, stream=None):
     """Sparse MLA-latent attention over a fused paged latent pool.
 
     q [S, H, 576] bf16; kv_cache [P, ps, C] bf16; page_table [PTW]; indices [S, K]
@@ -363,7 +353,7 @@ def sparse_mla_forward(q, kv_cache, page_table, indices, positions, *, seq_len, 
     """
     torch = _torch()
     lib = load_library()
-    _check_dev(q, kv_cache, page_table, indices, positions, out, workspace)
+    _check_dev(q, kv_cache, page_table, indices, positions, out)
     S, H, Dk = q.shape
     if Dk != kv_lora_rank + rope_dim:
         raise ValueError("q last dim must be kv_lora_rank + rope_dim")
@@ -371,14 +361,10 @@ def sparse_mla_forward(q, kv_cache, page_table, indices, positions, *, seq_len, 
     K = indices.shape[1]
     if out is None:
         out = torch.empty((S, H, kv_lora_rank), dtype=torch.float32, device=q.device)
-    need = int(lib.sparse_mla_workspace_size(S, H, K, read_block, kv_lora_rank))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = lib.sparse_mla_forward(_ptr(q), _ptr(kv_cache), _ptr(_i32(page_table)),
                                 _ptr(_i32(indices)), _ptr(_i32(positions)), int(seq_len), S, H, K,
                                 int(read_block), ps, P, C, page_table.numel(), kv_lora_rank,
-                                rope_dim, float(sm_scale), _ptr(out), _ptr(workspace),
-                                0 if workspace is None else workspace.numel(), _stream(stream))
+                                rope_dim, float(sm_scale), _ptr(out), _stream(stream))
     _raise(lib, st)
     return out
 

@@ -212,8 +212,7 @@ const char* rpa_last_error(void) { return g_last_error.c_str(); }
 const char* rpa_last_path(void) { return g_last_path; }
 
 size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int32_t num_kv_heads,
-                          int32_t head_dim, int32_t page_size) {
-  (void)page_size;
+                          int32_t head_dim) {
   if (!meta || num_kv_heads <= 0 || num_q_heads <= 0 || meta->max_num_seqs <= 0) return 0;
   return rpa::gqa_workspace_bytes(meta->max_num_seqs, meta->max_num_tokens, num_q_heads,
                                   num_kv_heads, head_dim, 0, nullptr);
@@ -276,7 +275,7 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
                                             num_q_heads / num_kv_heads) &&
                     is_pow2(page_size) && aligned16(q) && aligned16(kv_pages) && aligned16(out);
   if (mfma) {
-    const size_t need = rpa_workspace_size(meta, num_q_heads, num_kv_heads, head_dim, page_size);
+    const size_t need = rpa_workspace_size(meta, num_q_heads, num_kv_heads, head_dim);
     if (noalloc) {
       if (need > rpa::noalloc_scratch_bytes())
         return fail(RPA_E_WORKSPACE,
@@ -424,9 +423,7 @@ rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const voi
   return hip_status(rpa::launch_kv_update(a, num_tokens, stream), "kv_cache_update launch");
 }
 
-size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, int32_t lkv_dim,
-                              int32_t page_size) {
-  (void)page_size;
+size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, int32_t lkv_dim) {
   if (!meta || meta->max_num_seqs <= 0 || num_heads <= 0 || lkv_dim <= 0) return 0;
   return rpa::mla_workspace_bytes(meta->max_num_seqs, meta->max_num_tokens, num_heads, lkv_dim);
 }
@@ -464,7 +461,7 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
   if (!aligned16(ql_nope) || !aligned16(q_pe) || !aligned16(cache_kv_c) || !aligned16(cache_k_pe) ||
       !aligned16(out))
     return fail(RPA_E_INVALID, "MLA tensors must be 16-byte aligned");
-  const size_t need = mla_rpa_workspace_size(meta, num_heads, lkv_dim, page_size);
+  const size_t need = mla_rpa_workspace_size(meta, num_heads, lkv_dim);
   if (!workspace || workspace_bytes < need || !aligned16(workspace))
     return fail(RPA_E_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
@@ -504,16 +501,6 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
   a.window = opts->sliding_window;
   rpa::mla_bind_workspace(a, workspace);
   return hip_status(rpa::launch_mla(a, stream), "mla_rpa_forward launch");
-}
-
-size_t sparse_mla_workspace_size(int32_t num_queries, int32_t num_heads, int32_t top_k,
-                                 int32_t read_block, int32_t kv_lora_rank) {
-  (void)num_queries;
-  (void)num_heads;
-  (void)top_k;
-  (void)read_block;
-  (void)kv_lora_rank;
-  return 0;
 }
 
 }  // extern "C"
@@ -582,10 +569,7 @@ rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t
                               int32_t num_queries, int32_t num_heads, int32_t top_k,
                               int32_t read_block, int32_t page_size, int32_t total_num_pages,
                               int32_t cache_dim, int32_t ptw, int32_t kv_lora_rank,
-                              int32_t rope_dim, float sm_scale, float* out, void* workspace,
-                              size_t workspace_bytes, rpa_stream_t stream_) {
-  (void)workspace;
-  (void)workspace_bytes;
+                              int32_t rope_dim, float sm_scale, float* out, rpa_stream_t stream_) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
   rpa::SparseArgs a;
   const rpa_status st = sparse_prepare(a, q, kv_cache, page_table, indices, positions, num_queries,

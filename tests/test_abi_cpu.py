@@ -93,9 +93,9 @@ def test_rpa_forward_static_rejections(lib):
 
 
 def test_workspace_size_depends_only_on_capacities(lib):
-    a = lib.rpa_workspace_size(ctypes.byref(_meta(S=128, pps=512, T=128)), 32, 8, 128, 16)
-    b = lib.rpa_workspace_size(ctypes.byref(_meta(S=128, pps=512, T=128)), 32, 8, 128, 16)
-    c = lib.rpa_workspace_size(ctypes.byref(_meta(S=256, pps=512, T=128)), 32, 8, 128, 16)
+    a = lib.rpa_workspace_size(ctypes.byref(_meta(S=128, pps=512, T=128)), 32, 8, 128)
+    b = lib.rpa_workspace_size(ctypes.byref(_meta(S=128, pps=512, T=128)), 32, 8, 128)
+    c = lib.rpa_workspace_size(ctypes.byref(_meta(S=256, pps=512, T=128)), 32, 8, 128)
     assert a == b > 0 and c > a
 
 
@@ -132,7 +132,7 @@ def test_sparse_static_rejections(lib):
     def call(**k):
         a = {**base, **k}
         return f(FAKE, FAKE, FAKE, FAKE, FAKE, a["seq_len"], a["S"], a["H"], a["K"], a["RB"],
-                 a["ps"], a["P"], a["C"], a["ptw"], a["kl"], a["rd"], a["sc"], FAKE, None, 0, None)
+                 a["ps"], a["P"], a["C"], a["ptw"], a["kl"], a["rd"], a["sc"], FAKE, None)
 
     assert call(sc=0.0) == RPA_E_INVALID       # sm_scale is required
     assert call(RB=24) == RPA_E_INVALID        # read_block % 16
@@ -172,10 +172,10 @@ def test_noalloc_rejects_capacities_beyond_its_scratch_before_any_launch(lib):
     cap = lib.rpa_noalloc_scratch_bytes()
     assert cap == 96 << 20
     big = _meta(S=4096, pps=512, T=4096)
-    assert lib.rpa_workspace_size(ctypes.byref(big), 32, 8, 128, 16) > cap
+    assert lib.rpa_workspace_size(ctypes.byref(big), 32, 8, 128) > cap
     st = lib.rpa_forward_noalloc(FAKE, 1, 32, 128, FAKE, 1, 64, 16, 8, ctypes.byref(big),
                                  ctypes.byref(_opts(lib)), FAKE, None)
     assert st == RPA_E_WORKSPACE
     assert "rpa_forward_noalloc holds at most" in lib.rpa_last_error().decode()
     small = _meta(S=128, pps=512, T=128)
-    assert lib.rpa_workspace_size(ctypes.byref(small), 32, 8, 128, 16) <= cap
+    assert lib.rpa_workspace_size(ctypes.byref(small), 32, 8, 128) <= cap

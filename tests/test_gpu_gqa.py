@@ -144,7 +144,7 @@ def test_side_stream_launch(idx, kv):
                     sliding_window=window, soft_cap=cap, extra_tokens=4096,
                     name=f"{name}-side-{kv}", **extra)
     kl, pi, cu, ns = _dev_meta(c)
-    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], Hq, Hkv, 128, ps)
+    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], Hq, Hkv, 128)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     outs = []
     for _ in range(3):
@@ -173,7 +173,7 @@ def test_graph_capture_with_side_stream():
                     device="cuda", kv_value_scale=2.0, sliding_window=window, soft_cap=cap,
                     k_scale=0.5, v_scale=0.5, extra_tokens=4096, name="graph-side")
     kl, pi, cu, ns = _dev_meta(c)
-    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], Hq, Hkv, 128, ps)
+    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], Hq, Hkv, 128)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     out = torch.zeros_like(c.q)
 
@@ -467,7 +467,7 @@ c = wl.make_gqa([(4, 4), (2, 1025), (24, 900)], num_q_heads=16, num_kv_heads=2, 
 d = "cuda"
 kl, pi = torch.from_numpy(c.kv_lens).to(d), torch.from_numpy(c.page_indices).to(d)
 cu, ns = torch.from_numpy(c.cu_q_lens).to(d), torch.tensor([c.num_seqs], dtype=torch.int32, device=d)
-ws = torch.empty(rpa.rpa_workspace_size(kl, pi, c.q.shape[0], 16, 2, 128, 16), dtype=torch.uint8,
+ws = torch.empty(rpa.rpa_workspace_size(kl, pi, c.q.shape[0], 16, 2, 128), dtype=torch.uint8,
                  device=d)
 out = torch.zeros_like(c.q)
 def call():

@@ -72,7 +72,7 @@ def test_noalloc_rejects_capacities_beyond_its_scratch():
     kl = torch.zeros(S, dtype=torch.int32, device=d)
     pi = torch.zeros((S, c.page_indices.shape[1]), dtype=torch.int32, device=d)
     cu = torch.zeros(S + 1, dtype=torch.int32, device=d)
-    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], 32, 8, 128, 16)
+    need = rpa.rpa_workspace_size(kl, pi, c.q.shape[0], 32, 8, 128)
     assert need > rpa.noalloc_scratch_bytes()
     with pytest.raises(rpa.RpaError, match="rpa_forward_noalloc holds at most"):
         rpa.rpa_forward_noalloc(c.q, c.kv_pages, kl, pi, cu, torch.ones(1, dtype=torch.int32,
