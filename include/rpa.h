@@ -115,6 +115,13 @@ typedef struct {
  *                  (0 < q_len <= kv_len, page count <= pages_per_seq, page ids
  *                  in [0, P), total tokens <= max_num_tokens,
  *                  num_seqs <= max_num_seqs) before launching.
+ *   split_keys     0 = tile sizes from the library's shape-keyed table (see
+ *                  rpa_tile_config); otherwise a multiple of 64 in [64, 2^20]
+ *                  fixing them, as the MLA v1 page's caller fixes its block
+ *                  sizes: rpa_forward's target keys per decode split (at most
+ *                  16 splits per sequence, larger chunks beyond that) and
+ *                  mla_rpa_forward's smallest share of the key space per
+ *                  workgroup. Results agree to rounding for every value.
  * Masked keys are excluded from the softmax exactly; on valid input this is
  * what the pages' finite mask value produces, since every query sees at least
  * its own position.
@@ -126,10 +133,37 @@ typedef struct {
   float k_scale;
   float v_scale;
   int32_t debug_validate;
+  int32_t split_keys;
 } rpa_opts;
 
 /* Fills *opts with the defaults above. */
 void rpa_opts_init(rpa_opts* opts);
+
+/*
+ * Tile sizes a call will use [RPA v2 page: get_tuned_block_sizes; MLA v1
+ * page: the block-size arguments of mla_ragged_paged_attention].
+ *   path RPA_TILE_DECODE_SPLIT: rpa_forward's decode splits; kv_dtype, head
+ *        counts and head_dim as rpa_forward gets them.
+ *   path RPA_TILE_MLA_SHARE: mla_rpa_forward's smallest share; pass the
+ *        latent dtype, num_q_heads = num_heads, num_kv_heads = 1 and
+ *        head_dim = lkv_dim + r_dim.
+ * The table is keyed by pool dtype, head_dim, num_kv_heads and the context
+ * capacity meta->pages_per_seq * page_size (host values only; no device read).
+ * out->keys: keys per split / per share; out->max_splits: split cap (decode
+ * path; 0 otherwise); out->table_row: matching table row, -1 for the built-in
+ * default, -2 when opts->split_keys fixed it.
+ */
+#define RPA_TILE_DECODE_SPLIT 0
+#define RPA_TILE_MLA_SHARE 1
+typedef struct {
+  int32_t keys;
+  int32_t max_splits;
+  int32_t table_row;
+} rpa_tile_params;
+rpa_status rpa_tile_config(int32_t path, rpa_dtype kv_dtype, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                           const rpa_ragged_meta* meta, const rpa_opts* opts,
+                           rpa_tile_params* out);
 
 /* Thread-local description of the last error (empty string after success). */
 const char* rpa_last_error(void);

@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(_HERE, "librpa.so")
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
 EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_last_path", "rpa_set_profile_events",
                     "rpa_set_profile_events_split",
-                    "rpa_workspace_size", "rpa_forward", "rpa_forward_noalloc",
+                    "rpa_tile_config", "rpa_workspace_size", "rpa_forward", "rpa_forward_noalloc",
                     "rpa_noalloc_scratch_bytes",
                     "kv_cache_update", "mla_rpa_workspace_size", "mla_rpa_forward",
                     "sparse_mla_forward",
@@ -57,7 +57,16 @@ class _Meta(ctypes.Structure):
 class _Opts(ctypes.Structure):
     _fields_ = [("sm_scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
                 ("soft_cap", ctypes.c_float), ("k_scale", ctypes.c_float),
-                ("v_scale", ctypes.c_float), ("debug_validate", ctypes.c_int32)]
+                ("v_scale", ctypes.c_float), ("debug_validate", ctypes.c_int32),
+                ("split_keys", ctypes.c_int32)]
+
+
+class _TileParams(ctypes.Structure):
+    _fields_ = [("keys", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("table_row", ctypes.c_int32)]
+
+
+TILE_DECODE_SPLIT, TILE_MLA_SHARE = 0, 1
 
 
 _lib = None
@@ -82,6 +91,9 @@ def load_library():
     lib.rpa_opts_init.restype = None
     lib.rpa_last_error.argtypes = []
     lib.rpa_last_error.restype = ctypes.c_char_p
+    lib.rpa_tile_config.argtypes = [I32, I32, I32, I32, I32, I32, MP, OP,
+                                    ctypes.POINTER(_TileParams)]
+    lib.rpa_tile_config.restype = I32
     lib.rpa_last_path.argtypes = []
     lib.rpa_last_path.restype = ctypes.c_char_p
     lib.rpa_set_profile_events.argtypes = [P, P]
@@ -174,7 +186,8 @@ def _meta(kv_lens, page_indices, cu_q_lens, num_seqs, max_num_tokens):
     return m
 
 
-def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate):
+def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
+          split_keys=None):
     o = _Opts()
     lib.rpa_opts_init(ctypes.byref(o))
     o.sm_scale = float(sm_scale)
@@ -183,7 +196,27 @@ def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_valid
     o.k_scale = float(1.0 if k_scale is None else k_scale)
     o.v_scale = float(1.0 if v_scale is None else v_scale)
     o.debug_validate = 1 if debug_validate else 0
+    o.split_keys = int(split_keys or 0)
     return o
+
+
+def tile_config(path, kv_dtype, num_q_heads, num_kv_heads, head_dim, page_size, pages_per_seq,
+                split_keys=None):
+    """Tile sizes a call would use (see rpa_tile_config in include/rpa.h):
+    returns (keys, max_splits, table_row). ``kv_dtype`` is a torch dtype or an
+    RPA dtype code; ``path`` is TILE_DECODE_SPLIT or TILE_MLA_SHARE."""
+    lib = load_library()
+    code = kv_dtype if isinstance(kv_dtype, int) else _dtype_code(_torch().empty(0, dtype=kv_dtype))
+    m = _Meta()
+    m.max_num_seqs = 1
+    m.pages_per_seq = pages_per_seq
+    m.max_num_tokens = 1
+    o = _opts(lib, 1.0, None, None, None, None, False, split_keys)
+    p = _TileParams()
+    st = lib.rpa_tile_config(path, code, num_q_heads, num_kv_heads, head_dim, page_size,
+                             ctypes.byref(m), ctypes.byref(o), ctypes.byref(p))
+    _raise(lib, st)
+    return p.keys, p.max_splits, p.table_row
 
 
 def last_path() -> str:
@@ -216,7 +249,7 @@ def rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_q_heads, num_k
 
 def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0,
                 sliding_window=None, soft_cap=None, k_scale=None, v_scale=None, out=None,
-                workspace=None, debug_validate=False, stream=None):
+                workspace=None, debug_validate=False, split_keys=None, stream=None):
     """GQA ragged paged attention (see ``rpa_forward`` in include/rpa.h).
 
     q [T, Hq, D] (fp32/bf16); kv_pages [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn);
@@ -233,7 +266,8 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
     if out is None:
         out = torch.empty_like(q)
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
-    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
+                 split_keys)
     need = int(lib.rpa_workspace_size(ctypes.byref(meta), Hq, ch // 2, D))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -246,7 +280,7 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
 
 def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, out,
                         sm_scale=1.0, sliding_window=None, soft_cap=None, k_scale=None,
-                        v_scale=None, debug_validate=False, stream=None):
+                        v_scale=None, debug_validate=False, split_keys=None, stream=None):
     """rpa_forward on the library's static scratch (see ``rpa_forward_noalloc``
     in include/rpa.h): no workspace and no allocation; ``out`` must be given."""
     lib = load_library()
@@ -256,7 +290,8 @@ def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs,
     if D2 != D or ch % 2:
         raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
-    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
+                 split_keys)
     st = lib.rpa_forward_noalloc(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages),
                                  _dtype_code(kv_pages), P, ps, ch // 2, ctypes.byref(meta),
                                  ctypes.byref(opts), _ptr(out), _stream(stream))
@@ -315,7 +350,8 @@ def mla_rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_heads, lkv
 
 def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, kv_lens,
                     page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0, sliding_window=None,
-                    soft_cap=None, out=None, workspace=None, debug_validate=False, stream=None):
+                    soft_cap=None, out=None, workspace=None, debug_validate=False, split_keys=None,
+                    stream=None):
     """MLA ragged paged attention: scatter (unless new_* are None) then attend.
 
     ql_nope [T, H, 512], q_pe [T, H, 64], new_kv_c [T, 512], new_k_pe [T, 64],
@@ -332,7 +368,7 @@ def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, k
     if out is None:
         out = torch.empty_like(ql_nope)
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
-    opts = _opts(lib, sm_scale, sliding_window, soft_cap, None, None, debug_validate)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, None, None, debug_validate, split_keys)
     need = int(lib.mla_rpa_workspace_size(ctypes.byref(meta), H, Dl))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ql_nope.device)

@@ -1219,14 +1219,15 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int kv_dtype) {
+GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int split_keys) {
   GqaGeometry g;
   g.group = num_q_heads / num_kv_heads;
   g.qdec = g.group <= 16 ? 16 / g.group : 0;
   g.bq = g.group <= 64 ? 64 / g.group : 1;
-  // Decode splits of about 512 KB of K and V per kv head (1024 bf16 keys,
-  // 2048 fp8 keys); measured against 512/1024/2048 keys on the decode batches.
-  g.split_keys = kv_dtype == DT_FP8 ? 2048 : 1024;
+  // Decode split target from the tile table or the caller (a multiple of 64;
+  // the split count is capped at kMaxSplits, so the workspace does not depend
+  // on it).
+  g.split_keys = split_keys;
   g.max_splits = kMaxSplits;
   g.window = window;
   return g;
@@ -1239,7 +1240,7 @@ bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
 
 size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads,
                            int num_kv_heads, int head_dim, int window, int* tile_capacity) {
-  const GqaGeometry g = gqa_geometry(num_q_heads, num_kv_heads, window, DT_BF16);  // size: split count only
+  const GqaGeometry g = gqa_geometry(num_q_heads, num_kv_heads, window, 1024);  // size: split cap only
   const int64_t cap = (int64_t)num_kv_heads *
                       ((int64_t)max_num_tokens / g.bq + max_num_seqs +
                        (int64_t)max_num_seqs * g.max_splits);

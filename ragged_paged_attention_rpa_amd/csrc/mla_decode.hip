@@ -58,7 +58,6 @@ constexpr int kDt = kDl / 32;                  // 16 output tiles of 32 dims
 constexpr int kDtPerWave = kDt / kWaves;       // 4: a wave's 128 value dims
 constexpr int kDmaPerWave = 9;                 // per stage: 8 latent rows + 8 rope parts
 constexpr int kPageWin = 1024;                 // page ids cached in LDS
-constexpr int kMinPiece = 128;                 // smallest share of the key space
 
 __device__ __attribute__((aligned(16))) const uint8_t kZeroLatent[kKvcBytes + kKpeBytes] = {0};
 
@@ -160,7 +159,7 @@ __global__ void __launch_bounds__(kThreads) mla_plan_kernel(MlaArgs a) {
   const long long space = ktot * HG;
   long long q = (space + kMlaGrid - 1) / kMlaGrid;
   q = (q + kBlk - 1) / kBlk * kBlk;
-  if (q < kMinPiece) q = kMinPiece;
+  if (q < a.min_share) q = a.min_share;
 
   // Pass 2: pieces per (head group, token) item, in key-space order.
   const int items = T * HG;

@@ -78,7 +78,22 @@ rpa_status check_opts(const rpa_opts* o) {
   if (!std::isfinite(o->soft_cap)) return fail(RPA_E_INVALID, "soft_cap must be finite (0 = none)");
   if (!std::isfinite(o->k_scale) || !std::isfinite(o->v_scale))
     return fail(RPA_E_INVALID, "k_scale and v_scale must be finite");
+  if (o->split_keys != 0 && (o->split_keys < 64 || o->split_keys > (1 << 20) || o->split_keys % 64))
+    return fail(RPA_E_INVALID, "split_keys=%d must be 0 (tile table) or a multiple of 64 in [64, 2^20]",
+                o->split_keys);
   return RPA_OK;
+}
+
+// Keys per decode split (path kTileGqaDecode) or smallest MLA share
+// (kTileMlaShare): the caller's split_keys, else the tile table's row.
+int resolve_tile_keys(int path, const rpa_opts* o, int kv_dtype, int head_dim, int num_kv_heads,
+                      const rpa_ragged_meta* meta, int page_size, int* row) {
+  if (o->split_keys > 0) {
+    if (row) *row = -2;
+    return o->split_keys;
+  }
+  const int64_t ctx = (int64_t)meta->pages_per_seq * page_size;
+  return rpa::tile_keys(path, kv_dtype, head_dim, num_kv_heads, ctx, row);
 }
 
 struct HostMeta {
@@ -205,6 +220,27 @@ void rpa_opts_init(rpa_opts* o) {
   o->k_scale = 1.0f;
   o->v_scale = 1.0f;
   o->debug_validate = 0;
+  o->split_keys = 0;
+}
+
+rpa_status rpa_tile_config(int32_t path, rpa_dtype kv_dtype, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                           const rpa_ragged_meta* meta, const rpa_opts* opts,
+                           rpa_tile_params* out) {
+  if (!out || !meta || !opts) return fail(RPA_E_INVALID, "out, meta and opts must be non-NULL");
+  RPA_TRY(check_opts(opts));
+  if (path != RPA_TILE_DECODE_SPLIT && path != RPA_TILE_MLA_SHARE)
+    return fail(RPA_E_INVALID, "path=%d must be RPA_TILE_DECODE_SPLIT or RPA_TILE_MLA_SHARE", path);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
+      meta->pages_per_seq < 0)
+    return fail(RPA_E_SHAPE, "head counts, head_dim, page_size must be positive");
+  int row = -1;
+  const int tp = path == RPA_TILE_DECODE_SPLIT ? rpa::kTileGqaDecode : rpa::kTileMlaShare;
+  out->keys = resolve_tile_keys(tp, opts, (int)kv_dtype, head_dim, num_kv_heads, meta, page_size,
+                                &row);
+  out->max_splits = path == RPA_TILE_DECODE_SPLIT ? 16 : 0;
+  out->table_row = row;
+  return ok();
 }
 
 const char* rpa_last_error(void) { return g_last_error.c_str(); }
@@ -269,7 +305,9 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   a.score_scale = opts->sm_scale * opts->k_scale;
   a.soft_cap = opts->soft_cap;
   a.v_scale = opts->v_scale;
-  a.geo = rpa::gqa_geometry(num_q_heads, num_kv_heads, opts->sliding_window, a.kv_dtype);
+  a.geo = rpa::gqa_geometry(num_q_heads, num_kv_heads, opts->sliding_window,
+                            resolve_tile_keys(rpa::kTileGqaDecode, opts, a.kv_dtype, head_dim,
+                                              num_kv_heads, meta, page_size, nullptr));
 
   const bool mfma = rpa::gqa_mfma_supported(a.q_dtype, a.kv_dtype, head_dim,
                                             num_q_heads / num_kv_heads) &&
@@ -499,6 +537,8 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
   a.score_scale = opts->sm_scale;
   a.soft_cap = opts->soft_cap;
   a.window = opts->sliding_window;
+  a.min_share = resolve_tile_keys(rpa::kTileMlaShare, opts, (int)dtype, lkv_dim + r_dim, 1, meta,
+                                  page_size, nullptr);
   rpa::mla_bind_workspace(a, workspace);
   return hip_status(rpa::launch_mla(a, stream), "mla_rpa_forward launch");
 }

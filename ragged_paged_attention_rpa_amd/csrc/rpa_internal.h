@@ -86,7 +86,12 @@ struct GqaArgs {
 constexpr int kXcdCursor0 = 16;  // first per-XCD prefill cursor in GqaArgs::counters
 constexpr int kXcds = 8;         // XCDs of an MI355X (one prefill cursor each)
 
-GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int kv_dtype);
+// Tile-size table (tile_table.cpp): keys per decode split (kTileGqaDecode)
+// or smallest MLA share (kTileMlaShare) for a shape; *row receives the
+// matching row (-1: built-in default).
+enum TilePath { kTileGqaDecode = 0, kTileMlaShare = 1 };
+int tile_keys(int path, int kv_dtype, int head_dim, int num_kv_heads, int64_t context, int* row);
+GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int split_keys);
 size_t gqa_workspace_bytes(int max_num_seqs, int max_num_tokens, int num_q_heads,
                            int num_kv_heads, int head_dim, int window, int* tile_capacity);
 // Carves the workspace into tiles/counters/partials of GqaArgs.
@@ -124,6 +129,7 @@ struct MlaArgs {
   float score_scale;
   float soft_cap;
   int window;
+  int min_share;      // smallest share of the key space per workgroup (multiple of 32)
   // workspace
   int32_t* counters;  // [0] pieces, [1] partial slots used
   int32_t* wg_start;  // [kMlaGrid + 1] first piece of each workgroup's share

@@ -179,3 +179,23 @@ def test_noalloc_rejects_capacities_beyond_its_scratch_before_any_launch(lib):
     assert "rpa_forward_noalloc holds at most" in lib.rpa_last_error().decode()
     small = _meta(S=128, pps=512, T=128)
     assert lib.rpa_workspace_size(ctypes.byref(small), 32, 8, 128) <= cap
+
+
+def test_tile_table_rows_and_override():
+    """rpa_tile_config reports the table row a call would use (host values
+    only), and a caller's split_keys overrides it; invalid values are refused."""
+    import torch
+    bf16 = rpa.tile_config(rpa.TILE_DECODE_SPLIT, torch.bfloat16, 32, 8, 128, 16, 512)
+    fp8 = rpa.tile_config(rpa.TILE_DECODE_SPLIT, torch.float8_e4m3fn, 32, 8, 128, 16, 512)
+    assert bf16[0] == 1024 and bf16[1] == 16 and bf16[2] >= 0
+    assert fp8[0] == 2048 and fp8[2] >= 0 and fp8[2] != bf16[2]
+    mla = rpa.tile_config(rpa.TILE_MLA_SHARE, torch.bfloat16, 128, 1, 576, 64, 512)
+    assert mla[0] % 32 == 0 and mla[1] == 0 and mla[2] >= 0
+    assert rpa.tile_config(rpa.TILE_DECODE_SPLIT, torch.bfloat16, 32, 8, 128, 16, 512,
+                           split_keys=320) == (320, 16, -2)
+    for bad in (32, 100, (1 << 20) + 64):
+        with pytest.raises(rpa.RpaError):
+            rpa.tile_config(rpa.TILE_DECODE_SPLIT, torch.bfloat16, 32, 8, 128, 16, 512,
+                            split_keys=bad)
+    with pytest.raises(rpa.RpaError):
+        rpa.tile_config(7, torch.bfloat16, 32, 8, 128, 16, 512)

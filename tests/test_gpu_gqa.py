@@ -520,3 +520,27 @@ def test_last_path_names_the_kernel_path():
                     device="cuda")
     _check(c, _run_gpu(c), _run_oracle(c), "bf16")
     assert rpa.last_path() == "gqa_generic"
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_explicit_split_keys_agree_with_the_oracle(kv):
+    """Decode splits fixed by the caller (rpa_opts.split_keys) instead of the
+    tile table: 64-key splits (the smallest; long sequences hit the 16-split
+    cap and take larger chunks), 448 and 8192 keys, with a window and a cap,
+    on decodes and a short prefill chunk; each matches the oracle."""
+    _say(f"explicit split sizes ({kv})")
+    kvd = torch.bfloat16 if kv == "bf16" else torch.float8_e4m3fn
+    seqs = [(1, 5000), (1, 700), (2, 64), (1, 1), (1, 3000), (7, 2100), (1, 12345)]
+    c = wl.make_gqa(seqs, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=kvd, seed=460, device="cuda",
+                    sliding_window=4000, soft_cap=30.0, k_scale=0.5 if kv == "fp8" else None,
+                    v_scale=0.5 if kv == "fp8" else None, name=f"split-{kv}")
+    want = _run_oracle(c)
+    outs = []
+    for sk in (None, 64, 448, 8192):
+        got = _run_gpu(c, split_keys=sk)
+        _check(c, got, want, kv)
+        outs.append(as_f64(got))
+    rows = np.arange(int(c.cu_q_lens[c.num_seqs]))
+    for o in outs[1:]:
+        assert_close(o[rows], outs[0][rows], *TOL[kv], what=f"split-{kv} vs table")

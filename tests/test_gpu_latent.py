@@ -101,6 +101,25 @@ def test_mla_decode_full_size_sampled():
     assert_close(as_f64(got)[tokens], want[tokens], *TOL, what="mla_decode")
 
 
+def test_mla_explicit_min_share():
+    """mla_rpa_forward with the smallest share fixed by the caller (64 keys:
+    every workgroup takes a share on a small batch; 4096: few workgroups, few
+    cut tokens) instead of the tile table; the caches and outputs match."""
+    _say("mla explicit min share")
+    for sk in (64, 4096):
+        c = wl.make_mla([(1, 1500), (3, 900), (1, 64), (2, 2)], num_heads=128, page_size=16,
+                        seed=470, device="cuda", name=f"share-{sk}")
+        ckv, ckp = _host_caches_after_update(c)
+        kl, pi, cu, ns = _meta(c)
+        got = rpa.mla_rpa_forward(c.ql_nope, c.q_pe, c.new_kv_c, c.new_k_pe, c.cache_kv_c,
+                                  c.cache_k_pe, kl, pi, cu, ns, sm_scale=c.sm_scale, split_keys=sk)
+        torch.cuda.synchronize()
+        assert np.array_equal(storage(c.cache_kv_c)[0], ckv)
+        assert np.array_equal(storage(c.cache_k_pe)[0], ckp)
+        want = _mla_oracle(c, ckv, ckp)
+        assert_close(as_f64(got), want, *TOL, what=f"share-{sk}")
+
+
 # ------------------------------------------------------------------ sparse --
 
 def _sparse_gpu(c, indices=None):
