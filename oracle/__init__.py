@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rpa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
 
 _lib = None
@@ -59,13 +59,14 @@ def _load():
         lib.oracle_rpa.argtypes = [c_void_p, c_int, c_int, c_int, c_int,
                                    c_void_p, c_int, c_int, c_int, c_int,
                                    c_void_p, c_void_p, c_int, c_void_p, c_int,
-                                   c_double, c_int, c_double, c_double, c_double,
+                                   c_double, c_int, c_double, c_double, c_double, c_double,
                                    c_void_p, c_int, c_void_p]
         lib.oracle_mla.restype = c_int
         lib.oracle_mla.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                    c_void_p, c_int, c_void_p, c_int, c_int, c_int, c_int,
                                    c_void_p, c_void_p, c_int, c_void_p, c_int,
-                                   c_double, c_int, c_double, c_void_p, c_int, c_void_p]
+                                   c_double, c_int, c_double, c_double, c_double, c_double,
+                                   c_void_p, c_int, c_void_p]
         lib.oracle_sparse_mla.restype = c_int
         lib.oracle_sparse_mla.argtypes = [c_void_p, c_int, c_int, c_int, c_int, c_int,
                                           c_void_p, c_int, c_int, c_int,
@@ -101,7 +102,7 @@ def _c(a, dtype=None):
 
 def _storage(a, dtype):
     """Raw storage array for one of the oracle's dtype codes."""
-    want = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8}[dtype]
+    want = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, INT8: np.int8}[dtype]
     a = np.ascontiguousarray(a)
     if a.dtype != want:
         raise TypeError(f"expected storage dtype {want} for code {dtype}, got {a.dtype}")
@@ -119,8 +120,9 @@ def _check(rc, what):
 
 def rpa(q, q_dtype, kv_pages, kv_dtype, kv_lens, page_indices, cu_q_lens, num_seqs, *,
         sm_scale=1.0, sliding_window=None, soft_cap=None, k_scale=None, v_scale=None,
-        tokens=None):
+        q_scale=None, tokens=None):
     """GQA ragged paged attention [RPA v2 page: ref_ragged_paged_attention].
+    Stored K, V and Q are dequantised exactly by k_scale, v_scale, q_scale.
 
     q [T, Hq, D]; kv_pages [P, ps, 2*Hkv, D]; page_indices [max_num_seqs, pps]
     (or flat). Returns fp64 [T, Hq, D]; rows outside ``tokens`` (when given)
@@ -143,6 +145,7 @@ def rpa(q, q_dtype, kv_pages, kv_dtype, kv_lens, page_indices, cu_q_lens, num_se
         _ptr(kv_lens), _ptr(pi), pps, _ptr(cu_q_lens), int(num_seqs),
         float(sm_scale), int(sliding_window or 0), float(soft_cap or 0.0),
         float(1.0 if k_scale is None else k_scale), float(1.0 if v_scale is None else v_scale),
+        float(1.0 if q_scale is None else q_scale),
         _ptr(tl), 0 if tl is None else tl.size, _ptr(out))
     _check(rc, "rpa")
     return out
@@ -150,14 +153,15 @@ def rpa(q, q_dtype, kv_pages, kv_dtype, kv_lens, page_indices, cu_q_lens, num_se
 
 def mla(ql_nope, q_pe, dtype, cache_kv_c, cache_k_pe, kv_lens, page_indices, cu_q_lens,
         num_seqs, *, sm_scale=1.0, sliding_window=None, soft_cap=None, tokens=None,
-        fused=False):
+        fused=False, q_scale=None, k_scale=None, v_scale=None):
     """MLA latent attention over an updated cache
     [MLA v1 page: ref_mla_ragged_paged_attention].
 
     ql_nope [T, H, Dl], q_pe [T, H, Dr]; cache_kv_c [P, ps, >=Dl] and
     cache_k_pe [P, ps, >=Dr] (split layout) or, with ``fused``, one array
     [P, ps, >=Dl+Dr] passed as cache_kv_c (cache_k_pe ignored).
-    Returns fp64 [T, H, Dl].
+    Scores are multiplied by sm_scale, k_scale and q_scale, the value sum by
+    v_scale (the page's kernel scales). Returns fp64 [T, H, Dl].
     """
     ql_nope = _storage(ql_nope, dtype)
     q_pe = _storage(q_pe, dtype)
@@ -180,7 +184,9 @@ def mla(ql_nope, q_pe, dtype, cache_kv_c, cache_k_pe, kv_lens, page_indices, cu_
         _ptr(ql_nope), _ptr(q_pe), dtype, T, H, Dl, Dr, _ptr(cache_kv_c), kvc_stride,
         _ptr(cache_k_pe), kpe_stride, kpe_col, P, ps, _ptr(kv_lens), _ptr(pi), pps,
         _ptr(cu_q_lens), int(num_seqs), float(sm_scale), int(sliding_window or 0),
-        float(soft_cap or 0.0), _ptr(tl), 0 if tl is None else tl.size, _ptr(out))
+        float(soft_cap or 0.0), float(1.0 if q_scale is None else q_scale),
+        float(1.0 if k_scale is None else k_scale), float(1.0 if v_scale is None else v_scale),
+        _ptr(tl), 0 if tl is None else tl.size, _ptr(out))
     _check(rc, "mla")
     return out
 

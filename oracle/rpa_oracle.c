@@ -40,7 +40,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_INT8 = 3 };
 enum { OR_LAYOUT_COMBINED_GQA = 0, OR_LAYOUT_MLA_SPLIT = 1, OR_LAYOUT_MLA_FUSED = 2 };
 
 /* ---- storage decoders (own implementations, from the format definitions) ---- */
@@ -73,12 +73,14 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
     case OR_F32: return (double)((const float*)base)[idx];
     case OR_BF16: return dec_bf16(((const uint16_t*)base)[idx]);
     case OR_FP8_E4M3: return dec_e4m3fn(((const uint8_t*)base)[idx]);
+    /* two's-complement byte: the integer it encodes (dequantised by the caller's scale) */
+    case OR_INT8: return (double)((const int8_t*)base)[idx];
   }
   return NAN;
 }
 
 static int dtype_bytes(int dtype) {
-  return dtype == OR_F32 ? 4 : dtype == OR_BF16 ? 2 : dtype == OR_FP8_E4M3 ? 1 : 0;
+  return dtype == OR_F32 ? 4 : dtype == OR_BF16 ? 2 : (dtype == OR_FP8_E4M3 || dtype == OR_INT8) ? 1 : 0;
 }
 
 /* Visibility of key position t to a query at position p
@@ -127,6 +129,9 @@ static int owner_seq(const int32_t* cu_q_lens, int num_seqs, int tok) {
  * as on the page; num_seqs is the dynamic sequence count.
  * Query r of sequence i sits at position kv_len - q_len + r.
  * q head h reads kv head h / (num_q_heads / num_kv_heads).
+ * Stored values are dequantised exactly before use: K by k_scale, V by
+ * v_scale, Q by q_scale (the RPA v2 page scales K and V this way; q_scale is
+ * the MLA v1 page's scale on the scores, which equals scaling Q).
  * token_list (optional, n_list entries): compute only those packed tokens.
  * out [num_tokens, num_q_heads, head_dim] fp64; rows not computed are left
  * as they were.
@@ -137,7 +142,7 @@ int oracle_rpa(const void* q, int q_dtype, int num_tokens, int num_q_heads, int 
                int num_kv_heads, const int32_t* kv_lens, const int32_t* page_indices,
                int pages_per_seq, const int32_t* cu_q_lens, int num_seqs, double sm_scale,
                int sliding_window, double soft_cap, double k_scale, double v_scale,
-               const int32_t* token_list, int n_list, double* out) {
+               double q_scale, const int32_t* token_list, int n_list, double* out) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
   const int group = num_q_heads / num_kv_heads;
   const int ch = 2 * num_kv_heads;
@@ -176,7 +181,8 @@ int oracle_rpa(const void* q, int q_dtype, int num_tokens, int num_q_heads, int 
         const int64_t kbase = (row * ch + 2 * kvh) * head_dim;
         const int64_t qbase = ((int64_t)tok * num_q_heads + h) * head_dim;
         for (int d = 0; d < head_dim; ++d)
-          dot += load_elem(q, q_dtype, qbase + d) * (load_elem(kv_pages, kv_dtype, kbase + d) * k_scale);
+          dot += (load_elem(q, q_dtype, qbase + d) * q_scale) *
+                 (load_elem(kv_pages, kv_dtype, kbase + d) * k_scale);
         s[n] = apply_cap(dot * sm_scale, soft_cap);
         key_row[n] = row;
         ++n;
@@ -212,14 +218,16 @@ int oracle_rpa(const void* q, int q_dtype, int num_tokens, int num_q_heads, int 
  * For the fused pool (one array [P, ps, stride] holding [kv_c || k_pe || 0])
  * pass the same pointer for both caches with kpe_col = lkv_dim; otherwise
  * kpe_col = 0.
+ * Scales as the page's kernel applies them: scores times sm_scale, k_scale
+ * and q_scale (before the cap), the value sum times v_scale.
  */
 int oracle_mla(const void* ql_nope, const void* q_pe, int dtype, int num_tokens, int num_heads,
                int lkv_dim, int r_dim, const void* cache_kv_c, int kvc_stride,
                const void* cache_k_pe, int kpe_stride, int kpe_col, int total_num_pages,
                int page_size, const int32_t* kv_lens, const int32_t* page_indices,
                int pages_per_seq, const int32_t* cu_q_lens, int num_seqs, double sm_scale,
-               int sliding_window, double soft_cap, const int32_t* token_list, int n_list,
-               double* out) {
+               int sliding_window, double soft_cap, double q_scale, double k_scale,
+               double v_scale, const int32_t* token_list, int n_list, double* out) {
   for (int i = 0; i < num_seqs; ++i) {
     int ql = cu_q_lens[i + 1] - cu_q_lens[i];
     if (ql < 0 || ql > kv_lens[i]) return -2;
@@ -259,7 +267,7 @@ int oracle_mla(const void* ql_nope, const void* q_pe, int dtype, int num_tokens,
         for (int d = 0; d < r_dim; ++d)
           dot += load_elem(q_pe, dtype, qr + d) *
                  load_elem(cache_k_pe, dtype, row * kpe_stride + kpe_col + d);
-        s[n] = apply_cap(dot * sm_scale, soft_cap);
+        s[n] = apply_cap(dot * sm_scale * k_scale * q_scale, soft_cap);
         key_row[n] = row;
         ++n;
       }
@@ -270,7 +278,7 @@ int oracle_mla(const void* ql_nope, const void* q_pe, int dtype, int num_tokens,
         for (int64_t k = 0; k < n; ++k)
           for (int d = 0; d < lkv_dim; ++d)
             o[d] += w[k] * load_elem(cache_kv_c, dtype, key_row[k] * kvc_stride + d);
-        for (int d = 0; d < lkv_dim; ++d) o[d] /= norm;
+        for (int d = 0; d < lkv_dim; ++d) o[d] = o[d] * v_scale / norm;
       }
       free(s);
       free(w);

@@ -14,6 +14,8 @@ def storage(t: torch.Tensor):
         return t.view(torch.int16).numpy().view(np.uint16), oracle.BF16
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy(), oracle.FP8_E4M3
+    if t.dtype == torch.int8:
+        return t.numpy(), oracle.INT8
     raise TypeError(t.dtype)
 
 

@@ -37,9 +37,16 @@ MUTATIONS = [
      "load_elem(kv_pages, kv_dtype, vbase + d)", None),
     ("gqa_sm_scale_dropped", "s[n] = apply_cap(dot * sm_scale, soft_cap);",
      "s[n] = apply_cap(dot, soft_cap);", 0),
-    ("mla_sm_scale_dropped", "s[n] = apply_cap(dot * sm_scale, soft_cap);",
-     "s[n] = apply_cap(dot, soft_cap);", 1),
-    ("mla_cap_dropped", "s[n] = apply_cap(dot * sm_scale, soft_cap);", "s[n] = dot * sm_scale;", 1),
+    ("mla_sm_scale_dropped", "s[n] = apply_cap(dot * sm_scale * k_scale * q_scale, soft_cap);",
+     "s[n] = apply_cap(dot * k_scale * q_scale, soft_cap);", None),
+    ("mla_cap_dropped", "s[n] = apply_cap(dot * sm_scale * k_scale * q_scale, soft_cap);",
+     "s[n] = dot * sm_scale * k_scale * q_scale;", None),
+    ("mla_q_scale_dropped", "dot * sm_scale * k_scale * q_scale", "dot * sm_scale * k_scale", None),
+    ("mla_k_scale_dropped", "dot * sm_scale * k_scale * q_scale", "dot * sm_scale * q_scale", None),
+    ("mla_v_scale_dropped", "o[d] = o[d] * v_scale / norm;", "o[d] = o[d] / norm;", None),
+    ("gqa_q_scale_dropped", "(load_elem(q, q_dtype, qbase + d) * q_scale)",
+     "load_elem(q, q_dtype, qbase + d)", None),
+    ("int8_read_unsigned", "(double)((const int8_t*)base)[idx]", "(double)((const uint8_t*)base)[idx]", None),
     ("mla_window_dropped", "if (!key_visible(t, pos, sliding_window)) continue;",
      "if (!key_visible(t, pos, 0)) continue;", 1),
     ("gqa_no_causal_offset", "const int64_t pos = kv_len - q_len + (tok - cu_q_lens[i]);",

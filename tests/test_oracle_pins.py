@@ -322,6 +322,61 @@ def test_mla_fused_pool_equals_split_pool():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------------------ scales and int8 KV --
+
+def _gqa_small(seed):
+    return wl.make_gqa([(3, 20), (1, 7), (6, 40), (1, 1)], num_q_heads=8, num_kv_heads=2,
+                       head_dim=16, page_size=4, q_dtype=torch.float32, kv_dtype=torch.float32,
+                       seed=seed)
+
+
+
+
+def test_q_scale_multiplies_the_scores():
+    """q_scale dequantises Q, so it enters the scores like sm_scale does and
+    leaves the values alone; a power of two keeps the products exact, so the
+    two calls agree bit for bit."""
+    c = _gqa_small(seed=90)
+    q, qd = storage(c.q)
+    kv, kd = storage(c.kv_pages)
+    args = (q, qd, kv, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs)
+    a = oracle.rpa(*args, sm_scale=c.sm_scale, q_scale=4.0)
+    b = oracle.rpa(*args, sm_scale=4.0 * c.sm_scale)
+    assert np.array_equal(a, b)
+    assert not np.allclose(a, oracle.rpa(*args, sm_scale=c.sm_scale), atol=1e-6)
+
+
+def test_mla_scales_follow_the_page_kernel():
+    """The MLA page's kernel multiplies the scores by k_scale and q_scale and
+    the value sum by v_scale: with powers of two that is sm_scale * k * q on
+    the scores and v on the output, exactly."""
+    c = wl.make_mla([(2, 70), (1, 33)], num_heads=3, lkv_dim=16, r_dim=8, page_size=8,
+                    dtype=torch.float32, seed=91)
+    ql, d = storage(c.ql_nope)
+    qp, _ = storage(c.q_pe)
+    ckv, _ = storage(c.cache_kv_c)
+    ckp, _ = storage(c.cache_k_pe)
+    args = (ql, qp, d, ckv, ckp, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs)
+    a = oracle.mla(*args, sm_scale=0.25, q_scale=2.0, k_scale=4.0, v_scale=0.5)
+    b = oracle.mla(*args, sm_scale=2.0)
+    assert np.array_equal(a, 0.5 * b)
+
+
+def test_int8_pool_is_its_integers():
+    """An int8 pool holds two's-complement integers (negative bytes included):
+    it gives exactly what an fp32 pool of the same integer values gives."""
+    c = _gqa_small(seed=92)
+    rng = np.random.default_rng(92)
+    ints = rng.integers(-128, 128, size=tuple(c.kv_pages.shape)).astype(np.int8)
+    q, qd = storage(c.q)
+    meta = (c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs)
+    a = oracle.rpa(q, qd, ints, oracle.INT8, *meta, sm_scale=c.sm_scale, k_scale=0.02,
+                   v_scale=0.03)
+    b = oracle.rpa(q, qd, ints.astype(np.float32), oracle.F32, *meta, sm_scale=c.sm_scale,
+                   k_scale=0.02, v_scale=0.03)
+    assert np.array_equal(a, b)
+
+
 # ------------------------------------------------------------------ sparse --
 
 def _sparse_small(seed=13, K=4, RB=16, ps=32, T=256, S=6, H=4, pad_frac=0.0):
