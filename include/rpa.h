@@ -70,7 +70,7 @@ typedef enum {
   RPA_E_HIP = 6          /* the HIP runtime reported an error */
 } rpa_status;
 
-typedef enum { RPA_F32 = 0, RPA_BF16 = 1, RPA_FP8_E4M3 = 2 } rpa_dtype;
+typedef enum { RPA_F32 = 0, RPA_BF16 = 1, RPA_FP8_E4M3 = 2, RPA_INT8 = 3 } rpa_dtype;
 
 typedef enum {
   RPA_LAYOUT_COMBINED_GQA = 0, /* [P, ps, 2*Hkv, D]: K of kv head h at 2h, V at 2h+1 */
@@ -109,7 +109,13 @@ typedef struct {
  *   sliding_window 0 = none; W > 0 masks keys at or before position - W.
  *   soft_cap       0 = none; otherwise scores become cap * tanh(score / cap)
  *                  after scaling and before masking.
- *   k_scale/v_scale multiply stored K and V (1.0 = none); used for fp8 pools.
+ *   k_scale/v_scale multiply stored K and V (1.0 = none); used for fp8 and
+ *                  int8 pools. mla_rpa_forward applies them as the MLA v1
+ *                  page's kernel does: k_scale on the scores, v_scale on the
+ *                  value sum.
+ *   q_scale        multiplies the scores, i.e. dequantises stored queries
+ *                  (1.0 = none) [MLA v1 page: flash_attention q_scale]; used
+ *                  with fp8 queries.
  *   debug_validate 1 = copy the metadata to the host (synchronising the stream)
  *                  and run the value checks the pages run at runtime
  *                  (0 < q_len <= kv_len, page count <= pages_per_seq, page ids
@@ -134,6 +140,7 @@ typedef struct {
   float v_scale;
   int32_t debug_validate;
   int32_t split_keys;
+  float q_scale;
 } rpa_opts;
 
 /* Fills *opts with the defaults above. */
@@ -214,11 +221,16 @@ size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int3
 
 /*
  * GQA ragged paged attention [RPA v2 page: ragged_paged_attention].
- *   q         [max_num_tokens, num_q_heads, head_dim], q_dtype (F32 or BF16)
+ *   q         [max_num_tokens, num_q_heads, head_dim], q_dtype (F32, BF16, or
+ *             FP8_E4M3 with opts->q_scale; fp8 queries need the MFMA path:
+ *             head_dim 128, a BF16/FP8/INT8 pool, power-of-two page size,
+ *             16-byte aligned q, kv_pages and out, else RPA_E_UNSUPPORTED).
  *   kv_pages  [total_num_pages, page_size, 2*num_kv_heads, head_dim], kv_dtype
- *             (F32, BF16 or FP8_E4M3); combined layout, K at 2h, V at 2h+1.
- *   out       [max_num_tokens, num_q_heads, head_dim], q_dtype. Rows of tokens
- *             at or past cu_q_lens[num_seqs] are not written.
+ *             (F32, BF16, FP8_E4M3 or INT8 with k_scale/v_scale dequantising
+ *             the integers); combined layout, K at 2h, V at 2h+1.
+ *   out       [max_num_tokens, num_q_heads, head_dim], q_dtype (BF16 for fp8
+ *             queries). Rows of tokens at or past cu_q_lens[num_seqs] are not
+ *             written.
  * Requires num_q_heads % num_kv_heads == 0. q head h reads kv head
  * h / (num_q_heads / num_kv_heads). The pool is read only at rows below each
  * sequence's kv_len, so unused pages and stale table entries are never read.
@@ -299,6 +311,8 @@ size_t mla_rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_heads, in
  * cache slot by the same work-group that finished attending for that token,
  * so no read of the caches in this call depends on those writes. Two tokens of
  * one call that map to the same cache slot are an error (debug_validate).
+ * Scores are multiplied by sm_scale, k_scale and q_scale before the cap and the
+ * value sum by v_scale, as the page's kernel applies its scales.
  * This build implements lkv_dim = 512, r_dim = 64, bf16.
  */
 rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* new_kv_c,

@@ -58,7 +58,7 @@ class _Opts(ctypes.Structure):
     _fields_ = [("sm_scale", ctypes.c_float), ("sliding_window", ctypes.c_int32),
                 ("soft_cap", ctypes.c_float), ("k_scale", ctypes.c_float),
                 ("v_scale", ctypes.c_float), ("debug_validate", ctypes.c_int32),
-                ("split_keys", ctypes.c_int32)]
+                ("split_keys", ctypes.c_int32), ("q_scale", ctypes.c_float)]
 
 
 class _TileParams(ctypes.Structure):
@@ -139,6 +139,8 @@ def _dtype_code(t):
         return 1
     if t.dtype == torch.float8_e4m3fn:
         return 2
+    if t.dtype == torch.int8:
+        return 3
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -187,7 +189,7 @@ def _meta(kv_lens, page_indices, cu_q_lens, num_seqs, max_num_tokens):
 
 
 def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
-          split_keys=None):
+          split_keys=None, q_scale=None):
     o = _Opts()
     lib.rpa_opts_init(ctypes.byref(o))
     o.sm_scale = float(sm_scale)
@@ -197,6 +199,7 @@ def _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_valid
     o.v_scale = float(1.0 if v_scale is None else v_scale)
     o.debug_validate = 1 if debug_validate else 0
     o.split_keys = int(split_keys or 0)
+    o.q_scale = float(1.0 if q_scale is None else q_scale)
     return o
 
 
@@ -249,12 +252,14 @@ def rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_q_heads, num_k
 
 def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0,
                 sliding_window=None, soft_cap=None, k_scale=None, v_scale=None, out=None,
-                workspace=None, debug_validate=False, split_keys=None, stream=None):
+                workspace=None, debug_validate=False, split_keys=None, q_scale=None,
+                stream=None):
     """GQA ragged paged attention (see ``rpa_forward`` in include/rpa.h).
 
-    q [T, Hq, D] (fp32/bf16); kv_pages [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn);
+    q [T, Hq, D] (fp32/bf16, or fp8 e4m3fn with q_scale); kv_pages
+    [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn/int8 with k_scale, v_scale);
     kv_lens [S], page_indices [S, pps] or [S*pps], cu_q_lens [S+1], num_seqs [1]
-    (int32, on the GPU). Returns ``out`` [T, Hq, D] in q's dtype.
+    (int32, on the GPU). Returns ``out`` [T, Hq, D] in q's dtype (bf16 for fp8 q).
     """
     torch = _torch()
     lib = load_library()
@@ -264,10 +269,11 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
     if D2 != D or ch % 2:
         raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn
+                          else q.dtype, device=q.device)
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
     opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
-                 split_keys)
+                 split_keys, q_scale)
     need = int(lib.rpa_workspace_size(ctypes.byref(meta), Hq, ch // 2, D))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -280,7 +286,8 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
 
 def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, out,
                         sm_scale=1.0, sliding_window=None, soft_cap=None, k_scale=None,
-                        v_scale=None, debug_validate=False, split_keys=None, stream=None):
+                        v_scale=None, debug_validate=False, split_keys=None, q_scale=None,
+                        stream=None):
     """rpa_forward on the library's static scratch (see ``rpa_forward_noalloc``
     in include/rpa.h): no workspace and no allocation; ``out`` must be given."""
     lib = load_library()
@@ -291,7 +298,7 @@ def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs,
         raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
     opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
-                 split_keys)
+                 split_keys, q_scale)
     st = lib.rpa_forward_noalloc(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages),
                                  _dtype_code(kv_pages), P, ps, ch // 2, ctypes.byref(meta),
                                  ctypes.byref(opts), _ptr(out), _stream(stream))
@@ -351,11 +358,12 @@ def mla_rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_heads, lkv
 def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, kv_lens,
                     page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0, sliding_window=None,
                     soft_cap=None, out=None, workspace=None, debug_validate=False, split_keys=None,
-                    stream=None):
+                    q_scale=None, k_scale=None, v_scale=None, stream=None):
     """MLA ragged paged attention: scatter (unless new_* are None) then attend.
 
     ql_nope [T, H, 512], q_pe [T, H, 64], new_kv_c [T, 512], new_k_pe [T, 64],
-    cache_kv_c [P, ps, 512], cache_k_pe [P, ps, 128] (bf16). Returns out [T, H, 512].
+    cache_kv_c [P, ps, 512], cache_k_pe [P, ps, 128] (bf16). Scores are scaled by
+    sm_scale, k_scale and q_scale, the value sum by v_scale. Returns out [T, H, 512].
     """
     torch = _torch()
     lib = load_library()
@@ -368,7 +376,8 @@ def mla_rpa_forward(ql_nope, q_pe, new_kv_c, new_k_pe, cache_kv_c, cache_k_pe, k
     if out is None:
         out = torch.empty_like(ql_nope)
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
-    opts = _opts(lib, sm_scale, sliding_window, soft_cap, None, None, debug_validate, split_keys)
+    opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
+                 split_keys, q_scale)
     need = int(lib.mla_rpa_workspace_size(ctypes.byref(meta), H, Dl))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=ql_nope.device)

@@ -467,7 +467,7 @@ __device__ __forceinline__ void finish_tile(const GqaArgs& a, const Tile& tile, 
       // for fp8 pools, bf16 for bf16 pools), with (m, l) in fp32.
       uint16_t* pa = a.part_acc + (pidx * kPartRows + r) * kD;
       const float inv_l = l_row > 0.f ? 1.f / l_row : 0.f;
-      const bool f16 = a.kv_dtype == DT_FP8;
+      const bool f16 = a.kv_dtype != DT_BF16;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
         *reinterpret_cast<u32x2*>(pa + 16 * dt + 4 * g) =
@@ -521,11 +521,11 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
   {
     const int tok = s.cu0 + t.qtok0 + (row_ok ? r / G : 0);
     const int head = t.kvh * G + (row_ok ? r % G : 0);
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.num_q_heads + head) * kD;
+    const int64_t q0 = ((int64_t)tok * a.num_q_heads + head) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * j + 8 * g);
+      if (row_ok) v = load_q8(a.q, q0 + 32 * j + 8 * g, a.q_dtype);
       qv[j] = v;
     }
   }
@@ -636,7 +636,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     const bool shared = !keysplit || KV_DT != DT_BF16;
     if (shared) wg_barrier();
     uint32_t cur = sbase + (uint32_t)(b % NST) * dma_stride;
-    if (KV_DT == DT_FP8) {
+    if (KV_DT != DT_BF16) {
       // Widen the raw block: thread tid takes raw column tid/16 (16 fp8
       // values: bf16 columns 2(tid/16) and 2(tid/16) + 1) of keys tid%16 + 16i,
       // so sixteen consecutive lanes touch sixteen keys.
@@ -644,10 +644,10 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
       for (int i = 0; i < 4; ++i) {
         const int key = (tid & 15) + 16 * i, rc = tid >> 4;
         const u32x4 w = lds_read_b128(cur + raw_col(key, rc));
-        const u32x2 b0 = fp8x4_to_bf16x4(w[0]);
-        const u32x2 b1 = fp8x4_to_bf16x4(w[1]);
-        const u32x2 b2 = fp8x4_to_bf16x4(w[2]);
-        const u32x2 b3 = fp8x4_to_bf16x4(w[3]);
+        const u32x2 b0 = kv8x4_to_bf16x4<KV_DT>(w[0]);
+        const u32x2 b1 = kv8x4_to_bf16x4<KV_DT>(w[1]);
+        const u32x2 b2 = kv8x4_to_bf16x4<KV_DT>(w[2]);
+        const u32x2 b3 = kv8x4_to_bf16x4<KV_DT>(w[3]);
         *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
             (__attribute__((address_space(3))) char*)(uintptr_t)(conv + key_col(key, 2 * rc))) =
             u32x4{b0[0], b0[1], b1[0], b1[1]};
@@ -846,7 +846,7 @@ static_assert(4 * 16 * (kD + 2) * sizeof(float) <= sizeof(Dec8Smem::stage), "mer
 // bank conflicts.
 __device__ __forceinline__ int sw8(int key) { return (key & 15) ^ (((key >> 4) & 1) << 3); }
 
-template <bool CAP>
+template <int KV_DT, bool CAP>
 __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm, int ps_log2) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -865,11 +865,11 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
   {
     const int tok = s.cu0 + t.qtok0 + (row_ok ? r / G : 0);
     const int head = t.kvh * G + (row_ok ? r % G : 0);
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.num_q_heads + head) * kD;
+    const int64_t q0 = ((int64_t)tok * a.num_q_heads + head) * kD;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * j + 8 * g);
+      if (row_ok) v = load_q8(a.q, q0 + 32 * j + 8 * g, a.q_dtype);
       qv[j] = v;
     }
   }
@@ -978,7 +978,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
       sv[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sv[tt] = mfma_16x16x32(as_bf16x8(fp8x8_to_bf16x8(kr[tt][j])), as_bf16x8(qv[j]), sv[tt]);
+        sv[tt] = mfma_16x16x32(as_bf16x8(kv8x8_to_bf16x8<KV_DT>(kr[tt][j])), as_bf16x8(qv[j]), sv[tt]);
     }
     // sv[tt][i] of lane group g is key kw + 16tt + 4g + i of row lane%16.
     float mblk = -INFINITY;
@@ -1040,14 +1040,14 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      acc[dt] = mfma_16x16x32(as_bf16x8(fp8x8_to_bf16x8(vr[dt])), as_bf16x8(pb), acc[dt]);
+      acc[dt] = mfma_16x16x32(as_bf16x8(kv8x8_to_bf16x8<KV_DT>(vr[dt])), as_bf16x8(pb), acc[dt]);
   }
 
   finish_tile(a, tile, t, s, acc, m_run, l_run, true, true, row_ok, r,
               reinterpret_cast<float*>(sm.stage));
 }
 
-template <bool CAP>
+template <int KV_DT, bool CAP>
 __global__ void __launch_bounds__(kThreads) gqa_decode8_kernel(GqaArgs a, int ps_log2) {
   __shared__ __attribute__((aligned(1024))) Dec8Smem sm;
   const int count = a.counters[0];
@@ -1058,7 +1058,7 @@ __global__ void __launch_bounds__(kThreads) gqa_decode8_kernel(GqaArgs a, int ps
     __syncthreads();
     if (ti >= count) break;
     const Tile tile = a.tiles[ti];
-    process_decode8<CAP>(a, tile, sm, ps_log2);
+    process_decode8<KV_DT, CAP>(a, tile, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -1100,7 +1100,7 @@ __global__ void __launch_bounds__(kThreads) gqa_merge_kernel(GqaArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float lo, hi;
-          unpack_part(x[i], lo, hi, a.kv_dtype == DT_FP8);
+          unpack_part(x[i], lo, hi, a.kv_dtype != DT_BF16);
           o[2 * i] += w * lo;
           o[2 * i + 1] += w * hi;
         }
@@ -1126,7 +1126,10 @@ __device__ __forceinline__ float load_as_f32(const void* base, int64_t idx, int 
   if (dt == DT_BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
   const uint8_t b = reinterpret_cast<const uint8_t*>(base)[idx];
   float f[4];
-  fp8x4_to_f32((uint32_t)b, f);
+  if (dt == DT_INT8)
+    i8x4_to_f32((uint32_t)b, f);
+  else
+    fp8x4_to_f32((uint32_t)b, f);
   return f[0];
 }
 
@@ -1234,7 +1237,8 @@ GqaGeometry gqa_geometry(int num_q_heads, int num_kv_heads, int window, int spli
 }
 
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim, int group) {
-  return q_dtype == DT_BF16 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && head_dim == kD &&
+  return (q_dtype == DT_BF16 || q_dtype == DT_FP8) &&
+         (kv_dtype == DT_BF16 || kv_dtype == DT_FP8 || kv_dtype == DT_INT8) && head_dim == kD &&
          group >= 1 && group <= 64;
 }
 
@@ -1371,13 +1375,28 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
     else
       RPA_TILE_LAUNCH(DT_BF16, false);
   } else if (a.pre_kernel) {
-    // Only decode-class tiles are left for this launch: the fp8 decode kernel.
+    // Only decode-class tiles are left for this launch: the one-byte decode
+    // kernel.
+#define RPA_DEC8_LAUNCH(DT, CAP)                                                               \
+  hipLaunchKernelGGL((gqa_decode8_kernel<DT, CAP>), dim3(grid), dim3(kThreads), 0, dstream, a, \
+                     ps_log2)
+    if (a.kv_dtype == DT_INT8) {
+      if (cap)
+        RPA_DEC8_LAUNCH(DT_INT8, true);
+      else
+        RPA_DEC8_LAUNCH(DT_INT8, false);
+    } else {
+      if (cap)
+        RPA_DEC8_LAUNCH(DT_FP8, true);
+      else
+        RPA_DEC8_LAUNCH(DT_FP8, false);
+    }
+#undef RPA_DEC8_LAUNCH
+  } else if (a.kv_dtype == DT_INT8) {
     if (cap)
-      hipLaunchKernelGGL(gqa_decode8_kernel<true>, dim3(grid), dim3(kThreads), 0, dstream, a,
-                         ps_log2);
+      RPA_TILE_LAUNCH(DT_INT8, true);
     else
-      hipLaunchKernelGGL(gqa_decode8_kernel<false>, dim3(grid), dim3(kThreads), 0, dstream, a,
-                         ps_log2);
+      RPA_TILE_LAUNCH(DT_INT8, false);
   } else {
     if (cap)
       RPA_TILE_LAUNCH(DT_FP8, true);

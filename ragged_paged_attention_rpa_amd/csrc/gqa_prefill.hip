@@ -89,7 +89,7 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p) {
 
 template <int KV_DT, bool CAP>
 __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& sm, int ps_log2) {
-  constexpr bool F8 = KV_DT == DT_FP8;
+  constexpr bool F8 = KV_DT != DT_BF16;  // one-byte pool (fp8 or int8), widened in LDS
   constexpr int kIPW = (F8 ? kRawStage : kStage) / 1024 / kWaves;  // DMA instructions per wave per block
   constexpr int kEB = F8 ? 1 : 2;
   const int tid = threadIdx.x;
@@ -127,11 +127,11 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   {
     const int tok = cu0 + qtok0 + (row_ok ? r / G : 0);
     const int head = kvh * G + (row_ok ? r % G : 0);
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.num_q_heads + head) * kD + 8 * c;
+    const int64_t q0 = ((int64_t)tok * a.num_q_heads + head) * kD + 8 * c;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      if (row_ok) v = load_q8(a.q, q0 + 16 * ks, a.q_dtype);
       qv[ks] = v;
     }
   }
@@ -231,8 +231,8 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 w = lds_read_b128(src + (uint32_t)(i * 16 * kRawKeyBytes));
-      const u32x4 lo4 = fp8x8_to_bf16x8(u32x2{w[0], w[1]});
-      const u32x4 hi4 = fp8x8_to_bf16x8(u32x2{w[2], w[3]});
+      const u32x4 lo4 = kv8x8_to_bf16x8<KV_DT>(u32x2{w[0], w[1]});
+      const u32x4 hi4 = kv8x8_to_bf16x8<KV_DT>(u32x2{w[2], w[3]});
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
           (__attribute__((address_space(3))) char*)(uintptr_t)(dlo + (uint32_t)(i * 16 * kKeyBytes))) = lo4;
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
@@ -630,7 +630,8 @@ __global__ void __launch_bounds__(kThreads, 1) gqa_prefill_kernel(GqaArgs a, int
 int gqa_prefill_rows() { return kWaves * kRowsPerWave; }
 
 bool gqa_prefill_supported(int q_dtype, int kv_dtype, int head_dim, int group, int page_size) {
-  return q_dtype == DT_BF16 && (kv_dtype == DT_BF16 || kv_dtype == DT_FP8) && head_dim == kD &&
+  return (q_dtype == DT_BF16 || q_dtype == DT_FP8) &&
+         (kv_dtype == DT_BF16 || kv_dtype == DT_FP8 || kv_dtype == DT_INT8) && head_dim == kD &&
          group >= 1 && group <= kWaves * kRowsPerWave && page_size >= 8 &&
          (page_size & (page_size - 1)) == 0;
 }
@@ -644,6 +645,11 @@ hipError_t launch_gqa_prefill(const GqaArgs& a, int ps_log2, int grid, hipStream
       RPA_PRE_LAUNCH(DT_BF16, true);
     else
       RPA_PRE_LAUNCH(DT_BF16, false);
+  } else if (a.kv_dtype == DT_INT8) {
+    if (cap)
+      RPA_PRE_LAUNCH(DT_INT8, true);
+    else
+      RPA_PRE_LAUNCH(DT_INT8, false);
   } else {
     if (cap)
       RPA_PRE_LAUNCH(DT_FP8, true);

@@ -737,7 +737,7 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
   for (int h = 0; h < kWaves; ++h) {
     const int hh = hg * kHeadsPerWg + kWaveHeads * h + (lane & 31);
     const float lh = sm.lsum[h][lane & 31];
-    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    const float inv = lh > 0.f ? a.v_scale / lh : 0.f;
     const bool ok = hh < a.num_heads;
     uint16_t* dst = slot >= 0 ? a.part_acc + ((int64_t)slot * a.num_heads + hh) * kDl
                               : (uint16_t*)a.out + ((int64_t)tok * a.num_heads + hh) * kDl;

@@ -51,6 +51,7 @@ int dtype_bytes(rpa_dtype d) {
     case RPA_F32: return 4;
     case RPA_BF16: return 2;
     case RPA_FP8_E4M3: return 1;
+    case RPA_INT8: return 1;
   }
   return 0;
 }
@@ -76,8 +77,8 @@ rpa_status check_opts(const rpa_opts* o) {
   if (o->sliding_window < 0)
     return fail(RPA_E_INVALID, "sliding_window=%d must be positive (0 = none)", o->sliding_window);
   if (!std::isfinite(o->soft_cap)) return fail(RPA_E_INVALID, "soft_cap must be finite (0 = none)");
-  if (!std::isfinite(o->k_scale) || !std::isfinite(o->v_scale))
-    return fail(RPA_E_INVALID, "k_scale and v_scale must be finite");
+  if (!std::isfinite(o->k_scale) || !std::isfinite(o->v_scale) || !std::isfinite(o->q_scale))
+    return fail(RPA_E_INVALID, "k_scale, v_scale and q_scale must be finite");
   if (o->split_keys != 0 && (o->split_keys < 64 || o->split_keys > (1 << 20) || o->split_keys % 64))
     return fail(RPA_E_INVALID, "split_keys=%d must be 0 (tile table) or a multiple of 64 in [64, 2^20]",
                 o->split_keys);
@@ -221,6 +222,7 @@ void rpa_opts_init(rpa_opts* o) {
   o->v_scale = 1.0f;
   o->debug_validate = 0;
   o->split_keys = 0;
+  o->q_scale = 1.0f;
 }
 
 rpa_status rpa_tile_config(int32_t path, rpa_dtype kv_dtype, int32_t num_q_heads,
@@ -280,9 +282,10 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   if (page_size <= 0 || total_num_pages <= 0)
     return fail(RPA_E_SHAPE, "page_size=%d and total_num_pages=%d must be positive", page_size,
                 total_num_pages);
-  if (q_dtype != RPA_F32 && q_dtype != RPA_BF16)
-    return fail(RPA_E_DTYPE, "q dtype must be F32 or BF16");
-  if (dtype_bytes(kv_dtype) == 0) return fail(RPA_E_DTYPE, "kv dtype must be F32, BF16 or FP8_E4M3");
+  if (q_dtype != RPA_F32 && q_dtype != RPA_BF16 && q_dtype != RPA_FP8_E4M3)
+    return fail(RPA_E_DTYPE, "q dtype must be F32, BF16 or FP8_E4M3");
+  if (dtype_bytes(kv_dtype) == 0)
+    return fail(RPA_E_DTYPE, "kv dtype must be F32, BF16, FP8_E4M3 or INT8");
 
   rpa::GqaArgs a{};
   a.q = q;
@@ -302,7 +305,7 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   a.total_num_pages = total_num_pages;
   a.q_dtype = (int)q_dtype;
   a.kv_dtype = (int)kv_dtype;
-  a.score_scale = opts->sm_scale * opts->k_scale;
+  a.score_scale = opts->sm_scale * opts->k_scale * opts->q_scale;
   a.soft_cap = opts->soft_cap;
   a.v_scale = opts->v_scale;
   a.geo = rpa::gqa_geometry(num_q_heads, num_kv_heads, opts->sliding_window,
@@ -312,6 +315,10 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   const bool mfma = rpa::gqa_mfma_supported(a.q_dtype, a.kv_dtype, head_dim,
                                             num_q_heads / num_kv_heads) &&
                     is_pow2(page_size) && aligned16(q) && aligned16(kv_pages) && aligned16(out);
+  if (q_dtype == RPA_FP8_E4M3 && !mfma)
+    return fail(RPA_E_UNSUPPORTED,
+                "fp8 queries run on the MFMA path only: head_dim 128, a BF16, FP8_E4M3 or INT8 "
+                "pool, a power-of-two page size, 16-byte aligned q, kv_pages and out");
   if (mfma) {
     const size_t need = rpa_workspace_size(meta, num_q_heads, num_kv_heads, head_dim);
     if (noalloc) {
@@ -494,8 +501,6 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
   if (page_size <= 0 || total_num_pages <= 0 || !is_pow2(page_size))
     return fail(RPA_E_SHAPE, "page_size=%d must be a positive power of two; total_num_pages=%d > 0",
                 page_size, total_num_pages);
-  if (opts->k_scale != 1.0f || opts->v_scale != 1.0f)
-    return fail(RPA_E_UNSUPPORTED, "k_scale/v_scale are not applied by the MLA path");
   if (!aligned16(ql_nope) || !aligned16(q_pe) || !aligned16(cache_kv_c) || !aligned16(cache_k_pe) ||
       !aligned16(out))
     return fail(RPA_E_INVALID, "MLA tensors must be 16-byte aligned");
@@ -534,7 +539,10 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
   a.kpe_stride = kpe_stride;
   a.page_size = page_size;
   a.total_num_pages = total_num_pages;
-  a.score_scale = opts->sm_scale;
+  // The MLA page's kernel scales the scores by k_scale and q_scale and the
+  // value sum by v_scale.
+  a.score_scale = opts->sm_scale * opts->k_scale * opts->q_scale;
+  a.v_scale = opts->v_scale;
   a.soft_cap = opts->soft_cap;
   a.window = opts->sliding_window;
   a.min_share = resolve_tile_keys(rpa::kTileMlaShare, opts, (int)dtype, lkv_dim + r_dim, 1, meta,

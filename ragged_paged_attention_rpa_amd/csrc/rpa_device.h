@@ -16,7 +16,7 @@ typedef float floatx2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT8 = 3 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -310,6 +310,49 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(u32x2 w) {
     r[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[h], 1.0f, true));
   }
   return r;
+}
+
+// Four two's-complement bytes of `w` -> four fp32, exactly: byte n of
+// w ^ 0x80808080 is b + 128 as an unsigned byte (one v_cvt_f32_ubyteN), and
+// 128 comes off again.
+__device__ __forceinline__ void i8x4_to_f32(uint32_t w, float* o) {
+  const uint32_t u = w ^ 0x80808080u;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) o[n] = (float)((u >> (8 * n)) & 0xffu) - 128.f;
+}
+
+// Four int8 -> two dwords of packed bf16 (exact: integers of magnitude <= 128
+// are bf16 values).
+__device__ __forceinline__ u32x2 i8x4_to_bf16x4(uint32_t w) {
+  float f[4];
+  i8x4_to_f32(w, f);
+  return u32x2{pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])};
+}
+
+// Eight int8 (in order) to eight bf16 (in order), exactly.
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(u32x2 w) {
+  const u32x2 lo = i8x4_to_bf16x4(w[0]), hi = i8x4_to_bf16x4(w[1]);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// One-byte pool elements (fp8 E4M3FN or int8) widened to bf16, by pool dtype.
+template <int DT>
+__device__ __forceinline__ u32x2 kv8x4_to_bf16x4(uint32_t w) {
+  if constexpr (DT == DT_INT8) return i8x4_to_bf16x4(w);
+  else return fp8x4_to_bf16x4(w);
+}
+template <int DT>
+__device__ __forceinline__ u32x4 kv8x8_to_bf16x8(u32x2 w) {
+  if constexpr (DT == DT_INT8) return i8x8_to_bf16x8(w);
+  else return fp8x8_to_bf16x8(w);
+}
+
+// Eight queries in storage type `dt` (bf16, or fp8 E4M3FN widened exactly) as
+// eight bf16: `p` points at element `e` of a bf16 or byte array.
+__device__ __forceinline__ u32x4 load_q8(const void* p, int64_t e, int dt) {
+  if (dt == DT_FP8)
+    return fp8x8_to_bf16x8(*reinterpret_cast<const u32x2*>((const uint8_t*)p + e));
+  return *reinterpret_cast<const u32x4*>((const uint16_t*)p + e);
 }
 
 // Largest i in [0, n) with cu[i] <= t (the sequence owning packed token t),

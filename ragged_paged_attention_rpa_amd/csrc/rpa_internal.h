@@ -130,6 +130,7 @@ struct MlaArgs {
   float soft_cap;
   int window;
   int min_share;      // smallest share of the key space per workgroup (multiple of 32)
+  float v_scale;      // multiplies the normalised output (the page's scale on the value sum)
   // workspace
   int32_t* counters;  // [0] pieces, [1] partial slots used
   int32_t* wg_start;  // [kMlaGrid + 1] first piece of each workgroup's share

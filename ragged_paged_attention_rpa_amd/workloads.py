@@ -43,10 +43,14 @@ def _gen(device, seed):
 
 
 def randn(shape, dtype, gen, device, scale=1.0):
-    """N(0,1)*scale drawn in fp32 and cast to ``dtype`` (bf16/fp8/fp32)."""
+    """N(0,1)*scale drawn in fp32 and cast to ``dtype`` (bf16/fp8/fp32); for
+    int8, the integers round(32 * N(0,1) * scale) clipped to [-128, 127] (a pool
+    quantised at 1/32 per step, dequantised by a scale of 1/32)."""
     x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
     if scale != 1.0:
         x.mul_(scale)
+    if dtype == torch.int8:
+        return x.mul_(32.0).round_().clamp_(-128, 127).to(torch.int8)
     return x.to(dtype)
 
 

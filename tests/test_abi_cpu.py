@@ -61,8 +61,8 @@ def _opts(lib, **kw):
 
 def test_opts_defaults(lib):
     o = _opts(lib)
-    assert (o.sm_scale, o.sliding_window, o.soft_cap, o.k_scale, o.v_scale, o.debug_validate) == \
-        (1.0, 0, 0.0, 1.0, 1.0, 0)
+    assert (o.sm_scale, o.sliding_window, o.soft_cap, o.k_scale, o.v_scale, o.debug_validate,
+            o.split_keys, o.q_scale) == (1.0, 0, 0.0, 1.0, 1.0, 0, 0, 1.0)
 
 
 FAKE = ctypes.c_void_p(0x10000)
@@ -81,8 +81,13 @@ def test_rpa_forward_static_rejections(lib):
     assert "divisible" in lib.rpa_last_error().decode()
     assert _fwd(lib, D=0) == RPA_E_SHAPE
     assert _fwd(lib, ps=0) == RPA_E_SHAPE
-    assert _fwd(lib, qd=2) == RPA_E_DTYPE            # fp8 queries are not accepted
+    assert _fwd(lib, qd=5) == RPA_E_DTYPE
+    assert _fwd(lib, qd=2, D=64) == RPA_E_UNSUPPORTED  # fp8 queries: MFMA path only
+    assert "MFMA path" in lib.rpa_last_error().decode()
+    assert _fwd(lib, qd=2) == RPA_E_WORKSPACE        # fp8 queries accepted there
+    assert _fwd(lib, kvd=3) == RPA_E_WORKSPACE       # int8 pools accepted
     assert _fwd(lib, kvd=7) == RPA_E_DTYPE
+    assert _fwd(lib, opts=_opts(lib, q_scale=float("inf"))) == RPA_E_INVALID
     assert _fwd(lib, opts=_opts(lib, sliding_window=-1)) == RPA_E_INVALID
     assert _fwd(lib, opts=_opts(lib, soft_cap=float("inf"))) == RPA_E_INVALID
     assert _fwd(lib, opts=_opts(lib, sm_scale=float("nan"))) == RPA_E_INVALID

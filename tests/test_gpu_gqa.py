@@ -544,3 +544,53 @@ def test_explicit_split_keys_agree_with_the_oracle(kv):
     rows = np.arange(int(c.cu_q_lens[c.num_seqs]))
     for o in outs[1:]:
         assert_close(o[rows], outs[0][rows], *TOL[kv], what=f"split-{kv} vs table")
+
+
+INT8_CASES = {
+    # prefill chunks (prefill kernel) next to decodes (one-byte decode kernel)
+    "mixed": ([(1, 3000), (300, 1200), (1, 17), (64, 64), (1, 5000), (700, 2100)], 16, 4, 128, 16,
+              "gqa_mfma_prefill"),
+    # page size 4 (below the prefill kernel's minimum): every tile on the tile
+    # kernel's one-byte blocks, decodes and a short chunk
+    "tile-kernel-ps4": ([(1, 3000), (40, 700), (1, 17), (1, 9000), (3, 64)], 32, 8, 128, 4,
+                        "gqa_mfma"),
+    # head_dim 64: the generic kernel
+    "generic-d64": ([(1, 300), (5, 70), (1, 1)], 8, 2, 64, 16, "gqa_generic"),
+}
+
+
+@pytest.mark.parametrize("mode", list(INT8_CASES))
+def test_int8_pool(mode):
+    """int8 pools with per-tensor scales (the integers of N(0,1) quantised at
+    1/32, dequantised by k_scale = v_scale = 1/32), on every kernel path."""
+    seqs, hq, hkv, d, ps, path = INT8_CASES[mode]
+    _say(f"int8 pool ({mode})")
+    c = wl.make_gqa(seqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.int8, seed=480, device="cuda",
+                    sliding_window=2500 if mode == "mixed" else None,
+                    soft_cap=30.0 if mode != "tile-kernel-ps4" else None, k_scale=1 / 32,
+                    v_scale=1 / 32,
+                    name=f"int8-{mode}")
+    got = _run_gpu(c)
+    assert rpa.last_path() == path
+    _check(c, got, _run_oracle(c), "bf16")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
+def test_fp8_queries_with_q_scale(kv):
+    """fp8 queries dequantised by q_scale (widened exactly to bf16 on load),
+    on a mixed batch; the output is bf16."""
+    _say(f"fp8 queries ({kv} pool)")
+    kvd = {"bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn, "int8": torch.int8}[kv]
+    ks = {"bf16": None, "fp8": 0.5, "int8": 1 / 32}[kv]
+    c = wl.make_gqa([(1, 2000), (400, 1500), (1, 33), (5, 600)], num_q_heads=16, num_kv_heads=4,
+                    head_dim=128, page_size=16, q_dtype=torch.float8_e4m3fn, kv_dtype=kvd,
+                    seed=490, device="cuda", q_value_scale=4.0, k_scale=ks, v_scale=ks,
+                    name=f"fp8q-{kv}")
+    got = _run_gpu(c, q_scale=0.25)
+    assert got.dtype == torch.bfloat16
+    q, qd = storage(c.q)
+    kvs, kd = storage(c.kv_pages)
+    want = oracle.rpa(q, qd, kvs, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
+                      sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale, q_scale=0.25)
+    _check(c, got, want, "fp8" if kv == "fp8" else "bf16")

@@ -120,6 +120,24 @@ def test_mla_explicit_min_share():
         assert_close(as_f64(got), want, *TOL, what=f"share-{sk}")
 
 
+def test_mla_scales_as_the_page_kernel():
+    """q_scale and k_scale on the scores, v_scale on the value sum (the MLA
+    page's kernel), with the fused update."""
+    _say("mla q/k/v scales")
+    c = wl.make_mla([(1, 3000), (2, 500), (1, 64)], num_heads=128, page_size=64, seed=475,
+                    device="cuda", name="mla-scales")
+    ckv, ckp = _host_caches_after_update(c)
+    kl, pi, cu, ns = _meta(c)
+    got = rpa.mla_rpa_forward(c.ql_nope, c.q_pe, c.new_kv_c, c.new_k_pe, c.cache_kv_c,
+                              c.cache_k_pe, kl, pi, cu, ns, sm_scale=c.sm_scale, q_scale=0.5,
+                              k_scale=3.0, v_scale=0.25)
+    torch.cuda.synchronize()
+    want = oracle.mla(storage(c.ql_nope)[0], storage(c.q_pe)[0], oracle.BF16, ckv, ckp, c.kv_lens,
+                      c.page_indices, c.cu_q_lens, c.num_seqs, sm_scale=c.sm_scale, q_scale=0.5,
+                      k_scale=3.0, v_scale=0.25)
+    assert_close(as_f64(got), want, *TOL, what="mla-scales")
+
+
 # ------------------------------------------------------------------ sparse --
 
 def _sparse_gpu(c, indices=None):
