@@ -228,19 +228,29 @@ size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int3
  *   kv_pages  [total_num_pages, page_size, 2*num_kv_heads, head_dim], kv_dtype
  *             (F32, BF16, FP8_E4M3 or INT8 with k_scale/v_scale dequantising
  *             the integers); combined layout, K at 2h, V at 2h+1.
+ *   new_kv    NULL, or the step's new tokens [max_num_tokens, 2*num_kv_heads,
+ *             head_dim] in kv_dtype, laid out as a pool row (K of kv head h at
+ *             2h, V at 2h+1): the call then equals kv_cache_update of these
+ *             rows followed by attention, in one launch sequence. Keys at
+ *             positions >= kv_len - q_len are read from new_kv, and each new
+ *             row is copied to its pool slot (page_indices, kv_len - q_len + j)
+ *             by a launch that reads nothing it writes; a slot past the table
+ *             or on an invalid page is skipped. Two tokens mapping to one slot
+ *             are an error (debug_validate). kv_pages is written only then.
  *   out       [max_num_tokens, num_q_heads, head_dim], q_dtype (BF16 for fp8
  *             queries). Rows of tokens at or past cu_q_lens[num_seqs] are not
  *             written.
  * Requires num_q_heads % num_kv_heads == 0. q head h reads kv head
  * h / (num_q_heads / num_kv_heads). The pool is read only at rows below each
- * sequence's kv_len, so unused pages and stale table entries are never read.
- * New tokens must already be in the pool (call kv_cache_update first).
+ * sequence's kv_len - q_len (below kv_len without new_kv), so unused pages and
+ * stale table entries are never read. Without new_kv the new tokens must
+ * already be in the pool (call kv_cache_update first).
  */
 rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
-                       const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
-                       int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
-                       const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
-                       rpa_stream_t stream);
+                       void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
+                       int32_t page_size, int32_t num_kv_heads, const void* new_kv,
+                       const rpa_ragged_meta* meta, const rpa_opts* opts, void* out,
+                       void* workspace, size_t workspace_bytes, rpa_stream_t stream);
 
 /*
  * rpa_forward without a workspace argument and without any allocation, for
@@ -256,10 +266,10 @@ rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
  * call): calls that overlap in time on one device race, so serialise them.
  */
 rpa_status rpa_forward_noalloc(const void* q, rpa_dtype q_dtype, int32_t num_q_heads,
-                               int32_t head_dim, const void* kv_pages, rpa_dtype kv_dtype,
+                               int32_t head_dim, void* kv_pages, rpa_dtype kv_dtype,
                                int32_t total_num_pages, int32_t page_size, int32_t num_kv_heads,
-                               const rpa_ragged_meta* meta, const rpa_opts* opts, void* out,
-                               rpa_stream_t stream);
+                               const void* new_kv, const rpa_ragged_meta* meta,
+                               const rpa_opts* opts, void* out, rpa_stream_t stream);
 
 /* Bytes of the static per-device scratch array of rpa_forward_noalloc. */
 size_t rpa_noalloc_scratch_bytes(void);

@@ -102,9 +102,9 @@ def load_library():
     lib.rpa_set_profile_events_split.restype = None
     lib.rpa_workspace_size.argtypes = [MP, I32, I32, I32]
     lib.rpa_workspace_size.restype = SZ
-    lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P, SZ, P]
+    lib.rpa_forward.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, P, MP, OP, P, P, SZ, P]
     lib.rpa_forward.restype = I32
-    lib.rpa_forward_noalloc.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, MP, OP, P, P]
+    lib.rpa_forward_noalloc.argtypes = [P, I32, I32, I32, P, I32, I32, I32, I32, P, MP, OP, P, P]
     lib.rpa_forward_noalloc.restype = I32
     lib.rpa_noalloc_scratch_bytes.argtypes = []
     lib.rpa_noalloc_scratch_bytes.restype = SZ
@@ -155,6 +155,14 @@ def _check_dev(*ts):
                 raise ValueError("all tensors must be on the GPU")
             if not t.is_contiguous():
                 raise ValueError("all tensors must be contiguous")
+
+
+def _check_new_kv(new_kv, kv_pages, T):
+    if new_kv is None:
+        return
+    if new_kv.dtype != kv_pages.dtype or tuple(new_kv.shape[1:]) != tuple(kv_pages.shape[2:]) \
+            or new_kv.shape[0] < T:
+        raise ValueError("new_kv must be [T, 2*Hkv, D] in the pool's dtype")
 
 
 def _i32(t):
@@ -253,8 +261,11 @@ def rpa_workspace_size(kv_lens, page_indices, max_num_tokens, num_q_heads, num_k
 def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_scale=1.0,
                 sliding_window=None, soft_cap=None, k_scale=None, v_scale=None, out=None,
                 workspace=None, debug_validate=False, split_keys=None, q_scale=None,
-                stream=None):
+                new_kv=None, stream=None):
     """GQA ragged paged attention (see ``rpa_forward`` in include/rpa.h).
+
+    With ``new_kv`` [T, 2*Hkv, D] (the step's new tokens as pool rows, in the
+    pool's dtype) the call also writes those rows into ``kv_pages``.
 
     q [T, Hq, D] (fp32/bf16, or fp8 e4m3fn with q_scale); kv_pages
     [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn/int8 with k_scale, v_scale);
@@ -263,7 +274,7 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
     """
     torch = _torch()
     lib = load_library()
-    _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out, workspace)
+    _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out, workspace, new_kv)
     T, Hq, D = q.shape
     P, ps, ch, D2 = kv_pages.shape
     if D2 != D or ch % 2:
@@ -277,9 +288,10 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
     need = int(lib.rpa_workspace_size(ctypes.byref(meta), Hq, ch // 2, D))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_new_kv(new_kv, kv_pages, T)
     st = lib.rpa_forward(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages), _dtype_code(kv_pages), P,
-                         ps, ch // 2, ctypes.byref(meta), ctypes.byref(opts), _ptr(out),
-                         _ptr(workspace), workspace.numel(), _stream(stream))
+                         ps, ch // 2, _ptr(new_kv), ctypes.byref(meta), ctypes.byref(opts),
+                         _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
     _raise(lib, st)
     return out
 
@@ -287,11 +299,11 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
 def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, out,
                         sm_scale=1.0, sliding_window=None, soft_cap=None, k_scale=None,
                         v_scale=None, debug_validate=False, split_keys=None, q_scale=None,
-                        stream=None):
+                        new_kv=None, stream=None):
     """rpa_forward on the library's static scratch (see ``rpa_forward_noalloc``
     in include/rpa.h): no workspace and no allocation; ``out`` must be given."""
     lib = load_library()
-    _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out)
+    _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out, new_kv)
     T, Hq, D = q.shape
     P, ps, ch, D2 = kv_pages.shape
     if D2 != D or ch % 2:
@@ -299,9 +311,11 @@ def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs,
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
     opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
                  split_keys, q_scale)
+    _check_new_kv(new_kv, kv_pages, T)
     st = lib.rpa_forward_noalloc(_ptr(q), _dtype_code(q), Hq, D, _ptr(kv_pages),
-                                 _dtype_code(kv_pages), P, ps, ch // 2, ctypes.byref(meta),
-                                 ctypes.byref(opts), _ptr(out), _stream(stream))
+                                 _dtype_code(kv_pages), P, ps, ch // 2, _ptr(new_kv),
+                                 ctypes.byref(meta), ctypes.byref(opts), _ptr(out),
+                                 _stream(stream))
     _raise(lib, st)
     return out
 

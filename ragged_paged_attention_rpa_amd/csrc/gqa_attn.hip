@@ -359,6 +359,7 @@ __device__ __forceinline__ u32x2 vtr(uint32_t tile, uint32_t vx) {
 
 struct TileCtx {
   int seq, kvh, qtok0, ntok, lo, hi, nsplit, first_pos, nrows;
+  int new_start, cu0;  // first position of the step's new tokens, the sequence's first token
 };
 
 __device__ __forceinline__ TileCtx tile_ctx(const GqaArgs& a, const Tile& tile, const SeqInfo& s) {
@@ -383,6 +384,8 @@ __device__ __forceinline__ TileCtx tile_ctx(const GqaArgs& a, const Tile& tile, 
   }
   t.first_pos = s.kv_len - s.q_len + t.qtok0;
   t.nrows = t.ntok * a.geo.group;
+  t.new_start = a.new_kv != nullptr ? s.kv_len - s.q_len : 0x7fffffff;
+  t.cu0 = s.cu0;
   return t;
 }
 
@@ -548,6 +551,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
 
   const int64_t token_bytes = (int64_t)2 * a.num_kv_heads * kD * kEB;
   const char* kv_head = (const char*)a.kv + (int64_t)(2 * t.kvh) * kD * kEB;
+  const char* new_head = (const char*)a.new_kv + (int64_t)(2 * t.kvh) * kD * kEB;
   const uint32_t sbase = lds_addr(sm.stage);
   const uint32_t dma_stride = KV_DT == DT_BF16 ? kStageBytes : kRawStageBytes;
   const uint32_t conv = sbase + NST * kRawStageBytes;  // fp8: converted stage
@@ -568,9 +572,13 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     const int key = kb + 16 * wave + (lane & 15);
     const char* row = (const char*)kZeroKV;
     if (key >= t.lo && key < t.hi) {
-      const int page = sm.pages[(key >> ps_log2) - pwin];
-      if (page >= 0 && page < a.total_num_pages)
-        row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+      if (key >= t.new_start) {
+        row = new_head + (int64_t)(t.cu0 + key - t.new_start) * token_bytes;
+      } else {
+        const int page = sm.pages[(key >> ps_log2) - pwin];
+        if (page >= 0 && page < a.total_num_pages)
+          row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+      }
     }
     const uint32_t rlo = (uint32_t)(uintptr_t)row;
     const uint32_t rhi = (uint32_t)((uintptr_t)row >> 32);
@@ -892,6 +900,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
 
   const int64_t token_bytes = (int64_t)2 * a.num_kv_heads * kD;
   const char* kv_head = (const char*)a.kv + (int64_t)(2 * t.kvh) * kD;
+  const char* new_head = (const char*)a.new_kv + (int64_t)(2 * t.kvh) * kD;
   const uint32_t sbase = lds_addr(sm.stage);
 
   // Block b: wave w moves its own 32 keys, four per instruction (lane L takes
@@ -911,9 +920,13 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
     const int key = kb + kWaveKeys8 * wave + (lane & 31);
     const char* row = (const char*)kZeroKV;
     if (key >= t.lo && key < t.hi) {
-      const int page = sm.pages[(key >> ps_log2) - pwin];
-      if (page >= 0 && page < a.total_num_pages)
-        row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+      if (key >= t.new_start) {
+        row = new_head + (int64_t)(t.cu0 + key - t.new_start) * token_bytes;
+      } else {
+        const int page = sm.pages[(key >> ps_log2) - pwin];
+        if (page >= 0 && page < a.total_num_pages)
+          row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+      }
     }
     const uint32_t rlo = (uint32_t)(uintptr_t)row;
     const uint32_t rhi = (uint32_t)((uintptr_t)row >> 32);
@@ -1068,6 +1081,27 @@ __global__ void __launch_bounds__(kThreads) gqa_merge_kernel(GqaArgs a) {
   const int kvh = blockIdx.x % a.num_kv_heads;
   if (seq >= num_seqs_clamped(a)) return;
   const SeqInfo s = seq_info(a, seq);
+  if (a.new_kv != nullptr) {
+    // The step's new K and V rows of this kv head go to their pool slots. The
+    // attention kernels of this call read those keys from new_kv, never from
+    // these slots, so the copy needs no ordering against them.
+    const int eb = a.kv_dtype == DT_BF16 ? 2 : 1;
+    const int chunks = 2 * kD * eb / 16;  // 16-byte pieces of one K+V row pair
+    const int64_t ch = 2 * a.num_kv_heads;
+    for (int i = threadIdx.x; i < s.q_len * chunks; i += kThreads) {
+      const int j = i / chunks, q = i - j * chunks;
+      const int pos = s.kv_len - s.q_len + j;
+      const int lp = pos / a.page_size;
+      const int page = (pos >= 0 && lp < a.pages_per_seq)
+                           ? a.page_indices[(int64_t)seq * a.pages_per_seq + lp] : -1;
+      if (page < 0 || page >= a.total_num_pages) continue;
+      const int64_t slot = (int64_t)page * a.page_size + pos % a.page_size;
+      const u32x4* sp = reinterpret_cast<const u32x4*>(
+          (const char*)a.new_kv + (((int64_t)(s.cu0 + j) * ch + 2 * kvh) * kD) * eb);
+      u32x4* dp = reinterpret_cast<u32x4*>((char*)a.kv_out + ((slot * ch + 2 * kvh) * kD) * eb);
+      dp[q] = sp[q];
+    }
+  }
   if (!is_decode_class(a, s.q_len)) return;
   int lo, hi, nsplit, chunk;
   decode_range(a, s, &lo, &hi);
@@ -1165,16 +1199,23 @@ __global__ void __launch_bounds__(64) gqa_generic_kernel(GqaArgs a) {
   }
   float m = -INFINITY, l = 0.f;
   const int64_t ch = 2 * a.num_kv_heads;
+  const int new_start = a.new_kv != nullptr ? s.kv_len - s.q_len : 0x7fffffff;
   for (int key = lo; key < hi; ++key) {
-    const int page = a.page_indices[(int64_t)seq * a.pages_per_seq + key / a.page_size];
-    if (page < 0 || page >= a.total_num_pages) continue;
-    const int64_t row = (int64_t)page * a.page_size + key % a.page_size;
-    const int64_t kbase = (row * ch + 2 * kvh) * D;
+    // The step's new tokens come from new_kv, the rest from the pool.
+    const void* src = a.new_kv;
+    int64_t kbase = ((int64_t)(s.cu0 + key - new_start) * ch + 2 * kvh) * D;
+    if (key < new_start) {
+      const int page = a.page_indices[(int64_t)seq * a.pages_per_seq + key / a.page_size];
+      if (page < 0 || page >= a.total_num_pages) continue;
+      const int64_t row = (int64_t)page * a.page_size + key % a.page_size;
+      src = a.kv;
+      kbase = (row * ch + 2 * kvh) * D;
+    }
     float part = 0.f;
 #pragma unroll
     for (int k = 0; k < kMaxChunks; ++k) {
       const int d = lane + 64 * k;
-      if (d < D) part += qf[k] * load_as_f32<float>(a.kv, kbase + d, a.kv_dtype);
+      if (d < D) part += qf[k] * load_as_f32<float>(src, kbase + d, a.kv_dtype);
     }
     float x = wave_sum(part) * a.score_scale;
     if (a.soft_cap != 0.f) x = a.soft_cap * tanhf(x / a.soft_cap);
@@ -1185,7 +1226,7 @@ __global__ void __launch_bounds__(64) gqa_generic_kernel(GqaArgs a) {
 #pragma unroll
     for (int k = 0; k < kMaxChunks; ++k) {
       const int d = lane + 64 * k;
-      const float v = d < D ? load_as_f32<float>(a.kv, kbase + D + d, a.kv_dtype) : 0.f;
+      const float v = d < D ? load_as_f32<float>(src, kbase + D + d, a.kv_dtype) : 0.f;
       acc[k] = acc[k] * alpha + p * v;
     }
     m = m_new;
@@ -1200,6 +1241,19 @@ __global__ void __launch_bounds__(64) gqa_generic_kernel(GqaArgs a) {
       reinterpret_cast<float*>(a.out)[o] = acc[k] * inv;
     else
       reinterpret_cast<uint16_t*>(a.out)[o] = (uint16_t)f32_to_bf16_bits(acc[k] * inv);
+  }
+  // The first q head of each kv head copies this token's K and V rows to the
+  // token's pool slot; no key read in this launch comes from that slot.
+  if (a.new_kv != nullptr && h % G == 0) {
+    const int lp = pos / a.page_size;
+    const int page = lp < a.pages_per_seq ? a.page_indices[(int64_t)seq * a.pages_per_seq + lp] : -1;
+    if (page >= 0 && page < a.total_num_pages) {
+      const int eb = a.kv_dtype == DT_F32 ? 4 : a.kv_dtype == DT_BF16 ? 2 : 1;
+      const int64_t slot = (int64_t)page * a.page_size + pos % a.page_size;
+      const uint8_t* sp = (const uint8_t*)a.new_kv + ((int64_t)tok * ch + 2 * kvh) * D * eb;
+      uint8_t* dp = (uint8_t*)a.kv_out + (slot * ch + 2 * kvh) * D * eb;
+      for (int i = lane; i < 2 * D * eb; i += 64) dp[i] = sp[i];
+    }
   }
 }
 
@@ -1405,7 +1459,7 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   }
 #undef RPA_TILE_LAUNCH
   prof_kernel_end(dstream, 1);
-  if (a.geo.qdec > 0)
+  if (a.geo.qdec > 0 || a.new_kv != nullptr)
     hipLaunchKernelGGL(gqa_merge_kernel, dim3(a.max_num_seqs * a.num_kv_heads), dim3(kThreads),
                        0, dstream, a);
   hipError_t e = hipGetLastError();

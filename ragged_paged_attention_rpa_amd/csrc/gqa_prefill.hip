@@ -158,6 +158,10 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   const int ps_mask = (1 << ps_log2) - 1;
   const int64_t token_bytes = (int64_t)2 * a.num_kv_heads * kD * kEB;
   const char* kv_head = (const char*)a.kv + (int64_t)(2 * kvh) * kD * kEB;
+  // Keys at or past new_start are the step's new tokens, read from new_kv
+  // (same row layout as the pool, one row per packed token).
+  const int new_start = a.new_kv != nullptr ? kv_len - q_len : 0x7fffffff;
+  const char* new_head = (const char*)a.new_kv + (int64_t)(2 * kvh) * kD * kEB;
   const uint32_t sbase = lds_addr(sm.buf);
 
   // LDS byte address of the bf16 block j (j >= -1; block -1 is the zeroed
@@ -201,19 +205,28 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
     const int k8 = kb0 + j * kBN + 8 * wave;
     const bool page_ok = page >= 0 && page < a.total_num_pages;
     const char* rowbase = kv_head + (((int64_t)page << ps_log2) + (k8 & ps_mask)) * token_bytes;
+    // Row of key k8 in new_kv (only lanes whose key is a new token use it).
+    const char* newbase = new_head + (int64_t)(cu0 + k8 - new_start) * token_bytes;
     const uint32_t dst = __builtin_amdgcn_readfirstlane((F8 ? raw_stage(j) : stage(j)) +
                                                        (uint32_t)(wave * kIPW) * 1024);
-    if (page_ok && k8 >= lo && k8 + 8 <= hi) {
+    const bool whole = k8 >= lo && k8 + 8 <= hi;
+    if (whole && page_ok && k8 + 8 <= new_start) {
 #pragma unroll
       for (int ii = 0; ii < kIPW; ++ii) dma_b128_s(rowbase, dofs[ii], dst + (uint32_t)ii * 1024);
+    } else if (whole && k8 >= new_start) {
+#pragma unroll
+      for (int ii = 0; ii < kIPW; ++ii) dma_b128_s(newbase, dofs[ii], dst + (uint32_t)ii * 1024);
     } else {
       const int sub = F8 ? lane >> 4 : lane >> 5;
 #pragma unroll
       for (int ii = 0; ii < kIPW; ++ii) {
         const int key = k8 + (F8 ? 4 : 2) * ii + sub;
-        const bool ok = page_ok && key >= lo && key < hi;
-        const char* src = ok ? rowbase + dofs[ii]
-                             : (const char*)kPreZero + (dofs[ii] & (F8 ? 0xF0u : 0x1F0u));
+        const bool in = key >= lo && key < hi;
+        const char* src = (const char*)kPreZero + (dofs[ii] & (F8 ? 0xF0u : 0x1F0u));
+        if (in && key >= new_start)
+          src = newbase + dofs[ii];
+        else if (in && page_ok)
+          src = rowbase + dofs[ii];
         dma_b128(src, dst + (uint32_t)ii * 1024);
       }
     }

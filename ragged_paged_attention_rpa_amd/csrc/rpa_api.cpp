@@ -264,8 +264,9 @@ namespace {
 // rpa_forward_noalloc, from the library's static per-device scratch array
 // (noalloc: no stream is created, every launch stays on `stream`).
 rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
-                       const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
-                       int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
+                       void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
+                       int32_t page_size, int32_t num_kv_heads, const void* new_kv,
+                       const rpa_ragged_meta* meta,
                        const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
                        bool noalloc, rpa_stream_t stream_) {
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
@@ -290,6 +291,8 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
   rpa::GqaArgs a{};
   a.q = q;
   a.kv = kv_pages;
+  a.new_kv = new_kv;
+  a.kv_out = kv_pages;
   a.out = out;
   a.cu_q_lens = meta->cu_q_lens;
   a.kv_lens = meta->kv_lens;
@@ -314,7 +317,8 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
 
   const bool mfma = rpa::gqa_mfma_supported(a.q_dtype, a.kv_dtype, head_dim,
                                             num_q_heads / num_kv_heads) &&
-                    is_pow2(page_size) && aligned16(q) && aligned16(kv_pages) && aligned16(out);
+                    is_pow2(page_size) && aligned16(q) && aligned16(kv_pages) && aligned16(out) &&
+                    (new_kv == nullptr || aligned16(new_kv));
   if (q_dtype == RPA_FP8_E4M3 && !mfma)
     return fail(RPA_E_UNSUPPORTED,
                 "fp8 queries run on the MFMA path only: head_dim 128, a BF16, FP8_E4M3 or INT8 "
@@ -339,6 +343,7 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
     HostMeta h;
     RPA_TRY(fetch_meta(meta, true, stream, &h));
     RPA_TRY(validate_values(meta, h, page_size, total_num_pages));
+    if (new_kv) RPA_TRY(check_update_slots(meta, h, page_size));
   }
   if (meta->max_num_tokens == 0) return ok();
   if (mfma) {
@@ -367,22 +372,22 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
 extern "C" {
 
 rpa_status rpa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, int32_t head_dim,
-                       const void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
-                       int32_t page_size, int32_t num_kv_heads, const rpa_ragged_meta* meta,
-                       const rpa_opts* opts, void* out, void* workspace, size_t workspace_bytes,
-                       rpa_stream_t stream) {
+                       void* kv_pages, rpa_dtype kv_dtype, int32_t total_num_pages,
+                       int32_t page_size, int32_t num_kv_heads, const void* new_kv,
+                       const rpa_ragged_meta* meta, const rpa_opts* opts, void* out,
+                       void* workspace, size_t workspace_bytes, rpa_stream_t stream) {
   return gqa_forward(q, q_dtype, num_q_heads, head_dim, kv_pages, kv_dtype, total_num_pages,
-                     page_size, num_kv_heads, meta, opts, out, workspace, workspace_bytes, false,
-                     stream);
+                     page_size, num_kv_heads, new_kv, meta, opts, out, workspace, workspace_bytes,
+                     false, stream);
 }
 
 rpa_status rpa_forward_noalloc(const void* q, rpa_dtype q_dtype, int32_t num_q_heads,
-                               int32_t head_dim, const void* kv_pages, rpa_dtype kv_dtype,
+                               int32_t head_dim, void* kv_pages, rpa_dtype kv_dtype,
                                int32_t total_num_pages, int32_t page_size, int32_t num_kv_heads,
-                               const rpa_ragged_meta* meta, const rpa_opts* opts, void* out,
-                               rpa_stream_t stream) {
+                               const void* new_kv, const rpa_ragged_meta* meta,
+                               const rpa_opts* opts, void* out, rpa_stream_t stream) {
   return gqa_forward(q, q_dtype, num_q_heads, head_dim, kv_pages, kv_dtype, total_num_pages,
-                     page_size, num_kv_heads, meta, opts, out, nullptr, 0, true, stream);
+                     page_size, num_kv_heads, new_kv, meta, opts, out, nullptr, 0, true, stream);
 }
 
 size_t rpa_noalloc_scratch_bytes(void) { return rpa::noalloc_scratch_bytes(); }

@@ -58,6 +58,12 @@ struct GqaGeometry {
 struct GqaArgs {
   const void* q;
   const void* kv;
+  // Step's new K/V rows [max_num_tokens, 2*num_kv_heads, head_dim] in the pool
+  // dtype (K of kv head h at 2h, V at 2h+1), or NULL. Keys at positions
+  // >= kv_len - q_len are read from here, and the merge launch copies these
+  // rows to their pool slots.
+  const void* new_kv;
+  void* kv_out;  // the pool as a writable pointer (the slots of new_kv's rows)
   void* out;
   const int32_t* cu_q_lens;
   const int32_t* kv_lens;

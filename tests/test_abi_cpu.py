@@ -72,7 +72,7 @@ def _fwd(lib, Hq=8, D=128, Hkv=2, ps=16, P=32, qd=1, kvd=1, meta=None, opts=None
          ws_bytes=0):
     meta = meta or _meta()
     opts = opts or _opts(lib)
-    return lib.rpa_forward(FAKE, qd, Hq, D, FAKE, kvd, P, ps, Hkv, ctypes.byref(meta),
+    return lib.rpa_forward(FAKE, qd, Hq, D, FAKE, kvd, P, ps, Hkv, None, ctypes.byref(meta),
                            ctypes.byref(opts), FAKE, ws, ws_bytes, None)
 
 
@@ -178,7 +178,7 @@ def test_noalloc_rejects_capacities_beyond_its_scratch_before_any_launch(lib):
     assert cap == 96 << 20
     big = _meta(S=4096, pps=512, T=4096)
     assert lib.rpa_workspace_size(ctypes.byref(big), 32, 8, 128) > cap
-    st = lib.rpa_forward_noalloc(FAKE, 1, 32, 128, FAKE, 1, 64, 16, 8, ctypes.byref(big),
+    st = lib.rpa_forward_noalloc(FAKE, 1, 32, 128, FAKE, 1, 64, 16, 8, None, ctypes.byref(big),
                                  ctypes.byref(_opts(lib)), FAKE, None)
     assert st == RPA_E_WORKSPACE
     assert "rpa_forward_noalloc holds at most" in lib.rpa_last_error().decode()

@@ -594,3 +594,54 @@ def test_fp8_queries_with_q_scale(kv):
     want = oracle.rpa(q, qd, kvs, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
                       sm_scale=c.sm_scale, k_scale=c.k_scale, v_scale=c.v_scale, q_scale=0.25)
     _check(c, got, want, "fp8" if kv == "fp8" else "bf16")
+
+
+FUSED_CASES = {
+    # (seqs, Hq, Hkv, D, page size, pool dtype, window, cap, kernel path)
+    "bf16-prefill-kernel": ([(1, 3000), (300, 1200), (1, 17), (64, 64), (1, 9000), (700, 2100)],
+                            16, 4, 128, 16, torch.bfloat16, 2500, 30.0, "gqa_mfma_prefill"),
+    "fp8-decode8": ([(1, 3000), (130, 900), (1, 1), (2, 5000)], 32, 8, 128, 16,
+                    torch.float8_e4m3fn, None, 50.0, "gqa_mfma_prefill"),
+    "int8-tile-ps4": ([(1, 3000), (40, 700), (1, 17), (1, 9000), (3, 64)], 32, 8, 128, 4,
+                      torch.int8, 1000, None, "gqa_mfma"),
+    "bf16-generic-d64": ([(1, 300), (5, 70), (1, 1), (17, 17)], 8, 2, 64, 16, torch.bfloat16,
+                         None, None, "gqa_generic"),
+}
+
+
+@pytest.mark.parametrize("mode", list(FUSED_CASES))
+def test_fused_cache_update(mode):
+    """rpa_forward with the step's new rows (new_kv): the pool afterwards is
+    bit-exact against the oracle's scatter, the outputs match the oracle on
+    the updated pool, and they equal kv_cache_update + rpa_forward bit for bit
+    (the keys of the step's tokens come from new_kv, the same values)."""
+    seqs, hq, hkv, d, ps, kvd, win, cap, path = FUSED_CASES[mode]
+    _say(f"fused cache update ({mode})")
+    scales = {torch.float8_e4m3fn: 0.5, torch.int8: 1 / 32}.get(kvd)
+    c = wl.make_gqa(seqs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, page_size=ps,
+                    q_dtype=torch.bfloat16, kv_dtype=kvd, seed=500, device="cuda",
+                    sliding_window=win, soft_cap=cap, k_scale=scales, v_scale=scales,
+                    spare_pages=2, name=f"fused-{mode}")
+    T = int(c.cu_q_lens[-1])
+    new_kv = wl.randn((T, 2 * hkv, d), kvd, wl._gen("cuda", 501), "cuda")
+    host = storage(c.kv_pages)[0].copy()
+    oracle.kv_update(oracle.LAYOUT_COMBINED_GQA, storage(new_kv[:, 0::2])[0],
+                     storage(new_kv[:, 1::2])[0], host, None, storage(c.kv_pages)[1],
+                     kv_lens=c.kv_lens, page_indices=c.page_indices, cu_q_lens=c.cu_q_lens,
+                     num_seqs=c.num_seqs)
+    two_step_pool = c.kv_pages.clone()
+    got = _run_gpu(c, new_kv=new_kv, debug_validate=True)
+    assert rpa.last_path() == path
+    assert np.array_equal(storage(c.kv_pages)[0], host)
+    kl, pi, cu, ns = _dev_meta(c)
+    rpa.kv_cache_update(rpa.LAYOUT_COMBINED_GQA, new_kv[:, 0::2].contiguous(),
+                        new_kv[:, 1::2].contiguous(), two_step_pool, kv_lens=kl, page_indices=pi,
+                        cu_q_lens=cu, num_seqs=ns)
+    ref = rpa.rpa_forward(c.q, two_step_pool, kl, pi, cu, ns, sm_scale=c.sm_scale,
+                          sliding_window=c.sliding_window, soft_cap=c.soft_cap,
+                          k_scale=c.k_scale, v_scale=c.v_scale)
+    torch.cuda.synchronize()
+    rows = slice(0, T)
+    assert torch.equal(got[rows], ref[rows])
+    want = _run_oracle(c)  # the device pool is the updated one (checked above)
+    _check(c, got, want, "fp8" if kvd == torch.float8_e4m3fn else "bf16")
