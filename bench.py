@@ -166,10 +166,17 @@ class HipEvents:
             assert self.hip.hipEventCreate(ctypes.byref(b)) == 0
             self.pairs.append((a, b))
 
-    def elapsed_ms(self, k):
+    def elapsed_ms(self, k, missing_ok=False):
+        """Milliseconds between pair k's events; with missing_ok, None when the
+        pair was never recorded (its kernel was not launched)."""
         ms = self._ct.c_float()
         rc = self.hip.hipEventElapsedTime(self._ct.byref(ms), self.pairs[k][0], self.pairs[k][1])
         if rc != 0:
+            if missing_ok:
+                # Clear the error the query left as HIP's last error, which the
+                # library's next launch check would otherwise report.
+                self.hip.hipGetLastError()
+                return None
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
@@ -228,13 +235,42 @@ def timed_loop(torch, rpa, fn, steps, warmup, split=False, flush=None):
     parts = {"kernel_ms_min": float(np.min(kern))}
     if split:
         lib.rpa_set_profile_events_split(None, None, None, None)
-        pre = [evs.elapsed_ms(2 * k) for k in range(steps)]
+        # The prefill-tile kernel is not launched on a batch without room for
+        # prefill chunks (its events then stay unrecorded).
+        pre = [evs.elapsed_ms(2 * k, missing_ok=True) for k in range(steps)]
         dec = [evs.elapsed_ms(2 * k + 1) for k in range(steps)]
         evs.close()
-        parts.update(prefill_kernel_ms=float(np.mean(pre)), decode_kernel_ms=float(np.mean(dec)),
-                     prefill_kernel_ms_min=float(np.min(pre)),
+        pre_ok = all(p is not None for p in pre)
+        parts.update(prefill_kernel_ms=float(np.mean(pre)) if pre_ok else None,
+                     decode_kernel_ms=float(np.mean(dec)),
+                     prefill_kernel_ms_min=float(np.min(pre)) if pre_ok else None,
                      decode_kernel_ms_min=float(np.min(dec)))
     return (t1 - t0) * 1e3 / steps, float(np.mean(kern)), float(np.median(kern)), parts
+
+
+def graph_loop(torch, fn, steps, warmup):
+    """Wall ms per step of `steps` replays of one captured call of `fn` (a HIP
+    graph: the call's launches without host launch overhead), after `warmup`
+    untimed replays, between two device synchronisations."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del g
+    return ms
 
 
 def measure(args, torch, rpa, fn, split=False):
@@ -250,6 +286,12 @@ def measure(args, torch, rpa, fn, split=False):
         cold = timed_loop(torch, rpa, fn, args.steps, max(1, args.warmup // 2), split,
                           flush=lambda: cache_flush(torch))
     warm = timed_loop(torch, rpa, fn, args.steps, args.warmup, split) if mode != "cold" else None
+    if warm is not None and getattr(args, "graph", "on") == "on":
+        # The step the line reports: the call replayed from a HIP graph, as a
+        # serving loop issues it; the eager wall time stays beside it.
+        gms = graph_loop(torch, fn, args.steps, args.warmup)
+        warm[3]["ms_per_step_eager"] = warm[0]
+        warm = (gms,) + tuple(warm[1:])
     return (warm or cold), cold
 
 
@@ -491,6 +533,7 @@ def bench_latent(args, torch, rpa, wl):
         ach = work["kv_bytes"] / (kmean / 1e3) / 1e9
         res = {"value": gbs, "unit": "GB/s", "ms_per_step": ms, "kernel_ms_mean": kmean,
                "kernel_ms_median": kmed, "kernel_ms_min": kparts["kernel_ms_min"],
+               "ms_per_step_eager": kparts.get("ms_per_step_eager"),
                "cold": cold_summary(cold), "ms_per_step_attention_only": ms_attn,
                "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
                "tokens_per_s": work["q_tokens"] / (ms / 1e3),
@@ -538,6 +581,7 @@ def bench_latent(args, torch, rpa, wl):
     ach = work["flops"] / (kmean / 1e3) / 1e12
     res = {"value": tf, "unit": "TFLOP/s", "ms_per_step": ms, "kernel_ms_mean": kmean,
            "kernel_ms_median": kmed, "kernel_ms_min": kparts["kernel_ms_min"],
+           "ms_per_step_eager": kparts.get("ms_per_step_eager"),
            "cold": cold_summary(cold),
            "pct_mfma_peak": 100 * tf / BF16_PEAK_TFLOPS,
            "gathered_gbs_in_kernel": work["gathered_bytes"] / (kmean / 1e3) / 1e9,
@@ -594,6 +638,9 @@ def main():
                          "(off for profiling runs of the decode kernel alone)")
     ap.add_argument("--extras-cpu-budget", type=float, default=8.0,
                     help="target seconds of oracle CPU work for each extra workload")
+    ap.add_argument("--graph", choices=("on", "off"), default="on",
+                    help="time the steps as replays of a captured HIP graph of the call (on), "
+                         "or as eager calls (off); the eager time is reported either way")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many bytes "
                          "(calibration run for the PMC byte counters)")
@@ -619,6 +666,7 @@ def main():
     res, cfg = run_config(args, torch, rpa, wl)
     line = {"metric": METRIC, "value": res.pop("value"), "unit": res.pop("unit"), "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.pop("ms_per_step"),
+            "step_timing": "hip_graph_replay" if args.graph == "on" else "eager_calls",
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16" if args.config != "tiny_gqa" else "f32", "data": "synthetic",
             "config": cfg}

@@ -351,7 +351,16 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
     // The prefill kernel takes row maxima on raw scores, which needs an
     // increasing logit map: a positive score scale.
     a.single_stream = noalloc ? 1 : 0;
-    if (a.score_scale > 0.f &&
+    // A bf16 batch whose token capacity leaves fewer than kPrefillMinTokens
+    // tokens beyond one per sequence (a batch of decodes) keeps every tile on
+    // the tile kernel: an empty prefill launch costs more than the rare short
+    // chunk gains from it. One-byte pools keep the prefill kernel, whose
+    // launch brings the one-byte decode kernel.
+    constexpr int64_t kPrefillMinTokens = 256;
+    const bool room_for_prefill =
+        a.kv_dtype != (int)RPA_BF16 ||
+        (int64_t)meta->max_num_tokens - meta->max_num_seqs >= kPrefillMinTokens;
+    if (a.score_scale > 0.f && room_for_prefill &&
         rpa::gqa_prefill_supported(a.q_dtype, a.kv_dtype, head_dim, a.geo.group, page_size)) {
       // Prefill-class tiles of 256 rows for the eight-wave kernel (fewer tiles
       // than the workspace was sized for).

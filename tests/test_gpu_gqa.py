@@ -87,14 +87,23 @@ RAGGED = [
 ]
 
 
+@pytest.mark.parametrize("room", ["tight", "room"])
 @pytest.mark.parametrize("idx", range(len(RAGGED)), ids=[r[-1] for r in RAGGED])
-def test_ragged_bf16(idx):
+def test_ragged_bf16(idx, room):
+    """Each ragged case twice: with the token capacity the batch needs (a bf16
+    batch with fewer than 256 tokens beyond one per sequence keeps every tile
+    on the tile kernel) and with 300 spare tokens of capacity (prefill-class
+    tiles on the prefill kernel)."""
     seqs, Hq, Hkv, ps, window, cap, name = RAGGED[idx]
-    _say(f"ragged bf16 {name}")
+    _say(f"ragged bf16 {name} ({room})")
     c = wl.make_gqa(seqs, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=128, page_size=ps,
                     q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=100 + idx,
-                    device="cuda", sliding_window=window, soft_cap=cap, name=name)
+                    device="cuda", sliding_window=window, soft_cap=cap, name=name,
+                    extra_tokens=300 if room == "room" else 0)
     _check(c, _run_gpu(c), _run_oracle(c), "bf16")
+    extra = int(c.q.shape[0]) - c.num_seqs
+    if ps >= 8:
+        assert rpa.last_path() == ("gqa_mfma_prefill" if extra >= 256 else "gqa_mfma")
 
 
 @pytest.mark.parametrize("idx", range(len(RAGGED)), ids=[r[-1] for r in RAGGED])
@@ -511,6 +520,11 @@ def test_first_call_under_capture_stays_on_one_stream():
 def test_last_path_names_the_kernel_path():
     _say("rpa_last_path")
     c = wl.make_gqa([(1, 100), (40, 200)], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                    page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=91,
+                    device="cuda")
+    _run_gpu(c)
+    assert rpa.last_path() == "gqa_mfma"          # bf16, no room for a prefill chunk
+    c = wl.make_gqa([(1, 100), (400, 600)], num_q_heads=8, num_kv_heads=2, head_dim=128,
                     page_size=16, q_dtype=torch.bfloat16, kv_dtype=torch.bfloat16, seed=91,
                     device="cuda")
     _run_gpu(c)
