@@ -641,6 +641,10 @@ def main():
     ap.add_argument("--graph", choices=("on", "off"), default="on",
                     help="time the steps as replays of a captured HIP graph of the call (on), "
                          "or as eager calls (off); the eager time is reported either way")
+    ap.add_argument("--probe", action="store_true",
+                    help="instead of the benchmark, run the ceiling probes (LDS-DMA streaming "
+                         "read, MFMA / LDS / exp issue rates, MFMA chain clocks per step) and "
+                         "print one JSON line per measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many bytes "
                          "(calibration run for the PMC byte counters)")
@@ -654,6 +658,11 @@ def main():
     import ragged_paged_attention_rpa_amd as rpa
     from ragged_paged_attention_rpa_amd import workloads as wl
     rpa.load_library()
+    if args.probe:
+        from ragged_paged_attention_rpa_amd import probes
+        for row in probes.run_all(torch):
+            print(json.dumps(row), flush=True)
+        return
     if args.copy_bytes:
         n = args.copy_bytes // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")

@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "librpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["rpa_api.cpp", "tile_table.cpp", "kv_update.hip", "gqa_attn.hip", "gqa_prefill.hip",
-           "mla_attn.hip", "mla_decode.hip"]
+           "mla_attn.hip", "mla_decode.hip", "probes.hip"]
 
 # Packed-fp32 VALU ops stay off: the compiler must not emit v_pk_{add,mul,fma}_f32.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

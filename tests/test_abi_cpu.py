@@ -11,6 +11,7 @@ import ragged_paged_attention_rpa_amd as rpa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rpa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "rpa_probe.h")
 
 RPA_E_INVALID, RPA_E_SHAPE, RPA_E_DTYPE, RPA_E_UNSUPPORTED, RPA_E_WORKSPACE = 1, 2, 3, 4, 5
 
@@ -23,8 +24,8 @@ def lib():
     return rpa.load_library()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\*?\s+\*?([a-z_][a-z0-9_]*)\s*\(",
                        text, flags=re.M)
@@ -39,8 +40,30 @@ def test_header_declares_the_four_operations():
 
 
 def test_every_declared_symbol_is_exported(lib):
-    for name in _declared_functions():
+    for name in _declared_functions() + _declared_functions(PROBE_HEADER):
         assert hasattr(lib, name), f"{name} not exported by librpa.so"
+
+
+def test_probe_header_declares_the_three_probes():
+    assert _declared_functions(PROBE_HEADER) == ["rpa_probe_chain", "rpa_probe_rate",
+                                                 "rpa_probe_stream"]
+
+
+def test_probes_reject_invalid_arguments(lib):
+    from ragged_paged_attention_rpa_amd import probes
+    probes._lib()
+    fake, st = 0x10000, None
+    assert lib.rpa_probe_stream(None, 1 << 30, 256, 1, st) == RPA_E_INVALID
+    assert lib.rpa_probe_stream(fake, 1 << 30, 0, 1, st) == RPA_E_INVALID
+    assert lib.rpa_probe_stream(fake, 1 << 30, 65537, 0, st) == RPA_E_INVALID
+    assert lib.rpa_probe_stream(fake, 32 * 1024 * 256 - 1, 256, 1, st) == RPA_E_INVALID
+    assert lib.rpa_probe_rate(3, 256, fake, st) == RPA_E_INVALID
+    assert lib.rpa_probe_rate(-1, 256, fake, st) == RPA_E_INVALID
+    assert lib.rpa_probe_rate(0, 256, None, st) == RPA_E_INVALID
+    for mode in (1, 3, 16, -2):
+        assert lib.rpa_probe_chain(mode, 256, fake, fake, st) == RPA_E_INVALID
+    assert lib.rpa_probe_chain(0, 0, fake, fake, st) == RPA_E_INVALID
+    assert lib.rpa_probe_chain(0, 256, None, fake, st) == RPA_E_INVALID
 
 
 def _meta(S=4, pps=8, T=16):
