@@ -345,7 +345,10 @@ struct MlaSmem {
 static_assert(sizeof(MlaSmem) <= 160 * 1024, "MLA LDS budget");
 
 // One piece: the 128 heads of head group hg of one query token over keys
-// [lo, hi).
+// [lo, hi). CAP: the soft cap is set (a compile-time switch: as a run-time
+// flag the compiler if-converts the logit map, and every block then pays for
+// the capped map's transcendentals).
+template <bool CAP>
 __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, int ps_log2) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -501,7 +504,7 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
   mfma_agpr_fence();
   float m_run = -INFINITY, l_run = 0.f;
 
-  const bool capped = a.soft_cap != 0.f;
+  constexpr bool capped = CAP;
   const float c1 = capped ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
   const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
   auto logit = [&](float sraw) -> float {
@@ -760,6 +763,7 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
   }
 }
 
+template <bool CAP>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_tile_kernel(MlaArgs a, int ps_log2) {
   __shared__ __attribute__((aligned(1024))) MlaSmem sm;
@@ -768,7 +772,7 @@ mla_tile_kernel(MlaArgs a, int ps_log2) {
   for (int p = p0; p < p1; ++p) {
     const int4 r0 = reinterpret_cast<const int4*>(a.pieces)[2 * p];
     const int4 r1 = reinterpret_cast<const int4*>(a.pieces)[2 * p + 1];
-    process_piece(a, r0, r1, sm, ps_log2);
+    process_piece<CAP>(a, r0, r1, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -878,7 +882,10 @@ hipError_t launch_mla(const MlaArgs& a, hipStream_t stream) {
   while ((1 << ps_log2) < a.page_size) ++ps_log2;
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(kThreads), 0, stream, a);
   prof_begin(stream);
-  hipLaunchKernelGGL(mla_tile_kernel, dim3(kMlaGrid), dim3(kThreads), 0, stream, a, ps_log2);
+  if (a.soft_cap != 0.f)
+    hipLaunchKernelGGL(mla_tile_kernel<true>, dim3(kMlaGrid), dim3(kThreads), 0, stream, a, ps_log2);
+  else
+    hipLaunchKernelGGL(mla_tile_kernel<false>, dim3(kMlaGrid), dim3(kThreads), 0, stream, a, ps_log2);
   prof_end(stream);
   const int hg = (a.num_heads + kHeadsPerWg - 1) / kHeadsPerWg;
   hipLaunchKernelGGL(mla_merge_kernel, dim3(hg * a.max_num_tokens, kHeadsPerWg * 64 / kThreads),
