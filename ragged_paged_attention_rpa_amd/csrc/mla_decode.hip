@@ -535,10 +535,15 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
 #pragma unroll
   for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 
-  auto kread = [&](uint32_t stb, int st) -> u32x4 {
-    return st < 32 ? lds_read_b128(stb + xor_here(klat, (uint32_t)(st << 4)))
-                   : lds_read_b128(stb + xor_here(krope, (uint32_t)((st - 32) << 5)));
+  // K operand of k-step st from the per-stage bases kl = stage + klat and
+  // kp = stage + krope: stage addresses are multiples of 512 bytes, so the
+  // column XOR (bits 4..8, or 5..6 for the rope part) commutes with adding
+  // the stage address and each read costs one XOR.
+  auto kread = [&](uint32_t kl, uint32_t kp, int st) -> u32x4 {
+    return st < 32 ? lds_read_b128(xor_here(kl, (uint32_t)(st << 4)))
+                   : lds_read_b128(xor_here(kp, (uint32_t)((st - 32) << 5)));
   };
+  static_assert(kStageBytes % 512 == 0, "stage bases must leave the swizzle bits alone");
 
   // MODE 0: QK only (j = -1); 1: QK + softmax of a stage inside [lo, hi);
   // 2: QK + softmax of a stage that needs the key mask; 3: masked softmax
@@ -555,9 +560,10 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
     float mblk = -INFINITY, mref = 0.f, psum = 0.f;
     constexpr int kAheadK = 4;  // K reads run four k-steps ahead of their MFMAs
     u32x4 kr[kAheadK];
+    const uint32_t kl = qst + klat, kp = qst + krope;
     if constexpr (do_qk) {
 #pragma unroll
-      for (int i = 0; i < kAheadK; ++i) kr[i] = kread(qst, i);
+      for (int i = 0; i < kAheadK; ++i) kr[i] = kread(kl, kp, i);
 #pragma unroll
       for (int r = 0; r < 16; ++r) sn[r] = 0.f;
     }
@@ -567,7 +573,7 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
         u32x4 kf = kr[st % kAheadK];
         pin_after(kf);
         sn = mfma_32x32x16(as_bf16x8(kf), as_bf16x8(qv[st]), sn);
-        if (st + kAheadK < kSteps) kr[st % kAheadK] = kread(qst, st + kAheadK);
+        if (st + kAheadK < kSteps) kr[st % kAheadK] = kread(kl, kp, st + kAheadK);
         // Stage j + 3's loads go out together after the first MFMA: their
         // addresses then die at once (spreading them keeps them live across
         // the k-steps, which the register budget does not allow).
@@ -674,12 +680,15 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
     // u takes keys 16u + 4c + {0..3, 8..11}; each V^T operand feeds the four
     // head tiles. The flags, the first weights and the first V^T operand are
     // read together.
+    // Per-stage bases as for K: the dims XOR (bits 6..9) commutes with adding
+    // the stage address, and the 16-key step is the read's offset field.
     const uint32_t cur = stage_addr(j);
+    const uint32_t vlb = cur + vlo, vhb = cur + vhi;
     auto vread = [&](int u, int d) -> u32x4 {
-      const uint32_t b = cur + (uint32_t)(u * 16 * kKvcBytes);
       const uint32_t dsel = (uint32_t)((kDtPerWave * wave + d) << 6);
-      const u32x2 v0 = lds_read_tr16(b + xor_here(vlo, dsel));
-      const u32x2 v1 = lds_read_tr16(b + xor_here(vhi, dsel));
+      const uint32_t ub = (uint32_t)(u * 16 * kKvcBytes);
+      const u32x2 v0 = lds_read_tr16(xor_here(vlb, dsel) + ub);
+      const u32x2 v1 = lds_read_tr16(xor_here(vhb, dsel) + ub);
       return u32x4{v0[0], v0[1], v1[0], v1[1]};
     };
     const int4 flags = *reinterpret_cast<const int4*>(sm.rescale);
