@@ -253,9 +253,9 @@ __global__ void __launch_bounds__(kThreads) mla_plan_kernel(MlaArgs a) {
 // values in AGPRs between statements; the rare rescale and the final read go
 // through acc_read / acc_write. The compiler does not see MFMAs inside asm, so
 // the wait states they need are explicit: 24 between an MFMA result and a
-// v_accvgpr_read (acc_read), mfma_agpr_fence() after writes before the next
-// MFMA reads the tile, and operand_fence() between the VALU writes of the
-// packed weights and the MFMAs that read them.
+// v_accvgpr_read (acc_read) and mfma_agpr_fence() after writes before the
+// next MFMA reads the tile. Their A and B operands come straight from LDS
+// reads (no VALU write precedes them).
 #define RPA_WAIT24 "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
 
 __device__ __forceinline__ void acc_mfma(floatx16& acc, const u32x4& a, const u32x4& b) {
@@ -310,13 +310,6 @@ __device__ __forceinline__ floatx16 acc_read(int dt, const floatx16& acc) {
     default: break;
   }
   return x;
-}
-
-// The packed softmax weights are written by VALU conversions and read by the
-// asm MFMAs right after: a few wait states between them (the operands are
-// tied to this statement, so the writes stay above it).
-__device__ __forceinline__ void operand_fence(u32x4 (&pb)[2]) {
-  asm volatile("s_nop 4" : "+v"(pb[0]), "+v"(pb[1]));
 }
 
 // Workgroup barrier after this wave's LDS writes have landed; unlike
@@ -507,9 +500,11 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
   constexpr bool capped = CAP;
   const float c1 = capped ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
   const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
+  // A masked key's raw score is -inf (mask_pass) and its logit stays -inf.
   auto logit = [&](float sraw) -> float {
     if (!capped) return sraw * c1;
-    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
+    const float x = c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
+    return sraw == -INFINITY ? -INFINITY : x;
   };
 
   // Lane operand offsets within a stage.
@@ -525,15 +520,18 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
     vhi = (uint32_t)(k_hi * kKvcBytes + ((x ^ swz(k_hi)) << 4) + 8 * (jj & 1));
   }
 
-  // Software pipeline over the stages: iteration j (from -1) multiplies
-  // S^T(j+1) = K Q^T on the matrix cores while the VALU runs the online
-  // softmax of stage j (its scores came out of the previous iteration) between
-  // those MFMAs, then hands P(j) to the other waves and adds V^T P^T(j).
-  // Stage buffers in use during iteration j: j (PV), j + 1 (QK), j + 2 (in
-  // flight), j + 3 (loads issued during the QK).
-  floatx16 sc, sn;  // S^T of stage j (being softmaxed) and of stage j + 1
-#pragma unroll
-  for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+  // Software pipeline over the stages. Iteration j (0 .. nst - 1):
+  //   S^T(j+1) = K Q^T on stage j + 1: a plain chain of MFMAs with its K
+  //   reads (the loads of stage j + 3 go out at its first step);
+  //   O^T += V^T P^T(j) on stage j, with the online softmax of S(j+1) spread
+  //   between those MFMAs (the PV MFMAs keep their accumulators in AGPRs, so
+  //   the VALU work beside them costs little issue time);
+  //   after a barrier (every wave is done with P(j)), P(j+1) and its rescale
+  //   factors are published in LDS for iteration j + 1.
+  // Iteration -1 computes S(0), its softmax and P(0) alone. Stage buffers in
+  // use during iteration j: j (PV), j + 1 (QK), j + 2 (in flight), j + 3
+  // (loads issued during the QK).
+  floatx16 sn;  // S^T of the next stage, softmaxed in place
 
   // K operand of k-step st from the per-stage bases kl = stage + klat and
   // kp = stage + krope: stage addresses are multiples of 512 bytes, so the
@@ -545,141 +543,102 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
   };
   static_assert(kStageBytes % 512 == 0, "stage bases must leave the swizzle bits alone");
 
-  // MODE 0: QK only (j = -1); 1: QK + softmax of a stage inside [lo, hi);
-  // 2: QK + softmax of a stage that needs the key mask; 3: masked softmax
-  // only (the last stage). The softmax work is spread over the 36 k-steps:
-  // logits and the block max at steps 0..15, the reference update at 16, the
-  // weights at 17..32, their bf16 packing at 33.
-  auto qk_soft = [&](auto MODE, uint32_t qst, uint32_t nxt, bool more, uint64_t nkvc,
-                     uint64_t nkpe, int kb, u32x4 (&pb)[2], float& alpha, int& moved) {
-    constexpr int mode = decltype(MODE)::value;
-    constexpr bool do_qk = mode != 3, do_soft = mode != 0, full = mode == 1;
-    // Register r holds key kb + 8(r/4) + 4c + r%4; the window relative to
-    // this lane's register-0 key.
-    const int lo_r = lo - (kb + 4 * c), hi_r = hi - (kb + 4 * c);
-    float mblk = -INFINITY, mref = 0.f, psum = 0.f;
+  auto qk = [&](uint32_t qst, uint32_t nxt, bool more, uint64_t nkvc, uint64_t nkpe) {
     constexpr int kAheadK = 4;  // K reads run four k-steps ahead of their MFMAs
     u32x4 kr[kAheadK];
     const uint32_t kl = qst + klat, kp = qst + krope;
-    if constexpr (do_qk) {
 #pragma unroll
-      for (int i = 0; i < kAheadK; ++i) kr[i] = kread(kl, kp, i);
+    for (int i = 0; i < kAheadK; ++i) kr[i] = kread(kl, kp, i);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sn[r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) sn[r] = 0.f;
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
-      if constexpr (do_qk) {
-        u32x4 kf = kr[st % kAheadK];
-        pin_after(kf);
-        sn = mfma_32x32x16(as_bf16x8(kf), as_bf16x8(qv[st]), sn);
-        if (st + kAheadK < kSteps) kr[st % kAheadK] = kread(kl, kp, st + kAheadK);
-        // Stage j + 3's loads go out together after the first MFMA: their
-        // addresses then die at once (spreading them keeps them live across
-        // the k-steps, which the register budget does not allow).
-        if (more && st == 0) {
+      u32x4 kf = kr[st % kAheadK];
+      pin_after(kf);
+      sn = mfma_32x32x16(as_bf16x8(kf), as_bf16x8(qv[st]), sn);
+      if (st + kAheadK < kSteps) kr[st % kAheadK] = kread(kl, kp, st + kAheadK);
+      // Stage j + 3's loads go out together after the first MFMA: their
+      // addresses then die at once (spreading them keeps them live across
+      // the k-steps, which the register budget does not allow).
+      if (more && st == 0) {
 #pragma unroll
-          for (int k = 0; k < kDmaPerWave; ++k) dma(nxt, nkvc, nkpe, k);
-        }
-      }
-      if constexpr (do_soft) {
-        if (st < 16) {
-          float x = logit(sc[st]);
-          if constexpr (!full) {
-            const int off = 8 * (st >> 2) + (st & 3);
-            x = (off >= lo_r && off < hi_r) ? x : -INFINITY;
-          }
-          pin_here(x);
-          sc[st] = x;
-          mblk = fmaxf(mblk, x);
-        } else if (st == 16) {
-          // Lane l ^ 32 holds the other 16 keys of the same head.
-          mblk = wave_max_xor<32>(mblk);
-          const bool need = mblk > m_run + kLazyTau;
-          moved = __builtin_amdgcn_readfirstlane(wave_any(need) ? 1 : 0);
-          alpha = need ? fast_exp2(m_run - mblk) : 1.f;  // rows not moving keep scale 1
-          l_run *= alpha;
-          m_run = need ? mblk : m_run;
-          mref = m_run == -INFINITY ? 0.f : m_run;  // no visible key yet: weights 0
-          pin_here(mref);
-        } else if (st <= 32) {
-          const int r = st - 17;
-          float e = fast_exp2(sc[r] - mref);
-          pin_here(e);
-          sc[r] = e;
-          psum += e;
-        } else if (st == 33) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pb[u][i] = pack_bf16x2(sc[8 * u + 2 * i], sc[8 * u + 2 * i + 1]);
-          pin_here(pb[0]);
-          pin_here(pb[1]);
-        }
+        for (int k = 0; k < kDmaPerWave; ++k) dma(nxt, nkvc, nkpe, k);
       }
     }
-    if constexpr (do_soft) l_run += psum;
   };
 
-  // Iteration -1 (S^T of stage 0 only), then iterations 0 .. nst - 1.
-  auto pre_stage = [&](int j, bool has_qk, bool& more, uint64_t& nkvc, uint64_t& nkpe) {
-    // Stage j + 1 landed once this wave's loads of stage j + 2 are all that
-    // is outstanding (the last iteration has none left). The barrier makes
-    // every wave's part visible, and every wave is past PV(j - 1): stage
-    // j - 1's buffer is free for stage j + 3, and the weights, scales and
-    // flags of j - 1 in LDS may be overwritten.
-    if (has_qk && j + 2 < nst)
-      wait_vmcnt<kDmaPerWave>();
-    else
-      wait_vmcnt<0>();
-    wg_barrier();
-    more = j + kStages - 1 < nst;
-    nkvc = 0;
-    nkpe = 0;
-    if (more) prep(j + kStages - 1, &nkvc, &nkpe);
+  // Raw scores of keys outside [lo, hi) become -inf, for a stage whose first
+  // key is kb (register r holds key kb + 8(r/4) + 4c + r%4). Run before the
+  // softmax of a stage that crosses lo or hi.
+  auto mask_pass = [&](int kb) {
+    const uint32_t span = (uint32_t)(hi - lo);
+    const int base = kb + 4 * c - lo;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const bool vis = (uint32_t)(base + 8 * (r >> 2) + (r & 3)) < span;
+      sn[r] = vis ? sn[r] : -INFINITY;
+    }
   };
-  if (nst > 0) {
-    bool more;
-    uint64_t nkvc, nkpe;
-    pre_stage(-1, true, more, nkvc, nkpe);
-    u32x4 pb[2];
-    float alpha = 1.f;
-    int moved = 0;
-    qk_soft(std::integral_constant<int, 0>{}, stage_addr(0), stage_addr(kStages - 2), more, nkvc,
-            nkpe, kb0 - kBlk, pb, alpha, moved);
-    sc = sn;
-  }
-#pragma unroll 1
-  for (int j = 0; j < nst; ++j) {
-    const bool has_qk = j + 1 < nst;
-    bool more;
-    uint64_t nkvc, nkpe;
-    pre_stage(j, has_qk, more, nkvc, nkpe);
-    const uint32_t qst = stage_addr(j + 1);
-    const uint32_t nxt = stage_addr(j + kStages - 1);
-    const int kb = kb0 + j * kBlk;
-    u32x4 pb[2];
-    float alpha = 1.f;
-    int moved = 0;
-    if (!has_qk)
-      qk_soft(std::integral_constant<int, 3>{}, qst, nxt, more, nkvc, nkpe, kb, pb, alpha, moved);
-    else if (kb >= lo && kb + kBlk <= hi)
-      qk_soft(std::integral_constant<int, 1>{}, qst, nxt, more, nkvc, nkpe, kb, pb, alpha, moved);
-    else
-      qk_soft(std::integral_constant<int, 2>{}, qst, nxt, more, nkvc, nkpe, kb, pb, alpha, moved);
 
-    // Hand the weights (and rescale factors) of this wave's heads to every
-    // wave: they are the B operands of the PV products of head tile `wave`.
+  // Softmax item t (0 .. 33) of the scores in sn: logits and the block max at
+  // t = 0..15, the reference update at 16, the weights at 17..32, their bf16
+  // packing at 33. The input is pinned where the item starts and the result
+  // where it ends, so the item's VALU work stays between the MFMAs around it.
+  struct SoftState {
+    float mblk, mref, psum, alpha;
+    int moved;
+  };
+  auto soft_item = [&](int t, SoftState& ss, u32x4 (&pb)[2]) {
+    if (t < 16) {
+      float x = sn[t];
+      pin_here(x);
+      x = logit(x);
+      pin_here(x);
+      sn[t] = x;
+      ss.mblk = fmaxf(ss.mblk, x);
+    } else if (t == 16) {
+      // Lane l ^ 32 holds the other 16 keys of the same head.
+      float mb = ss.mblk;
+      pin_here(mb);
+      mb = wave_max_xor<32>(mb);
+      const bool need = mb > m_run + kLazyTau;
+      ss.moved = __builtin_amdgcn_readfirstlane(wave_any(need) ? 1 : 0);
+      ss.alpha = need ? fast_exp2(m_run - mb) : 1.f;  // rows not moving keep scale 1
+      l_run *= ss.alpha;
+      m_run = need ? mb : m_run;
+      ss.mref = m_run == -INFINITY ? 0.f : m_run;  // no visible key yet: weights 0
+      pin_here(ss.mref);
+    } else if (t <= 32) {
+      const int r = t - 17;
+      float x = sn[r];
+      pin_here(x);
+      float e = fast_exp2(x - ss.mref);
+      pin_here(e);
+      sn[r] = e;
+      ss.psum += e;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[u][i] = pack_bf16x2(sn[8 * u + 2 * i], sn[8 * u + 2 * i + 1]);
+      pin_here(pb[0]);
+      pin_here(pb[1]);
+      l_run += ss.psum;
+    }
+  };
+  auto publish = [&](const u32x4 (&pb)[2], const SoftState& ss) {
     sm.pex[wave][0][lane] = pb[0];
     sm.pex[wave][1][lane] = pb[1];
-    if (lane < 32) sm.alpha[wave][lane] = alpha;
-    if (lane == 0) sm.rescale[wave] = moved;
-    lds_barrier();
+    if (lane < 32) sm.alpha[wave][lane] = ss.alpha;
+    if (lane == 0) sm.rescale[wave] = ss.moved;
+  };
 
-    // ---- O^T += V^T P^T(j) for dims 128*wave .. +127 of all 128 heads: k-step
-    // u takes keys 16u + 4c + {0..3, 8..11}; each V^T operand feeds the four
-    // head tiles. The flags, the first weights and the first V^T operand are
-    // read together.
+  // O^T += V^T P^T(j) for dims 128*wave .. +127 of all 128 heads (k-step u
+  // takes keys 16u + 4c + {0..3, 8..11}; each V^T operand feeds the four head
+  // tiles), with the softmax items of the scores in sn after the MFMAs. (One
+  // copy of this code serves every iteration: more copies in the loop body
+  // make the register allocator spill.)
+  auto pv_soft = [&](int j, u32x4 (&pb)[2], SoftState& ss) {
     // Per-stage bases as for K: the dims XOR (bits 6..9) commutes with adding
     // the stage address, and the 16-key step is the read's offset field.
     const uint32_t cur = stage_addr(j);
@@ -691,13 +650,15 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
       const u32x2 v1 = lds_read_tr16(xor_here(vhb, dsel) + ub);
       return u32x4{v0[0], v0[1], v1[0], v1[1]};
     };
+    // The flags, the first weights and the first V^T operand are read
+    // together.
     const int4 flags = *reinterpret_cast<const int4*>(sm.rescale);
     u32x4 pbh[kWaves];
 #pragma unroll
     for (int h = 0; h < kWaves; ++h) pbh[h] = sm.pex[h][0][lane];
     u32x4 vf = vread(0, 0);
 
-    // ---- rescale the accumulators of head tiles whose reference moved (the
+    // Rescale the accumulators of head tiles whose reference moved (the
     // common case skips it all).
     const int rs_any = __builtin_amdgcn_readfirstlane(flags.x | flags.y | flags.z | flags.w);
     if (rs_any) {
@@ -731,11 +692,78 @@ __device__ void process_piece(const MlaArgs& a, int4 r0, int4 r1, MlaSmem& sm, i
         if (n < 2 * kDtPerWave) vn = vread(n / kDtPerWave, n % kDtPerWave);
         pin_after(vf);
 #pragma unroll
-        for (int h = 0; h < kWaves; ++h) acc_mfma(acc[d][h], vf, pbh[h]);
+        for (int h = 0; h < kWaves; ++h) {
+          acc_mfma(acc[d][h], vf, pbh[h]);
+          const int t = 4 * (kDtPerWave * u + d) + h;  // 0 .. 31
+          soft_item(t, ss, pb);
+          if (t == 31) {
+            soft_item(32, ss, pb);
+            soft_item(33, ss, pb);
+          }
+        }
         vf = vn;
       }
     }
-    sc = sn;
+  };
+
+  // Iteration -1: S(0), its softmax and P(0).
+  auto pre_stage = [&](int j, bool has_qk, bool& more, uint64_t& nkvc, uint64_t& nkpe) {
+    // Stage j + 1 landed once this wave's loads of stage j + 2 are all that
+    // is outstanding (the last iteration has none left). The barrier (after
+    // this wave's LDS writes of P(j) have completed) makes every wave's part
+    // visible, and every wave is past PV(j - 1): stage j - 1's buffer is free
+    // for stage j + 3.
+    if (has_qk && j + 2 < nst)
+      wait_vmcnt<kDmaPerWave>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    more = j + kStages - 1 < nst;
+    nkvc = 0;
+    nkpe = 0;
+    if (more) prep(j + kStages - 1, &nkvc, &nkpe);
+  };
+  auto soft_alone = [&](u32x4 (&pb)[2], SoftState& ss) {
+#pragma unroll
+    for (int t = 0; t < 34; ++t) soft_item(t, ss, pb);
+  };
+  if (nst > 0) {
+    bool more;
+    uint64_t nkvc, nkpe;
+    pre_stage(-1, true, more, nkvc, nkpe);
+    qk(stage_addr(0), stage_addr(kStages - 2), more, nkvc, nkpe);
+    u32x4 pb[2];
+    SoftState ss{-INFINITY, 0.f, 0.f, 1.f, 0};
+    if (!(kb0 >= lo && kb0 + kBlk <= hi)) mask_pass(kb0);
+    soft_alone(pb, ss);
+    publish(pb, ss);
+  }
+#pragma unroll 1
+  for (int j = 0; j < nst; ++j) {
+    const bool has_qk = j + 1 < nst;
+    bool more;
+    uint64_t nkvc, nkpe;
+    pre_stage(j, has_qk, more, nkvc, nkpe);
+    u32x4 pb[2];
+    SoftState ss{-INFINITY, 0.f, 0.f, 1.f, 0};
+    const int kbn = kb0 + (j + 1) * kBlk;  // first key of stage j + 1
+    if (has_qk) {
+      qk(stage_addr(j + 1), stage_addr(j + kStages - 1), more, nkvc, nkpe);
+      if (!(kbn >= lo && kbn + kBlk <= hi)) mask_pass(kbn);
+    }
+    // The last iteration has no next stage: its softmax items run on stale
+    // scores and everything they produce is dropped.
+    const float m_keep = m_run, l_keep = l_run;
+    pv_soft(j, pb, ss);
+    if (has_qk) {
+      // Every wave is done reading P(j) and its rescale factors. (An early
+      // exit from the loop here instead makes the register allocator spill.)
+      wg_barrier();
+      publish(pb, ss);
+    } else {
+      m_run = m_keep;
+      l_run = l_keep;
+    }
   }
 
   // ---- end of piece: every wave needs the row sums of all 128 heads.
