@@ -129,11 +129,10 @@ __device__ __forceinline__ uint32_t v_lat() {
 // lane operand addresses of the first tile (stage included). Each K read
 // feeds NH MFMAs; the NT tiles give independent accumulation chains. The K
 // reads run AH k-steps ahead of their MFMAs (an LDS round trip takes several
-// MFMAs). after_step(j) runs after the MFMAs of k-step j (the callers issue
-// the next block's DMA from it, spread over the k-steps).
-template <int NT, int NH, int AH, typename F>
+// MFMAs).
+template <int NT, int NH, int AH>
 __device__ __forceinline__ void score_tiles(floatx4 (&sv)[NT][NH], uint32_t lat, uint32_t rope,
-                                            const u32x4 (&qv)[NH][kQSteps], F&& after_step) {
+                                            const u32x4 (&qv)[NH][kQSteps]) {
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -164,7 +163,6 @@ __device__ __forceinline__ void score_tiles(floatx4 (&sv)[NT][NH], uint32_t lat,
 #pragma unroll
       for (int t = 0; t < NT; ++t) ring[j % AH][t] = kread(j + AH, t);
     }
-    after_step(j);
   }
 }
 
@@ -173,8 +171,6 @@ __device__ __forceinline__ float score_log2(float s, float sc, float cap) {
   if (cap != 0.f) return cap * tanh_def(s * sc / cap) * kLog2e;
   return s * sc * kLog2e;
 }
-
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 
 // ============================================================ sparse ========
@@ -293,33 +289,35 @@ sparse_mla_kernel(SparseArgs a) {
   const uint32_t klat = k_lat() + wave * kTileKvc;
   const uint32_t krope = k_rope() + wave * kTileKpe;
   const uint32_t vlat = v_lat() + wave * kTileKvc;
-  uint64_t vm_cur[kSpGroups] = {0, 0}, vm_next[kSpGroups] = {0, 0};
-  drain_vmem_before_loop();
-  if (nblk > 0) {
-    int rows0[kSpGroups];
-    prep_rows(0, rows0, vm_next);
+  // Validity masks of the blocks in the two stages.
+  uint64_t vm_st[2][kSpGroups] = {{0, 0}, {0, 0}};
+  // Block b goes to stage b % 2 as soon as every wave is done with block
+  // b - 2 there, so while a block is multiplied the next one is in flight,
+  // and while a wave waits for that one the block after it is too.
+  auto issue_block = [&](int b, uint32_t stage) {
+    int rows[kSpGroups];
+    prep_rows(b, rows, vm_st[b & 1]);
 #pragma unroll
     for (int j = 0; j < kSpIPW; ++j)
-      issue_key_dma(src, st0, kSpGroups * wave + j / kDmaPer8, rows0[j / kDmaPer8], j % kDmaPer8);
-  }
+      issue_key_dma(src, stage, kSpGroups * wave + j / kDmaPer8, rows[j / kDmaPer8], j % kDmaPer8);
+  };
+  drain_vmem_before_loop();
+  if (nblk > 0) issue_block(0, st0);
+  if (nblk > 1) issue_block(1, st1);
   for (int b = 0; b < nblk; ++b) {
     const uint32_t cur = (b & 1) ? st1 : st0;
-    const uint32_t nxt = (b & 1) ? st0 : st1;
-    vm_cur[0] = vm_next[0];
-    vm_cur[1] = vm_next[1];
-    // Block b was issued during the previous block's work; after the barrier
-    // every wave is also done with stage nxt, which block b + 1 now fills.
-    wait_vmcnt<0>();
+    // Block b has landed once only block b + 1's loads (if any) are
+    // outstanding; the barrier makes every wave's part of it visible.
+    if (b + 1 < nblk)
+      wait_vmcnt<kSpIPW>();
+    else
+      wait_vmcnt<0>();
     wg_barrier();
-    const bool more = b + 1 < nblk;
-    int nrows[kSpGroups] = {-1, -1};
-    if (more) prep_rows(b + 1, nrows, vm_next);
+    uint64_t vm_cur[kSpGroups];
+    vm_cur[0] = vm_st[b & 1][0];
+    vm_cur[1] = vm_st[b & 1][1];
     floatx4 sv2[1][1];
-    // One DMA instruction of block b + 1 after each of the 18 k-steps.
-    score_tiles<1, 1, kSpAhead>(sv2, (cur + klat), (cur + krope), qv, [&](int j) {
-      if (more)
-        issue_key_dma(src, nxt, kSpGroups * wave + j / kDmaPer8, nrows[j / kDmaPer8], j % kDmaPer8);
-    });
+    score_tiles<1, 1, kSpAhead>(sv2, (cur + klat), (cur + krope), qv);
     floatx4 sv = sv2[0][0];
     // Keys 4g + i of this wave's tile: group g/2, bit 8*(4(g&1) + i) of its mask.
     const uint64_t vm = (g >> 1) ? vm_cur[1] : vm_cur[0];
@@ -369,6 +367,11 @@ sparse_mla_kernel(SparseArgs a) {
         if (dt + kSpVAhead < kDvTiles)
           vr[dt % kSpVAhead] = lds_read_tr16(xor_here(cur + vlat, (uint32_t)((dt + kSpVAhead) << 5)));
       }
+    }
+    if (b + 2 < nblk) {
+      // Every wave is done reading stage cur: block b + 2 takes it.
+      wg_barrier();
+      issue_block(b + 2, cur);
     }
   }
   // The four waves hold the softmax state of disjoint key tiles: merge in LDS.
