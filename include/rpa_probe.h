@@ -8,7 +8,7 @@
  *                     LDS-DMA scheme (global_load_lds_dwordx4, 1 KB per
  *                     instruction, two 32 KB stages per workgroup, no compute);
  *   rpa_probe_rate    issue throughput of one instruction kind per CU:
- *                     32x32x16 bf16 MFMA, ds_read_b128, v_exp_f32;
+ *                     32x32x16 bf16 MFMA, ds_read_b128, v_exp_f32, v_fma_f32;
  *   rpa_probe_chain   shader clocks (s_memtime) per step of a dependent chain
  *                     of 36 32x32x16 bf16 MFMAs per loop trip, alone or next
  *                     to the VALU and LDS work a softmax step adds.
@@ -48,7 +48,8 @@ int rpa_probe_stream(const void* buf, size_t bytes, int workgroups, int interlea
  * kind 1: ds_read_b128 over a 64 KiB LDS array, 4096 reads per wave
  *         (16 MiB read per workgroup);
  * kind 2: v_exp_f32 in eight independent chains, 4096 per wave
- *         (16,384 wave-instructions per workgroup).
+ *         (16,384 wave-instructions per workgroup);
+ * kind 3: v_fma_f32 likewise (16,384 wave-instructions per workgroup).
  * `sink` receives workgroups * 256 floats (values meaningless; they keep the
  * work live). workgroups in [1, 65536].
  */

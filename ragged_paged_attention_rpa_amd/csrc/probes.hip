@@ -117,7 +117,8 @@ __global__ void __launch_bounds__(kProbeThreads, 1) probe_chain_kernel(unsigned 
 }
 
 // Throughput loops, timed by the caller: KIND 0 four independent MFMA chains
-// per wave; 1 ds_read_b128 streams over a 64 KB LDS array; 2 v_exp_f32.
+// per wave; 1 ds_read_b128 streams over a 64 KB LDS array; 2 v_exp_f32;
+// 3 v_fma_f32 (eight independent chains per lane in both VALU kinds).
 constexpr int kRateIters = 4096;
 template <int KIND>
 __global__ void __launch_bounds__(kProbeThreads) probe_rate_kernel(float* sink) {
@@ -159,7 +160,8 @@ __global__ void __launch_bounds__(kProbeThreads) probe_rate_kernel(float* sink) 
     for (int i = 0; i < 8; ++i) v[i] = 0.01f * (threadIdx.x + i);
     for (int it = 0; it < kRateIters / 8; ++it) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = __builtin_amdgcn_exp2f(-v[i]);
+      for (int i = 0; i < 8; ++i)
+        v[i] = KIND == 2 ? __builtin_amdgcn_exp2f(-v[i]) : __builtin_fmaf(v[i], 0.999f, 0.001f);
     }
     for (int i = 0; i < 8; ++i) out += v[i];
   }
@@ -213,6 +215,8 @@ hipError_t probe_rate(int kind, int grid, float* sink, hipStream_t stream) {
     hipLaunchKernelGGL(probe_rate_kernel<1>, dim3(grid), dim3(kProbeThreads), 0, stream, sink);
   else if (kind == 2)
     hipLaunchKernelGGL(probe_rate_kernel<2>, dim3(grid), dim3(kProbeThreads), 0, stream, sink);
+  else if (kind == 3)
+    hipLaunchKernelGGL(probe_rate_kernel<3>, dim3(grid), dim3(kProbeThreads), 0, stream, sink);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -234,7 +238,7 @@ extern "C" int rpa_probe_stream(const void* buf, size_t bytes, int workgroups, i
 }
 
 extern "C" int rpa_probe_rate(int kind, int workgroups, float* sink, rpa_stream_t stream) {
-  if (!sink || kind < 0 || kind > 2 || workgroups < 1 || workgroups > kMaxProbeGrid)
+  if (!sink || kind < 0 || kind > 3 || workgroups < 1 || workgroups > kMaxProbeGrid)
     return RPA_E_INVALID;
   return launched(rpa::probe_rate(kind, workgroups, sink, stream));
 }

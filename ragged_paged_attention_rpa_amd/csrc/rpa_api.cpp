@@ -6,6 +6,7 @@
 // caller asks for them (debug_validate), as the pages' runtime validators do
 // [RPA v2 page: dynamic_validate_inputs; MLA v1 page: dynamic_validate_inputs].
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -35,6 +36,26 @@ rpa_status fail(rpa_status st, const char* fmt, ...) {
   g_last_error = buf;
   return st;
 }
+
+// A roctx range around one call's launches, named after the operation and
+// the sizes that shape its tiles, like the pages' profiler scope names [MLA
+// v1 page: mla_ragged_paged_attention, named_scope]. rocprofv3
+// --marker-trace records them; without a profiler attached a range costs one
+// formatted string and two library calls.
+class TraceRange {
+ public:
+  explicit TraceRange(const char* fmt, ...) {
+    char buf[160];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    roctxRangePushA(buf);
+  }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 rpa_status ok() {
   g_last_error.clear();
@@ -367,10 +388,13 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
       a.pre_kernel = 1;
       a.geo.bq = rpa::gqa_prefill_rows() / a.geo.group;
     }
+    TraceRange range("RPA-gqa-bq%d-kvs%d-p%d-g%d%s", a.geo.bq, a.geo.split_keys, page_size,
+                     a.geo.group, a.pre_kernel ? "-prefill" : "");
     const rpa_status st = hip_status(rpa::launch_gqa(a, stream), "rpa_forward launch");
     if (st == RPA_OK) g_last_path = a.pre_kernel ? "gqa_mfma_prefill" : "gqa_mfma";
     return st;
   }
+  TraceRange range("RPA-gqa-generic-d%d-p%d-g%d", head_dim, page_size, a.geo.group);
   const rpa_status st = hip_status(rpa::launch_gqa_generic(a, stream), "rpa_forward launch");
   if (st == RPA_OK) g_last_path = "gqa_generic";
   return st;
@@ -479,6 +503,7 @@ rpa_status kv_cache_update(rpa_cache_layout layout, const void* new_a, const voi
     a.max_num_seqs = meta->max_num_seqs;
     a.pages_per_seq = meta->pages_per_seq;
   }
+  TraceRange range("RPA-kv_update-layout%d-t%d", (int)layout, num_tokens);
   return hip_status(rpa::launch_kv_update(a, num_tokens, stream), "kv_cache_update launch");
 }
 
@@ -562,6 +587,7 @@ rpa_status mla_rpa_forward(const void* ql_nope, const void* q_pe, const void* ne
   a.min_share = resolve_tile_keys(rpa::kTileMlaShare, opts, (int)dtype, lkv_dim + r_dim, 1, meta,
                                   page_size, nullptr);
   rpa::mla_bind_workspace(a, workspace);
+  TraceRange range("RPA-mla-h%d-share%d-p%d", num_heads, a.min_share, page_size);
   return hip_status(rpa::launch_mla(a, stream), "mla_rpa_forward launch");
 }
 
@@ -641,6 +667,7 @@ rpa_status sparse_mla_forward(const void* q, const void* kv_cache, const int32_t
   if (seq_len < 0) return fail(RPA_E_INVALID, "seq_len=%d must be >= 0", seq_len);
   if (num_queries == 0) return ok();
   a.seq_len = seq_len;
+  TraceRange range("RPA-sparse-k%d-rb%d-p%d", top_k, read_block, page_size);
   return hip_status(rpa::launch_sparse_mla(a, stream), "sparse_mla_forward launch");
 }
 
@@ -668,6 +695,7 @@ rpa_status sparse_mla_forward_ragged(const void* q, const void* kv_cache,
   a.seq_lens = seq_lens;
   a.cu_kv_lens = cu_kv_lens;
   a.num_seqs = num_seqs;
+  TraceRange range("RPA-sparse-ragged-k%d-rb%d-p%d-s%d", top_k, read_block, page_size, num_seqs);
   return hip_status(rpa::launch_sparse_mla(a, stream), "sparse_mla_forward_ragged launch");
 }
 

@@ -14,8 +14,9 @@ import ctypes
 NOMINAL_GHZ = 2.4
 THREADS = 256
 CHAIN_STEPS = 256 * 36
-RATE_PER_WG = {0: (536870912.0, "flop"), 1: (16777216.0, "byte"), 2: (16384.0, "wave_instr")}
-RATE_NAMES = {0: "mfma_32x32x16_bf16", 1: "ds_read_b128", 2: "v_exp_f32"}
+RATE_PER_WG = {0: (536870912.0, "flop"), 1: (16777216.0, "byte"), 2: (16384.0, "wave_instr"),
+               3: (16384.0, "wave_instr")}
+RATE_NAMES = {0: "mfma_32x32x16_bf16", 1: "ds_read_b128", 2: "v_exp_f32", 3: "v_fma_f32"}
 CHAIN_NAMES = {0: "mfma chain, accumulator in VGPRs", 2: "+ 4 VALU per step",
                4: "+ 1 LDS operand read per step", 6: "+ 4 VALU + 1 LDS read per step",
                8: "mfma chain, accumulator in AGPRs", 10: "AGPR + 4 VALU per step",
@@ -114,7 +115,7 @@ def chain(torch, mode):
 
 def run_all(torch):
     rows = [stream(torch, wg_per_cu=w, interleave=il) for il in (True, False) for w in (2, 1)]
-    for kind in (0, 1, 2):
+    for kind in (0, 1, 2, 3):
         for w in (1, 2):
             rows.append(rate(torch, kind, w))
     for mode in sorted(CHAIN_NAMES):
