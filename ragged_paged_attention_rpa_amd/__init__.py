@@ -25,7 +25,9 @@ __all__ = ["rpa_forward", "kv_cache_update", "mla_rpa_forward", "sparse_mla_forw
            "LAYOUT_COMBINED_GQA", "LAYOUT_MLA_SPLIT", "LAYOUT_MLA_FUSED", "EXPORTED_SYMBOLS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librpa.so")
+# RPA_LIBRARY names another build of the library (e.g. the host-sanitized one
+# the CPU tests make); by default the in-tree librpa.so.
+LIB_PATH = os.environ.get("RPA_LIBRARY") or os.path.join(_HERE, "librpa.so")
 
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
 EXPORTED_SYMBOLS = ("rpa_opts_init", "rpa_last_error", "rpa_last_path", "rpa_set_profile_events",
