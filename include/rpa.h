@@ -70,7 +70,12 @@ typedef enum {
   RPA_E_HIP = 6          /* the HIP runtime reported an error */
 } rpa_status;
 
-typedef enum { RPA_F32 = 0, RPA_BF16 = 1, RPA_FP8_E4M3 = 2, RPA_INT8 = 3 } rpa_dtype;
+/* RPA_INT4: signed 4-bit integers (two's complement, -8..7), two per byte
+ * along the innermost index, element 2i in the low nibble of byte i; a row
+ * of head_dim values takes head_dim / 2 bytes [RPA v2 page:
+ * strided_load_kv, eight values per 32-bit word]. KV pools of rpa_forward
+ * only. */
+typedef enum { RPA_F32 = 0, RPA_BF16 = 1, RPA_FP8_E4M3 = 2, RPA_INT8 = 3, RPA_INT4 = 4 } rpa_dtype;
 
 typedef enum {
   RPA_LAYOUT_COMBINED_GQA = 0, /* [P, ps, 2*Hkv, D]: K of kv head h at 2h, V at 2h+1 */
@@ -226,8 +231,9 @@ size_t rpa_workspace_size(const rpa_ragged_meta* meta, int32_t num_q_heads, int3
  *             head_dim 128, a BF16/FP8/INT8 pool, power-of-two page size,
  *             16-byte aligned q, kv_pages and out, else RPA_E_UNSUPPORTED).
  *   kv_pages  [total_num_pages, page_size, 2*num_kv_heads, head_dim], kv_dtype
- *             (F32, BF16, FP8_E4M3 or INT8 with k_scale/v_scale dequantising
- *             the integers); combined layout, K at 2h, V at 2h+1.
+ *             (F32, BF16, FP8_E4M3, or INT8 / INT4 with k_scale/v_scale
+ *             dequantising the integers; INT4 needs an even head_dim and runs
+ *             on the generic kernel); combined layout, K at 2h, V at 2h+1.
  *   new_kv    NULL, or the step's new tokens [max_num_tokens, 2*num_kv_heads,
  *             head_dim] in kv_dtype, laid out as a pool row (K of kv head h at
  *             2h, V at 2h+1): the call then equals kv_cache_update of these

@@ -26,7 +26,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rpa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8_E4M3, INT8 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, INT8, INT4 = 0, 1, 2, 3, 4
 LAYOUT_COMBINED_GQA, LAYOUT_MLA_SPLIT, LAYOUT_MLA_FUSED = 0, 1, 2
 
 _lib = None
@@ -102,7 +102,8 @@ def _c(a, dtype=None):
 
 def _storage(a, dtype):
     """Raw storage array for one of the oracle's dtype codes."""
-    want = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, INT8: np.int8}[dtype]
+    want = {F32: np.float32, BF16: np.uint16, FP8_E4M3: np.uint8, INT8: np.int8,
+            INT4: np.uint8}[dtype]
     a = np.ascontiguousarray(a)
     if a.dtype != want:
         raise TypeError(f"expected storage dtype {want} for code {dtype}, got {a.dtype}")
@@ -132,7 +133,8 @@ def rpa(q, q_dtype, kv_pages, kv_dtype, kv_lens, page_indices, cu_q_lens, num_se
     kv_pages = _storage(kv_pages, kv_dtype)
     T, Hq, D = q.shape
     P, ps, ch, D2 = kv_pages.shape
-    assert D2 == D and ch % 2 == 0
+    # INT4 storage: two values per byte along the last index.
+    assert (2 * D2 if kv_dtype == INT4 else D2) == D and ch % 2 == 0
     kv_lens = _c(kv_lens, np.int32)
     cu_q_lens = _c(cu_q_lens, np.int32)
     pi = _c(page_indices, np.int32)
@@ -235,7 +237,8 @@ def kv_update(layout, new_a, new_b, cache_a, cache_b, dtype, *, kv_lens=None,
     """Scatter new tokens into the caches IN PLACE (numpy arrays)
     [MLA v1 page: update_kv_cache; Sparse page: prefill_write_and_attend].
 
-    COMBINED_GQA: new_a = K [T, Hkv, D], new_b = V [T, Hkv, D], cache_a [P, ps, 2Hkv, D].
+    COMBINED_GQA: new_a = K [T, Hkv, D], new_b = V [T, Hkv, D], cache_a [P, ps, 2Hkv, D]
+                  (INT4: packed bytes, last dimension D / 2).
     MLA_SPLIT: new_a = kv_c [T, Dl], new_b = k_pe [T, Dr], cache_a [P, ps, >=Dl],
                cache_b [P, ps, >=Dr] (pad columns written as 0).
     MLA_FUSED: cache_a [P, ps, >=Dl+Dr] receives [kv_c || k_pe || 0].
@@ -247,7 +250,7 @@ def kv_update(layout, new_a, new_b, cache_a, cache_b, dtype, *, kv_lens=None,
     P, ps = cache_a.shape[0], cache_a.shape[1]
     T = new_a.shape[0]
     if layout == LAYOUT_COMBINED_GQA:
-        heads, dim_a = new_a.shape[1], new_a.shape[2]
+        heads, dim_a = new_a.shape[1], new_a.shape[2] * (2 if dtype == INT4 else 1)
         dim_b, stride_a, stride_b = dim_a, 0, 0
     else:
         heads = 0

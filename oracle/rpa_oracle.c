@@ -40,7 +40,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_INT8 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_INT8 = 3, OR_INT4 = 4 };
 enum { OR_LAYOUT_COMBINED_GQA = 0, OR_LAYOUT_MLA_SPLIT = 1, OR_LAYOUT_MLA_FUSED = 2 };
 
 /* ---- storage decoders (own implementations, from the format definitions) ---- */
@@ -75,6 +75,14 @@ static double load_elem(const void* base, int dtype, int64_t idx) {
     case OR_FP8_E4M3: return dec_e4m3fn(((const uint8_t*)base)[idx]);
     /* two's-complement byte: the integer it encodes (dequantised by the caller's scale) */
     case OR_INT8: return (double)((const int8_t*)base)[idx];
+    /* two values per byte along the innermost index, element 2i in the low
+     * four bits of byte i, each a two's-complement nibble -8..7
+     * [RPA v2 page: strided_load_kv, eight 4-bit values per 32-bit word] */
+    case OR_INT4: {
+      const uint8_t b = ((const uint8_t*)base)[idx / 2];
+      const int v = (idx % 2 == 0) ? (b & 0xF) : (b >> 4);
+      return (double)(v < 8 ? v : v - 16);
+    }
   }
   return NAN;
 }
@@ -144,6 +152,7 @@ int oracle_rpa(const void* q, int q_dtype, int num_tokens, int num_q_heads, int 
                int sliding_window, double soft_cap, double k_scale, double v_scale,
                double q_scale, const int32_t* token_list, int n_list, double* out) {
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  if (kv_dtype == OR_INT4 && head_dim % 2 != 0) return -5;
   const int group = num_q_heads / num_kv_heads;
   const int ch = 2 * num_kv_heads;
   for (int i = 0; i < num_seqs; ++i) {
@@ -413,8 +422,12 @@ int oracle_kv_update(int layout, const void* new_a, const void* new_b, void* cac
                      int dim_a, int dim_b, int stride_a, int stride_b, const int32_t* kv_lens,
                      const int32_t* page_indices, int pages_per_seq, const int32_t* cu_q_lens,
                      int num_seqs, const int32_t* slot_loc, int num_tokens) {
+  /* Bytes per element; INT4 rows (combined layout only, even dim_a) take
+   * dim_a / 2 bytes, two values per byte. */
   const int eb = dtype_bytes(dtype);
-  if (eb == 0) return -1;
+  if (eb == 0 && !(dtype == OR_INT4 && layout == OR_LAYOUT_COMBINED_GQA && dim_a % 2 == 0))
+    return -1;
+  const int64_t row_a = dtype == OR_INT4 ? dim_a / 2 : (int64_t)dim_a * eb;
   const int64_t n_slots = (int64_t)total_num_pages * page_size;
   const int n_tok = slot_loc ? num_tokens : (num_seqs > 0 ? cu_q_lens[num_seqs] : 0);
   for (int t = 0; t < n_tok; ++t) {
@@ -436,10 +449,10 @@ int oracle_kv_update(int layout, const void* new_a, const void* new_b, void* cac
     if (slot >= n_slots) return -5;
     if (layout == OR_LAYOUT_COMBINED_GQA) {
       for (int h = 0; h < heads; ++h) {
-        memcpy((char*)cache_a + ((slot * 2 * heads + 2 * h) * dim_a) * eb,
-               (const char*)new_a + (((int64_t)t * heads + h) * dim_a) * eb, (size_t)dim_a * eb);
-        memcpy((char*)cache_a + ((slot * 2 * heads + 2 * h + 1) * dim_a) * eb,
-               (const char*)new_b + (((int64_t)t * heads + h) * dim_a) * eb, (size_t)dim_a * eb);
+        memcpy((char*)cache_a + (slot * 2 * heads + 2 * h) * row_a,
+               (const char*)new_a + ((int64_t)t * heads + h) * row_a, (size_t)row_a);
+        memcpy((char*)cache_a + (slot * 2 * heads + 2 * h + 1) * row_a,
+               (const char*)new_b + ((int64_t)t * heads + h) * row_a, (size_t)row_a);
       }
     } else if (layout == OR_LAYOUT_MLA_SPLIT) {
       char* da = (char*)cache_a + slot * stride_a * eb;

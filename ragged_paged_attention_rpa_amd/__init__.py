@@ -143,7 +143,14 @@ def _dtype_code(t):
         return 2
     if t.dtype == torch.int8:
         return 3
+    if t.dtype == torch.uint8:
+        return 4  # a packed INT4 pool: two values per byte, element 2i in the low nibble
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _pool_head_dim(kv_pages):
+    """head_dim of a [P, ps, 2*Hkv, D] pool (a packed INT4 pool stores D / 2 bytes)."""
+    return kv_pages.shape[3] * (2 if kv_pages.dtype == _torch().uint8 else 1)
 
 
 def _ptr(t):
@@ -270,7 +277,9 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
     pool's dtype) the call also writes those rows into ``kv_pages``.
 
     q [T, Hq, D] (fp32/bf16, or fp8 e4m3fn with q_scale); kv_pages
-    [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn/int8 with k_scale, v_scale);
+    [P, ps, 2*Hkv, D] (fp32/bf16/fp8 e4m3fn/int8 with k_scale, v_scale), or
+    uint8 [P, ps, 2*Hkv, D/2] holding packed int4 values (two per byte, element
+    2i in the low nibble);
     kv_lens [S], page_indices [S, pps] or [S*pps], cu_q_lens [S+1], num_seqs [1]
     (int32, on the GPU). Returns ``out`` [T, Hq, D] in q's dtype (bf16 for fp8 q).
     """
@@ -278,9 +287,9 @@ def rpa_forward(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, *, sm_s
     lib = load_library()
     _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out, workspace, new_kv)
     T, Hq, D = q.shape
-    P, ps, ch, D2 = kv_pages.shape
-    if D2 != D or ch % 2:
-        raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
+    P, ps, ch, _ = kv_pages.shape
+    if _pool_head_dim(kv_pages) != D or ch % 2:
+        raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim] (head_dim / 2 bytes for int4)")
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn
                           else q.dtype, device=q.device)
@@ -307,9 +316,9 @@ def rpa_forward_noalloc(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs,
     lib = load_library()
     _check_dev(q, kv_pages, kv_lens, page_indices, cu_q_lens, num_seqs, out, new_kv)
     T, Hq, D = q.shape
-    P, ps, ch, D2 = kv_pages.shape
-    if D2 != D or ch % 2:
-        raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim]")
+    P, ps, ch, _ = kv_pages.shape
+    if _pool_head_dim(kv_pages) != D or ch % 2:
+        raise ValueError("kv_pages must be [P, ps, 2*Hkv, head_dim] (head_dim / 2 bytes for int4)")
     meta = _meta(kv_lens, page_indices, cu_q_lens, num_seqs, T)
     opts = _opts(lib, sm_scale, sliding_window, soft_cap, k_scale, v_scale, debug_validate,
                  split_keys, q_scale)

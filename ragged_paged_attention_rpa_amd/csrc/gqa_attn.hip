@@ -1158,6 +1158,12 @@ template <typename T>
 __device__ __forceinline__ float load_as_f32(const void* base, int64_t idx, int dt) {
   if (dt == DT_F32) return reinterpret_cast<const float*>(base)[idx];
   if (dt == DT_BF16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[idx]);
+  if (dt == DT_INT4) {
+    // Element idx: nibble idx % 2 of byte idx / 2, two's complement.
+    const uint32_t b = reinterpret_cast<const uint8_t*>(base)[idx >> 1];
+    const int v = (int)((idx & 1) ? (b >> 4) : (b & 15u));
+    return (float)(v >= 8 ? v - 16 : v);
+  }
   const uint8_t b = reinterpret_cast<const uint8_t*>(base)[idx];
   float f[4];
   if (dt == DT_INT8)
@@ -1248,11 +1254,13 @@ __global__ void __launch_bounds__(64) gqa_generic_kernel(GqaArgs a) {
     const int lp = pos / a.page_size;
     const int page = lp < a.pages_per_seq ? a.page_indices[(int64_t)seq * a.pages_per_seq + lp] : -1;
     if (page >= 0 && page < a.total_num_pages) {
-      const int eb = a.kv_dtype == DT_F32 ? 4 : a.kv_dtype == DT_BF16 ? 2 : 1;
+      // Bytes of one head's row (INT4: two values per byte, head_dim even).
+      const int64_t hb = a.kv_dtype == DT_INT4 ? D / 2
+                         : (int64_t)D * (a.kv_dtype == DT_F32 ? 4 : a.kv_dtype == DT_BF16 ? 2 : 1);
       const int64_t slot = (int64_t)page * a.page_size + pos % a.page_size;
-      const uint8_t* sp = (const uint8_t*)a.new_kv + ((int64_t)tok * ch + 2 * kvh) * D * eb;
-      uint8_t* dp = (uint8_t*)a.kv_out + (slot * ch + 2 * kvh) * D * eb;
-      for (int i = lane; i < 2 * D * eb; i += 64) dp[i] = sp[i];
+      const uint8_t* sp = (const uint8_t*)a.new_kv + ((int64_t)tok * ch + 2 * kvh) * hb;
+      uint8_t* dp = (uint8_t*)a.kv_out + (slot * ch + 2 * kvh) * hb;
+      for (int64_t i = lane; i < 2 * hb; i += 64) dp[i] = sp[i];
     }
   }
 }

@@ -306,8 +306,10 @@ rpa_status gqa_forward(const void* q, rpa_dtype q_dtype, int32_t num_q_heads, in
                 total_num_pages);
   if (q_dtype != RPA_F32 && q_dtype != RPA_BF16 && q_dtype != RPA_FP8_E4M3)
     return fail(RPA_E_DTYPE, "q dtype must be F32, BF16 or FP8_E4M3");
-  if (dtype_bytes(kv_dtype) == 0)
-    return fail(RPA_E_DTYPE, "kv dtype must be F32, BF16, FP8_E4M3 or INT8");
+  if (dtype_bytes(kv_dtype) == 0 && kv_dtype != RPA_INT4)
+    return fail(RPA_E_DTYPE, "kv dtype must be F32, BF16, FP8_E4M3, INT8 or INT4");
+  if (kv_dtype == RPA_INT4 && (head_dim & 1))
+    return fail(RPA_E_SHAPE, "an INT4 pool needs an even head_dim (got %d)", head_dim);
 
   rpa::GqaArgs a{};
   a.q = q;

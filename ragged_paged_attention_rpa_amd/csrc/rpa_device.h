@@ -16,7 +16,7 @@ typedef float floatx2 __attribute__((__vector_size__(2 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 typedef uint32_t u32x2 __attribute__((__vector_size__(2 * sizeof(uint32_t))));
 
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT8 = 3 };
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_INT8 = 3, DT_INT4 = 4 };
 
 constexpr float kLog2e = 1.4426950408889634f;
 

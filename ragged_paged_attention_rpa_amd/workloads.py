@@ -45,13 +45,25 @@ def _gen(device, seed):
 def randn(shape, dtype, gen, device, scale=1.0):
     """N(0,1)*scale drawn in fp32 and cast to ``dtype`` (bf16/fp8/fp32); for
     int8, the integers round(32 * N(0,1) * scale) clipped to [-128, 127] (a pool
-    quantised at 1/32 per step, dequantised by a scale of 1/32)."""
+    quantised at 1/32 per step, dequantised by a scale of 1/32); for uint8, a
+    packed int4 array: the integers round(2 * N(0,1) * scale) clipped to
+    [-8, 7], two per byte along the last index (element 2i in the low nibble),
+    so the result's last dimension is half of ``shape``'s."""
     x = torch.randn(tuple(shape), generator=gen, device=device, dtype=torch.float32)
     if scale != 1.0:
         x.mul_(scale)
     if dtype == torch.int8:
         return x.mul_(32.0).round_().clamp_(-128, 127).to(torch.int8)
+    if dtype == torch.uint8:
+        return pack_int4(x.mul_(2.0).round_().clamp_(-8, 7).to(torch.int16))
     return x.to(dtype)
+
+
+def pack_int4(v):
+    """Integers in [-8, 7] (last dimension even) as packed int4 bytes: element
+    2i in the low nibble of byte i, each a two's-complement nibble."""
+    n = v.to(torch.int16) & 15
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).to(torch.uint8)
 
 
 def deal_pages(rng, kv_lens, page_size, pages_per_seq, spare_pages=0):

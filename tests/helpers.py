@@ -16,6 +16,8 @@ def storage(t: torch.Tensor):
         return t.view(torch.uint8).numpy(), oracle.FP8_E4M3
     if t.dtype == torch.int8:
         return t.numpy(), oracle.INT8
+    if t.dtype == torch.uint8:  # packed int4 pool
+        return t.numpy(), oracle.INT4
     raise TypeError(t.dtype)
 
 

@@ -109,6 +109,11 @@ def test_rpa_forward_static_rejections(lib):
     assert "MFMA path" in lib.rpa_last_error().decode()
     assert _fwd(lib, qd=2) == RPA_E_WORKSPACE        # fp8 queries accepted there
     assert _fwd(lib, kvd=3) == RPA_E_WORKSPACE       # int8 pools accepted
+    # int4 pools pass the dtype check (an fp8 query is then turned away by the
+    # path rule, which comes later) and need an even head_dim
+    assert _fwd(lib, kvd=4, qd=2) == RPA_E_UNSUPPORTED
+    assert _fwd(lib, kvd=4, D=63) == RPA_E_SHAPE
+    assert "even head_dim" in lib.rpa_last_error().decode()
     assert _fwd(lib, kvd=7) == RPA_E_DTYPE
     assert _fwd(lib, opts=_opts(lib, q_scale=float("inf"))) == RPA_E_INVALID
     assert _fwd(lib, opts=_opts(lib, sliding_window=-1)) == RPA_E_INVALID

@@ -590,6 +590,34 @@ def test_int8_pool(mode):
     _check(c, got, _run_oracle(c), "bf16")
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_int4_pool(fused):
+    """Packed int4 pools (the integers of 2 N(0,1), dequantised by k_scale =
+    v_scale = 1/2) on the generic kernel, with a window and a cap; with
+    ``fused`` the call also scatters the step's new rows (packed bytes), and
+    the pool afterwards is bit-exact against the oracle's scatter."""
+    _say(f"int4 pool (fused={fused})")
+    seqs = [(1, 700), (30, 400), (1, 17), (8, 8), (3, 1200)]
+    c = wl.make_gqa(seqs, num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                    q_dtype=torch.bfloat16, kv_dtype=torch.uint8, seed=520, device="cuda",
+                    sliding_window=300, soft_cap=30.0, k_scale=0.5, v_scale=0.5, spare_pages=2,
+                    name=f"int4-fused{int(fused)}")
+    new_kv = None
+    if fused:
+        T = int(c.cu_q_lens[-1])
+        new_kv = wl.randn((T, 8, 128), torch.uint8, wl._gen("cuda", 521), "cuda")
+        host = storage(c.kv_pages)[0].copy()
+        oracle.kv_update(oracle.LAYOUT_COMBINED_GQA, storage(new_kv[:, 0::2])[0],
+                         storage(new_kv[:, 1::2])[0], host, None, oracle.INT4,
+                         kv_lens=c.kv_lens, page_indices=c.page_indices, cu_q_lens=c.cu_q_lens,
+                         num_seqs=c.num_seqs)
+    got = _run_gpu(c, new_kv=new_kv) if fused else _run_gpu(c)
+    assert rpa.last_path() == "gqa_generic"
+    if fused:
+        assert np.array_equal(storage(c.kv_pages)[0], host)
+    _check(c, got, _run_oracle(c), "bf16")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8", "int8"])
 def test_fp8_queries_with_q_scale(kv):
     """fp8 queries dequantised by q_scale (widened exactly to bf16 on load),

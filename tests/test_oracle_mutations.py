@@ -47,6 +47,9 @@ MUTATIONS = [
     ("gqa_q_scale_dropped", "(load_elem(q, q_dtype, qbase + d) * q_scale)",
      "load_elem(q, q_dtype, qbase + d)", None),
     ("int8_read_unsigned", "(double)((const int8_t*)base)[idx]", "(double)((const uint8_t*)base)[idx]", None),
+    ("int4_nibbles_swapped", "(idx % 2 == 0) ? (b & 0xF) : (b >> 4)", "(idx % 2 == 0) ? (b >> 4) : (b & 0xF)", None),
+    ("int4_unsigned", "return (double)(v < 8 ? v : v - 16);", "return (double)v;", None),
+    ("int4_byte_index", "((const uint8_t*)base)[idx / 2]", "((const uint8_t*)base)[idx]", None),
     ("mla_window_dropped", "if (!key_visible(t, pos, sliding_window)) continue;",
      "if (!key_visible(t, pos, 0)) continue;", 1),
     ("gqa_no_causal_offset", "const int64_t pos = kv_len - q_len + (tok - cu_q_lens[i]);",
@@ -74,8 +77,9 @@ MUTATIONS = [
     ("sparse_row_mod_read_block", "(int64_t)page * page_size + kp % page_size;",
      "(int64_t)page * page_size + kp % read_block;", None),
     ("update_pad_not_zeroed", "memset(db, 0, (size_t)stride_b * eb);", "", None),
-    ("update_k_to_value_head", "((slot * 2 * heads + 2 * h) * dim_a) * eb",
-     "((slot * 2 * heads + 2 * h + 1) * dim_a) * eb", None),
+    ("update_k_to_value_head", "(slot * 2 * heads + 2 * h) * row_a,",
+     "(slot * 2 * heads + 2 * h + 1) * row_a,", None),
+    ("update_int4_row_bytes", "dtype == OR_INT4 ? dim_a / 2 :", "dtype == OR_INT4 ? dim_a :", None),
     ("update_position_off_by_one", "const int64_t pos = kv_lens[i] - q_len + (t - cu_q_lens[i]);",
      "const int64_t pos = kv_lens[i] - q_len + (t - cu_q_lens[i]) - 1;", None),
     ("e4m3_exponent_bias", "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)", None),

@@ -377,6 +377,59 @@ def test_int8_pool_is_its_integers():
     assert np.array_equal(a, b)
 
 
+def _pack_nibbles(ints):
+    """Test-side packing of integers in [-8, 7]: element 2i in the low four bits
+    of byte i (the RPA_INT4 layout)."""
+    n = ints.astype(np.int16) & 15
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+
+def test_int4_pool_is_its_integers():
+    """A packed int4 pool holds two's-complement nibbles (negative values
+    included) in element order: it gives exactly what an fp32 pool of the same
+    integers gives."""
+    c = _gqa_small(seed=93)
+    rng = np.random.default_rng(93)
+    ints = rng.integers(-8, 8, size=tuple(c.kv_pages.shape))
+    q, qd = storage(c.q)
+    meta = (c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs)
+    a = oracle.rpa(q, qd, _pack_nibbles(ints), oracle.INT4, *meta, sm_scale=c.sm_scale,
+                   k_scale=0.25, v_scale=0.5)
+    b = oracle.rpa(q, qd, ints.astype(np.float32), oracle.F32, *meta, sm_scale=c.sm_scale,
+                   k_scale=0.25, v_scale=0.5)
+    assert np.array_equal(a, b)
+
+
+def test_int4_bytes_by_hand():
+    """One key, head_dim 2: the output is the key's V row times v_scale. Byte
+    0x3F holds (-1, 3) (low nibble first), byte 0x78 holds (-8, 7)."""
+    q = np.array([[[1.0, 0.0]]], dtype=np.float32)            # [T=1, Hq=1, D=2]
+    meta = (np.array([1], np.int32), np.array([[0]], np.int32), np.array([0, 1], np.int32), 1)
+    for vbyte, want in ((0x3F, (-1.0, 3.0)), (0x78, (-8.0, 7.0))):
+        kv = np.array([[[[0x21], [vbyte]]]], dtype=np.uint8)   # [P=1, ps=1, 2, D/2=1]
+        out = oracle.rpa(q, oracle.F32, kv, oracle.INT4, *meta, v_scale=0.5)
+        assert np.array_equal(out[0, 0], 0.5 * np.array(want))
+
+
+def test_int4_scatter_is_the_packed_int8_scatter():
+    """Scattering packed int4 rows gives the packing of the same scatter done
+    on int8 rows of the same integers."""
+    rng = np.random.default_rng(94)
+    P, ps, H, D = 6, 4, 2, 8
+    kv_lens = np.array([5, 9], np.int32)
+    cu = np.array([0, 2, 5], np.int32)
+    table = np.array([[3, 1, 0], [5, 2, 4]], np.int32)
+    pool = rng.integers(-8, 8, size=(P, ps, 2 * H, D)).astype(np.int8)
+    nk = rng.integers(-8, 8, size=(5, H, D)).astype(np.int8)
+    nv = rng.integers(-8, 8, size=(5, H, D)).astype(np.int8)
+    meta = dict(kv_lens=kv_lens, page_indices=table, cu_q_lens=cu, num_seqs=2)
+    packed = _pack_nibbles(pool)
+    oracle.kv_update(oracle.LAYOUT_COMBINED_GQA, _pack_nibbles(nk), _pack_nibbles(nv), packed,
+                     None, oracle.INT4, **meta)
+    oracle.kv_update(oracle.LAYOUT_COMBINED_GQA, nk, nv, pool, None, oracle.INT8, **meta)
+    assert np.array_equal(packed, _pack_nibbles(pool))
+
+
 # ------------------------------------------------------------------ sparse --
 
 def _sparse_small(seed=13, K=4, RB=16, ps=32, T=256, S=6, H=4, pad_frac=0.0):
