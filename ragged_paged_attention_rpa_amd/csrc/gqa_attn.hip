@@ -919,13 +919,16 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
     }
     const int key = kb + kWaveKeys8 * wave + (lane & 31);
     const char* row = (const char*)kZeroKV;
+    bool cache_row = false;  // key's row is a valid pool row
     if (key >= t.lo && key < t.hi) {
       if (key >= t.new_start) {
         row = new_head + (int64_t)(t.cu0 + key - t.new_start) * token_bytes;
       } else {
         const int page = sm.pages[(key >> ps_log2) - pwin];
-        if (page >= 0 && page < a.total_num_pages)
+        if (page >= 0 && page < a.total_num_pages) {
           row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+          cache_row = true;
+        }
       }
     }
     const uint32_t rlo = (uint32_t)(uintptr_t)row;
@@ -933,6 +936,23 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
     const uint32_t st = sbase + (uint32_t)(b % kStages8) * kRaw8Stage +
                         (uint32_t)wave * (kWaveKeys8 * kRawKeyBytes);
     const int sub = lane >> 4;
+    // When all 32 keys are pool rows, the four keys of one instruction
+    // (4-aligned, so on one page: pages hold at least 8 keys) are consecutive
+    // rows: one scalar base (the first key's row) plus a per-lane offset.
+    // (This kernel runs only beside the prefill kernel, whose page size is at
+    // least 8.)
+    if (__builtin_amdgcn_ballot_w64(!cache_row) == 0) {
+#pragma unroll
+      for (int ii = 0; ii < kIPW8; ++ii) {
+        const uint32_t l = __builtin_amdgcn_readlane(rlo, 4 * ii);
+        const uint32_t h = __builtin_amdgcn_readlane(rhi, 4 * ii);
+        const char* base = (const char*)(((uint64_t)h << 32) | l);
+        const uint32_t voff = (uint32_t)sub * (uint32_t)token_bytes +
+                              (uint32_t)(((lane & 15) ^ sw8(4 * ii + sub)) << 4);
+        dma_b128_s(base, voff, __builtin_amdgcn_readfirstlane(st + (uint32_t)ii * 1024));
+      }
+      return;
+    }
 #pragma unroll
     for (int ii = 0; ii < kIPW8; ++ii) {
       uint32_t lo = 0, hi = 0;
