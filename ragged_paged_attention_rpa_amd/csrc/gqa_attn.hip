@@ -571,20 +571,42 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     // group); every DMA instruction below takes its keys' rows by readlane.
     const int key = kb + 16 * wave + (lane & 15);
     const char* row = (const char*)kZeroKV;
+    bool cache_row = false;  // key's row is a valid pool row
     if (key >= t.lo && key < t.hi) {
       if (key >= t.new_start) {
         row = new_head + (int64_t)(t.cu0 + key - t.new_start) * token_bytes;
       } else {
         const int page = sm.pages[(key >> ps_log2) - pwin];
-        if (page >= 0 && page < a.total_num_pages)
+        if (page >= 0 && page < a.total_num_pages) {
           row = kv_head + (((int64_t)page << ps_log2) + (key & ps_mask)) * token_bytes;
+          cache_row = true;
+        }
       }
     }
     const uint32_t rlo = (uint32_t)(uintptr_t)row;
     const uint32_t rhi = (uint32_t)((uintptr_t)row >> 32);
     const uint32_t st = sbase + (uint32_t)(b % NST) * dma_stride;
     constexpr int kKeysPerDma = KV_DT == DT_BF16 ? 2 : 4;
+    constexpr int kKeysLog2 = KV_DT == DT_BF16 ? 1 : 2;
     const int sub = KV_DT == DT_BF16 ? lane >> 5 : lane >> 4;  // key of this lane in the DMA
+    // When all 16 keys are pool rows and a page holds a whole instruction's
+    // keys (they are kKeysPerDma-aligned), those keys are consecutive rows:
+    // one scalar base (the first key's row) plus a per-lane offset.
+    if (ps_log2 >= kKeysLog2 && __builtin_amdgcn_ballot_w64(!cache_row) == 0) {
+#pragma unroll
+      for (int ii = 0; ii < kIPW; ++ii) {
+        const uint32_t l = __builtin_amdgcn_readlane(rlo, kKeysPerDma * ii);
+        const uint32_t h = __builtin_amdgcn_readlane(rhi, kKeysPerDma * ii);
+        const char* base = (const char*)(((uint64_t)h << 32) | l);
+        const int kk = kKeysPerDma * ii + sub;  // key within this wave's 16
+        const uint32_t col = KV_DT == DT_BF16 ? (uint32_t)(((lane & 31) ^ swz(kk)) << 4)
+                                              : (uint32_t)(((lane & 15) ^ kk) << 4);
+        const int c = wave * kIPW + ii;  // 1 KB slot of the stage
+        dma_b128_s(base, (uint32_t)sub * (uint32_t)token_bytes + col,
+                   __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024));
+      }
+      return;
+    }
 #pragma unroll
     for (int ii = 0; ii < kIPW; ++ii) {
       uint32_t lo = 0, hi = 0;
