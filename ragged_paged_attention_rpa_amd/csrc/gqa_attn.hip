@@ -876,8 +876,28 @@ static_assert(4 * 16 * (kD + 2) * sizeof(float) <= sizeof(Dec8Smem::stage), "mer
 // bank conflicts.
 __device__ __forceinline__ int sw8(int key) { return (key & 15) ^ (((key >> 4) & 1) << 3); }
 
-template <int KV_DT, bool CAP>
+// S^T(16 keys x 16 rows) += K(16 x 128) Q^T(128 x 16) on one fp8 MFMA
+// (v_mfma_f32_16x16x128_f8f6f4, both operands OCP E4M3, no block scaling).
+// Lane l holds row l%16 of either operand over one 32-byte slice of the
+// contraction; the two operands only have to use the same slice per lane (a
+// dot product does not depend on the order of its terms), and the output
+// layout is that of the 16x16x32 bf16 form.
+__device__ __forceinline__ floatx4 mfma_16x16x128_fp8(const u32x4 (&a)[2], const u32x4 (&b)[2],
+                                                      const floatx4& c) {
+  typedef int intx8 __attribute__((ext_vector_type(8)));
+  const intx8 av = {(int)a[0][0], (int)a[0][1], (int)a[0][2], (int)a[0][3],
+                    (int)a[1][0], (int)a[1][1], (int)a[1][2], (int)a[1][3]};
+  const intx8 bv = {(int)b[0][0], (int)b[0][1], (int)b[0][2], (int)b[0][3],
+                    (int)b[1][0], (int)b[1][1], (int)b[1][2], (int)b[1][3]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
+}
+
+// QF8: fp8 queries over an fp8 pool: the scores run on the fp8 MFMA straight
+// from the raw K rows (a product of two E4M3 values is exact in fp32, as it
+// is after widening both to bf16); otherwise K is widened to bf16.
+template <int KV_DT, bool CAP, bool QF8>
 __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm, int ps_log2) {
+  static_assert(!QF8 || KV_DT == DT_FP8, "fp8 scores need an fp8 pool");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -891,16 +911,24 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
   const bool row_ok = r < t.nrows;
   const int qpos = row_ok ? t.first_pos + r / G : kNegBig;
 
-  u32x4 qv[4];
+  // Q^T: bf16 (widened on load) for four 16x16x32 k-steps, or with QF8 the
+  // raw fp8 bytes of dims 32g .. 32g + 31 for one 16x16x128 step.
+  u32x4 qv[QF8 ? 2 : 4];
   {
     const int tok = s.cu0 + t.qtok0 + (row_ok ? r / G : 0);
     const int head = t.kvh * G + (row_ok ? r % G : 0);
     const int64_t q0 = ((int64_t)tok * a.num_q_heads + head) * kD;
+    if constexpr (QF8) {
+      const u32x4* qp = reinterpret_cast<const u32x4*>((const uint8_t*)a.q + q0 + 32 * g);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = load_q8(a.q, q0 + 32 * j + 8 * g, a.q_dtype);
-      qv[j] = v;
+      for (int j = 0; j < 2; ++j) qv[j] = row_ok ? qp[j] : u32x4{0u, 0u, 0u, 0u};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok) v = load_q8(a.q, q0 + 32 * j + 8 * g, a.q_dtype);
+        qv[j] = v;
+      }
     }
   }
 
@@ -1002,6 +1030,9 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
   // key tt*16 + lane%16, dims 8(g + 4j) .. +7 = half g&1 of raw column 2j + g/2.
   const int km = lane & 15;
   const uint32_t ka = (uint32_t)(km * kRawKeyBytes + (((lane >> 5) ^ km) << 4) + 8 * (g & 1));
+  // QF8 K operand (tile tt, 16-byte half hh) at ka8 ^ (tt << 7 | hh << 4) + tt
+  // * 16 rows: key tt*16 + km, raw column 2g + hh (sw8 of that key is km ^ 8tt).
+  const uint32_t ka8 = (uint32_t)(km * kRawKeyBytes + (((2 * g) ^ km) << 4));
   // V^T operand of dims 16dt.. at va ^ (dt << 4): lanes 2r, 2r+1 of group g
   // name key slot r, i.e. key 4g + r (r < 4) or 16 + 4g + r - 4.
   const int vslot = (lane & 15) >> 1;
@@ -1018,22 +1049,39 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
     const uint32_t cur = sbase + (uint32_t)(b % kStages8) * kRaw8Stage +
                          (uint32_t)wave * (kWaveKeys8 * kRawKeyBytes);
     const int kw = kb0 + b * kBN8 + kWaveKeys8 * wave;  // first key of this wave's share
-    u32x2 kr[2][4], vr[8];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        kr[tt][j] = lds_read_b64(cur + (ka ^ (uint32_t)((j << 5) | (tt << 7))) +
-                                 (uint32_t)(tt * 16 * kRawKeyBytes));
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) vr[dt] = lds_read_tr8(cur + (va ^ (uint32_t)(dt << 4)));
     floatx4 sv[2];
+    u32x2 vr[8];
+    if constexpr (QF8) {
+      u32x4 k8[2][2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sv[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sv[tt] = mfma_16x16x32(as_bf16x8(kv8x8_to_bf16x8<KV_DT>(kr[tt][j])), as_bf16x8(qv[j]), sv[tt]);
+        for (int hh = 0; hh < 2; ++hh)
+          k8[tt][hh] = lds_read_b128(cur + (ka8 ^ (uint32_t)((tt << 7) | (hh << 4))) +
+                                     (uint32_t)(tt * 16 * kRawKeyBytes));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vr[dt] = lds_read_tr8(cur + (va ^ (uint32_t)(dt << 4)));
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+        sv[tt] = mfma_16x16x128_fp8(k8[tt], qv, floatx4{0.f, 0.f, 0.f, 0.f});
+    } else {
+      u32x2 kr[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          kr[tt][j] = lds_read_b64(cur + (ka ^ (uint32_t)((j << 5) | (tt << 7))) +
+                                   (uint32_t)(tt * 16 * kRawKeyBytes));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vr[dt] = lds_read_tr8(cur + (va ^ (uint32_t)(dt << 4)));
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sv[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sv[tt] = mfma_16x16x32(as_bf16x8(kv8x8_to_bf16x8<KV_DT>(kr[tt][j])), as_bf16x8(qv[j]),
+                                 sv[tt]);
+      }
     }
     // sv[tt][i] of lane group g is key kw + 16tt + 4g + i of row lane%16.
     float mblk = -INFINITY;
@@ -1102,7 +1150,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
               reinterpret_cast<float*>(sm.stage));
 }
 
-template <int KV_DT, bool CAP>
+template <int KV_DT, bool CAP, bool QF8>
 __global__ void __launch_bounds__(kThreads) gqa_decode8_kernel(GqaArgs a, int ps_log2) {
   __shared__ __attribute__((aligned(1024))) Dec8Smem sm;
   const int count = a.counters[0];
@@ -1113,7 +1161,7 @@ __global__ void __launch_bounds__(kThreads) gqa_decode8_kernel(GqaArgs a, int ps
     __syncthreads();
     if (ti >= count) break;
     const Tile tile = a.tiles[ti];
-    process_decode8<KV_DT, CAP>(a, tile, sm, ps_log2);
+    process_decode8<KV_DT, CAP, QF8>(a, tile, sm, ps_log2);
     __syncthreads();
   }
 }
@@ -1481,19 +1529,24 @@ hipError_t launch_gqa(const GqaArgs& a, hipStream_t stream) {
   } else if (a.pre_kernel) {
     // Only decode-class tiles are left for this launch: the one-byte decode
     // kernel.
-#define RPA_DEC8_LAUNCH(DT, CAP)                                                               \
-  hipLaunchKernelGGL((gqa_decode8_kernel<DT, CAP>), dim3(grid), dim3(kThreads), 0, dstream, a, \
-                     ps_log2)
+#define RPA_DEC8_LAUNCH(DT, CAP, QF8)                                                      \
+  hipLaunchKernelGGL((gqa_decode8_kernel<DT, CAP, QF8>), dim3(grid), dim3(kThreads), 0, \
+                     dstream, a, ps_log2)
     if (a.kv_dtype == DT_INT8) {
       if (cap)
-        RPA_DEC8_LAUNCH(DT_INT8, true);
+        RPA_DEC8_LAUNCH(DT_INT8, true, false);
       else
-        RPA_DEC8_LAUNCH(DT_INT8, false);
+        RPA_DEC8_LAUNCH(DT_INT8, false, false);
+    } else if (a.q_dtype == DT_FP8) {
+      if (cap)
+        RPA_DEC8_LAUNCH(DT_FP8, true, true);
+      else
+        RPA_DEC8_LAUNCH(DT_FP8, false, true);
     } else {
       if (cap)
-        RPA_DEC8_LAUNCH(DT_FP8, true);
+        RPA_DEC8_LAUNCH(DT_FP8, true, false);
       else
-        RPA_DEC8_LAUNCH(DT_FP8, false);
+        RPA_DEC8_LAUNCH(DT_FP8, false, false);
     }
 #undef RPA_DEC8_LAUNCH
   } else if (a.kv_dtype == DT_INT8) {

@@ -638,6 +638,28 @@ def test_fp8_queries_with_q_scale(kv):
     _check(c, got, want, "fp8" if kv == "fp8" else "bf16")
 
 
+@pytest.mark.parametrize("variant", ["plain", "window-cap"])
+def test_fp8_scores_over_fp8_pool(variant):
+    """fp8 queries over an fp8 pool: the decode tiles take their scores from
+    the fp8 MFMA on the raw bytes; split keys, ragged tails, a window and a
+    soft cap, against the oracle's exact fp8 decode."""
+    win, cap = (None, None) if variant == "plain" else (1500, 30.0)
+    _say(f"fp8 scores over an fp8 pool ({variant})")
+    c = wl.make_gqa([(1, 9000), (1, 1), (1, 47), (200, 900), (1, 4100), (3, 3000), (1, 16)],
+                    num_q_heads=32, num_kv_heads=4, head_dim=128, page_size=16,
+                    q_dtype=torch.float8_e4m3fn, kv_dtype=torch.float8_e4m3fn, seed=610,
+                    device="cuda", q_value_scale=4.0, k_scale=0.5, v_scale=0.5,
+                    sliding_window=win, soft_cap=cap, name=f"fp8q-fp8kv-{variant}")
+    got = _run_gpu(c, q_scale=0.25)
+    assert rpa.last_path() == "gqa_mfma_prefill"
+    q, qd = storage(c.q)
+    kvs, kd = storage(c.kv_pages)
+    want = oracle.rpa(q, qd, kvs, kd, c.kv_lens, c.page_indices, c.cu_q_lens, c.num_seqs,
+                      sm_scale=c.sm_scale, sliding_window=win, soft_cap=cap,
+                      k_scale=c.k_scale, v_scale=c.v_scale, q_scale=0.25)
+    _check(c, got, want, "fp8")
+
+
 FUSED_CASES = {
     # (seqs, Hq, Hkv, D, page size, pool dtype, window, cap, kernel path)
     "bf16-prefill-kernel": ([(1, 3000), (300, 1200), (1, 17), (64, 64), (1, 9000), (700, 2100)],
