@@ -498,6 +498,58 @@ __device__ __forceinline__ void finish_tile(const GqaArgs& a, const Tile& tile, 
   }
 }
 
+// Log2-domain logits of a raw score s = q.k: s * scale * log2(e), or with
+// the soft cap c, c * tanh(s * scale / c) * log2(e). The exact capped form
+// takes tanh(z) as 1 - 2 / (e^{2z} + 1) with the hardware exp2 and
+// reciprocal, i.e. c2 - c3 / (2^{s * c1} + 1); the series form (CapSeries)
+// serves a wave whose scores all lie within its range.
+struct LogitConsts {
+  float c1, c2, c3;
+  CapSeries cs;
+};
+
+template <bool CAP>
+__device__ __forceinline__ LogitConsts logit_consts(const GqaArgs& a) {
+  LogitConsts k;
+  k.c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
+  k.c2 = a.soft_cap * kLog2e;
+  k.c3 = 2.f * a.soft_cap * kLog2e;
+  k.cs = CAP ? cap_series(a.soft_cap, a.score_scale) : CapSeries{0.f, 0.f, 0.f, 0.f};
+  return k;
+}
+
+// The logits of the NT groups of four raw scores a wave holds, in place.
+// With the cap, one branch for the whole wave: the series when no score
+// exceeds its range (lanes masked afterwards count too, except NaN, which
+// the maximum ignores), else the exact form.
+template <bool CAP, int NT>
+__device__ __forceinline__ void to_logits(floatx4* sv, const LogitConsts& k) {
+  if constexpr (!CAP) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[t][i] *= k.c1;
+  } else {
+    float am = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(sv[t][i]));
+    if (!wave_any(am > k.cs.smax)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[t][i] = cap_series_eval(k.cs, sv[t][i], 0.f);
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sv[t][i] = k.c2 - k.c3 * __builtin_amdgcn_rcpf(fast_exp2(sv[t][i] * k.c1) + 1.f);
+    }
+  }
+}
+
 template <int KV_DT, int NST, bool CAP>
 __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT, NST>& sm,
                              int ps_log2) {
@@ -626,16 +678,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     }
   };
 
-  // Log2-domain logit of a raw score s = q.k: s * scale * log2(e), or with
-  // the soft cap c, c * tanh(s * scale / c) * log2(e). tanh(z) is taken as
-  // 1 - 2 / (e^{2z} + 1) with the hardware exp2 and reciprocal, so the capped
-  // logit is c2 - c3 / (2^{s * c1} + 1).
-  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
-  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
-  auto logit = [&](float sraw) -> float {
-    if (!CAP) return sraw * c1;
-    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
-  };
+  const LogitConsts lk = logit_consts<CAP>(a);
   // Keys [klo, khi) of this wave's share of a block are visible to every row
   // of the wave (rows past the tile's end do not count): the mask can be skipped.
   auto all_visible = [&](int klo, int khi) -> bool {
@@ -693,20 +736,18 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
     if (keysplit) {
       // One 16-key tile per wave; PV on v_mfma_f32_16x16x16_bf16.
       floatx4 sv = score16(cur + kTileBytes * wave, kx, qv);
+      to_logits<CAP, 1>(&sv, lk);
       float mblk = -INFINITY;
       if (all_visible(kb + 16 * wave, kb + 16 * wave + 16)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[i] = logit(sv[i]);
-          mblk = fmaxf(mblk, sv[i]);
-        }
+        for (int i = 0; i < 4; ++i) mblk = fmaxf(mblk, sv[i]);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = kb + 16 * wave + 4 * g + i;
           const bool vis =
               key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
-          sv[i] = vis ? logit(sv[i]) : -INFINITY;
+          sv[i] = vis ? sv[i] : -INFINITY;
           mblk = fmaxf(mblk, sv[i]);
         }
       }
@@ -744,15 +785,13 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
       floatx4 sv[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) sv[kt] = score16(cur + kTileBytes * kt, kx, qv);
+      to_logits<CAP, 4>(sv, lk);
       float mblk = -INFINITY;
       if (all_visible(kb, kb + kBN)) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sv[kt][i] = logit(sv[kt][i]);
-            mblk = fmaxf(mblk, sv[kt][i]);
-          }
+          for (int i = 0; i < 4; ++i) mblk = fmaxf(mblk, sv[kt][i]);
       } else {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -761,7 +800,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
             const int key = kb + 16 * kt + 4 * g + i;
             const bool vis =
                 key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
-            sv[kt][i] = vis ? logit(sv[kt][i]) : -INFINITY;
+            sv[kt][i] = vis ? sv[kt][i] : -INFINITY;
             mblk = fmaxf(mblk, sv[kt][i]);
           }
       }
@@ -1019,12 +1058,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
     }
   };
 
-  const float c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
-  const float c2 = a.soft_cap * kLog2e, c3 = 2.f * a.soft_cap * kLog2e;
-  auto logit = [&](float sraw) -> float {
-    if (!CAP) return sraw * c1;
-    return c2 - c3 * __builtin_amdgcn_rcpf(fast_exp2(sraw * c1) + 1.f);
-  };
+  const LogitConsts lk = logit_consts<CAP>(a);
 
   // K operand (tile tt, k-step j) at ka ^ (j << 5 | tt << 7) + tt * 16 rows:
   // key tt*16 + lane%16, dims 8(g + 4j) .. +7 = half g&1 of raw column 2j + g/2.
@@ -1084,6 +1118,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
       }
     }
     // sv[tt][i] of lane group g is key kw + 16tt + 4g + i of row lane%16.
+    to_logits<CAP, 2>(sv, lk);
     float mblk = -INFINITY;
     const bool all_vis =
         __builtin_amdgcn_ballot_w64(row_ok && !(kw >= t.lo && kw + kWaveKeys8 <= t.hi &&
@@ -1093,10 +1128,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sv[tt][i] = logit(sv[tt][i]);
-          mblk = fmaxf(mblk, sv[tt][i]);
-        }
+        for (int i = 0; i < 4; ++i) mblk = fmaxf(mblk, sv[tt][i]);
     } else {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
@@ -1105,7 +1137,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
           const int key = kw + 16 * tt + 4 * g + i;
           const bool vis =
               key >= t.lo && key < t.hi && key <= qpos && (W <= 0 || key > qpos - W);
-          sv[tt][i] = vis ? logit(sv[tt][i]) : -INFINITY;
+          sv[tt][i] = vis ? sv[tt][i] : -INFINITY;
           mblk = fmaxf(mblk, sv[tt][i]);
         }
     }

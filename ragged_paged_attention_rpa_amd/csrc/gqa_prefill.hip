@@ -280,6 +280,7 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
   const float cap = fabsf(a.soft_cap);
   const float c1 = CAP ? 2.f * kLog2e * a.score_scale / cap : a.score_scale * kLog2e;
   const float c2 = cap * kLog2e, c3 = 2.f * cap * kLog2e;
+  const CapSeries cs = cap_series(cap, a.score_scale);
 
   // MFMA phase j: O^T += V_{j-1}^T P_{j-1}^T (16 MFMAs), then S^T_j = K_j Q^T
   // (16 MFMAs). The 32 A operands (V^T from block j - 1, then K from block j)
@@ -370,17 +371,32 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
     // Logits are taken relative to mref (the reference, 0 for a fresh row).
     const float mref = m_run == -INFINITY ? 0.f : m_run;
     if (CAP) {
-      // Capped logits minus mref, one pass per step over the 32 scores in
-      // place (independent neighbours hide each step's latency).
+      // Capped logits minus mref, in place. A block whose raw scores all lie
+      // within the series' range (NaN garbage in masked lanes is ignored by
+      // the maximum, and masked afterwards) takes the series; any other the
+      // exact form, one pass per step over the 32 scores (independent
+      // neighbours hide each step's latency).
+      float am = 0.f;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[tt][i] = fast_exp2(sv[tt][i] * c1) + 1.f;
-      const float c2r = c2 - mref;
+        for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(sv[tt][i]));
+      if (!wave_any(am > cs.smax)) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sv[tt][i] = fmaf(__builtin_amdgcn_rcpf(sv[tt][i]), -c3, c2r);
+          for (int i = 0; i < 16; ++i) sv[tt][i] = cap_series_eval(cs, sv[tt][i], -mref);
+      } else {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[tt][i] = fast_exp2(sv[tt][i] * c1) + 1.f;
+        const float c2r = c2 - mref;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[tt][i] = fmaf(__builtin_amdgcn_rcpf(sv[tt][i]), -c3, c2r);
+      }
       if (!full) mask();
     }
     // Weights p = 2^{logit - mref - shift} into pb (bf16); returns this

@@ -102,6 +102,41 @@ __device__ __forceinline__ float tanh_def(float x) {
   return 1.0f - 2.0f / (e + 1.0f);
 }
 
+// The capped logit in the log2 domain, cap * tanh(s * scale / cap) * log2(e),
+// by its odd Taylor series in y = s * scale / cap up to y^5 (four VALU
+// instructions against two transcendentals and a reciprocal for the exact
+// form). For |y| <= ymax the series alternates with falling terms, so the
+// first omitted one, 17/315 y^7, bounds the error: ymax is the largest |y|
+// (at most 1/2) at which that term times cap * log2(e) stays within 1e-4,
+// i.e. a relative error of the weight 2^logit below 1e-4, a twentieth of its
+// rounding to bf16. smax is the matching bound on the raw score |s|.
+struct CapSeries {
+  float a0, a1, a2, smax;
+};
+
+// (cap * tanh(x / cap) is even in cap: |cap| is used; the scale keeps its sign.)
+__device__ __forceinline__ CapSeries cap_series(float cap, float scale) {
+  constexpr float kTol = 1e-4f;
+  const float c = scale / fabsf(cap);
+  const float k = fabsf(cap) * kLog2e;
+  // ymax = (kTol / (k * 17 / 315))^(1/7), by the hardware log2 and exp2.
+  const float ymax =
+      fminf(0.5f, fast_exp2(__builtin_amdgcn_logf(kTol / (k * (17.f / 315.f))) * (1.f / 7.f)));
+  const float c2 = c * c;
+  CapSeries r;
+  r.a0 = k * c;
+  r.a1 = -r.a0 * c2 * (1.f / 3.f);
+  r.a2 = r.a0 * c2 * c2 * (2.f / 15.f);
+  r.smax = ymax / fabsf(c);
+  return r;
+}
+
+// The series' capped logit of a raw score s plus `shift` (|s| <= smax).
+__device__ __forceinline__ float cap_series_eval(const CapSeries& cs, float s, float shift) {
+  const float s2 = s * s;
+  return fmaf(s, fmaf(s2, fmaf(s2, cs.a2, cs.a1), cs.a0), shift);
+}
+
 // D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16) on one wave.
 // Lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16], and
 // D[4*(l/16) + i][l%16] for i = 0..3.

@@ -213,8 +213,11 @@ def test_graph_capture_with_side_stream():
 
 
 @pytest.mark.parametrize("cap,qscale,ps", [(None, 1.0, 16), (50.0, 1.0, 16), (50.0, 16.0, 16),
-                                            (None, 1.0, 8)])
+                                            (50.0, 3.0, 16), (50.0, 6.0, 16), (None, 1.0, 8)])
 def test_ragged_fp8_scales(cap, qscale, ps):
+    """fp8 pool with scales; with the cap, queries x1 keep the scores within
+    the range of the capped logit's series form, x16 put nearly every wave on
+    the exact form, and x3 / x6 straddle the bound within one launch."""
     _say(f"ragged fp8 cap={cap} qscale={qscale} page={ps}")
     seqs = [(1, 700), (1, 33), (150, 900), (2, 2), (64, 64)]
     c = wl.make_gqa(seqs, num_q_heads=32, num_kv_heads=8, head_dim=128, page_size=ps,
