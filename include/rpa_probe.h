@@ -11,11 +11,13 @@
  *                     32x32x16 bf16 MFMA, ds_read_b128, v_exp_f32, v_fma_f32;
  *   rpa_probe_chain   shader clocks (s_memtime) per step of a dependent chain
  *                     of 36 32x32x16 bf16 MFMAs per loop trip, alone or next
- *                     to the VALU and LDS work a softmax step adds.
+ *                     to the VALU and LDS work a softmax step adds;
+ *   rpa_probe_issue   shader clocks a wave spends issuing 1 KB reads (LDS-DMA
+ *                     or into registers) back to back, and until they land.
  *
  * Buffers are DEVICE memory owned by the caller; calls are asynchronous on
- * `stream` (NULL = the default stream); every launch uses 256-thread
- * workgroups. Return values are rpa_status codes (rpa.h): RPA_E_INVALID for a
+ * `stream` (NULL = the default stream); launches use 256-thread workgroups
+ * (rpa_probe_issue: 64 * waves). Return values are rpa_status codes (rpa.h): RPA_E_INVALID for a
  * value out of range, RPA_E_HIP when the launch fails; nothing is launched
  * on an invalid argument.
  */
@@ -66,6 +68,22 @@ int rpa_probe_rate(int kind, int workgroups, float* sink, rpa_stream_t stream);
  * wave per SIMD).
  */
 int rpa_probe_chain(int mode, int workgroups, unsigned long long* cycles, float* sink,
+                    rpa_stream_t stream);
+
+/*
+ * Each of `waves` waves per workgroup (1..8) issues `count` (4 or 16) reads of
+ * 1 KiB (64 lanes x 16 bytes) back to back: kind 0 global_load_lds_dwordx4
+ * into LDS (the attention kernels' staging), kind 1 global_load_dwordx4 into
+ * registers. Wave g = workgroup * waves + w reads the count KiB at
+ * (g * count KiB) mod span of `src`, span = src_bytes rounded down to a
+ * multiple of count KiB (src_bytes >= count KiB). ticks[2g] receives the
+ * s_memtime clocks spent issuing the reads, ticks[2g + 1] the clocks until
+ * they have landed; ticks holds 2 * workgroups * waves entries, `sink`
+ * workgroups * waves * 64 floats (values meaningless). workgroups in
+ * [1, 65536].
+ */
+int rpa_probe_issue(int kind, int waves, int count, int workgroups, const void* src,
+                    size_t src_bytes, unsigned long long* ticks, float* sink,
                     rpa_stream_t stream);
 
 #ifdef __cplusplus

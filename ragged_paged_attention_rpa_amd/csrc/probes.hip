@@ -1,7 +1,8 @@
 // Measurement probes behind the practical ceilings the kernels are compared
 // with (bench.py --probe): a streaming read with the attention kernels' own
 // LDS-DMA scheme, MFMA chains next to VALU and LDS work (cycles per step),
-// and raw MFMA / LDS / transcendental throughput. Not part of the attention
+// raw MFMA / LDS / transcendental throughput, and the clocks a wave spends
+// issuing 1 KB reads. Not part of the attention
 // path; every access stays inside the buffers and LDS arrays below.
 #include "rpa_probe.h"
 
@@ -168,7 +169,75 @@ __global__ void __launch_bounds__(kProbeThreads) probe_rate_kernel(float* sink) 
   sink[blockIdx.x * kProbeThreads + threadIdx.x] = out;
 }
 
+// Issue cost of 1 KB vector-memory reads: each wave issues COUNT of them
+// back to back (KIND 0: global_load_lds_dwordx4 into its own 8 KB of LDS;
+// KIND 1: global_load_dwordx4 into registers) from its own COUNT KB of `src`
+// (wave g of the grid reads at (g * COUNT KB) mod span, span a multiple of
+// COUNT KB no larger than the buffer). ticks[2g] = s_memtime clocks spent
+// issuing them, ticks[2g + 1] = until the data has landed.
+constexpr int kIssueMaxWaves = 8;
+template <int KIND, int COUNT>
+__global__ void __launch_bounds__(64 * kIssueMaxWaves) probe_issue_kernel(
+    const char* src, size_t span, unsigned long long* ticks, float* sink) {
+  __shared__ __attribute__((aligned(1024))) char stage[kIssueMaxWaves][8192];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t g = (size_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  const char* base = src + (g * (size_t)COUNT * 1024) % span + lane * 16;
+  const uint32_t dst = lds_addr(stage[wave]);
+  u32x4 r[KIND == 1 ? COUNT : 1];
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int k = 0; k < COUNT; ++k) {
+    if constexpr (KIND == 0) {
+      dma_b128(base + k * 1024, dst + (uint32_t)(k & 7) * 1024);
+    } else {
+      u32x4 v;
+      asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(base + k * 1024) : "memory");
+      r[k] = v;
+    }
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  const unsigned long long t2 = __builtin_amdgcn_s_memtime();
+  uint32_t x = 0;
+  if constexpr (KIND == 1) {
+#pragma unroll
+    for (int k = 0; k < COUNT; ++k) x ^= r[k][0] ^ r[k][3];
+  } else {
+    x = *reinterpret_cast<const uint32_t*>(stage[wave] + lane * 16);
+  }
+  sink[g * 64 + lane] = (float)x;
+  if (lane == 0) {
+    ticks[2 * g] = t1 - t0;
+    ticks[2 * g + 1] = t2 - t0;
+  }
+}
+
 }  // namespace
+
+hipError_t probe_issue(int kind, int waves, int count, int grid, const void* src, size_t bytes,
+                       unsigned long long* ticks, float* sink, hipStream_t stream) {
+  // Every wave reads count KB at a multiple of count KB below span <= bytes.
+  const size_t chunk = (size_t)count * 1024;
+  const size_t span = bytes / chunk * chunk;
+  if (span == 0) return hipErrorInvalidValue;
+  const char* s = (const char*)src;
+#define RPA_PROBE_ISSUE(K, C)                                                                     \
+  if (kind == K && count == C) {                                                                  \
+    hipLaunchKernelGGL((probe_issue_kernel<K, C>), dim3(grid), dim3(64 * waves), 0, stream, s, \
+                       span, ticks, sink);                                                        \
+    return hipGetLastError();                                                                     \
+  }
+  RPA_PROBE_ISSUE(0, 4)
+  RPA_PROBE_ISSUE(0, 16)
+  RPA_PROBE_ISSUE(1, 4)
+  RPA_PROBE_ISSUE(1, 16)
+#undef RPA_PROBE_ISSUE
+  return hipErrorInvalidValue;
+}
 
 hipError_t probe_stream(const void* buf, size_t bytes, int grid, int interleave,
                         hipStream_t stream) {
@@ -241,6 +310,17 @@ extern "C" int rpa_probe_rate(int kind, int workgroups, float* sink, rpa_stream_
   if (!sink || kind < 0 || kind > 3 || workgroups < 1 || workgroups > kMaxProbeGrid)
     return RPA_E_INVALID;
   return launched(rpa::probe_rate(kind, workgroups, sink, stream));
+}
+
+extern "C" int rpa_probe_issue(int kind, int waves, int count, int workgroups, const void* src,
+                               size_t src_bytes, unsigned long long* ticks, float* sink,
+                               rpa_stream_t stream) {
+  if (!src || !ticks || !sink || kind < 0 || kind > 1 || waves < 1 || waves > 8 ||
+      (count != 4 && count != 16) || workgroups < 1 || workgroups > kMaxProbeGrid ||
+      src_bytes < (size_t)count * 1024)
+    return RPA_E_INVALID;
+  return launched(
+      rpa::probe_issue(kind, waves, count, workgroups, src, src_bytes, ticks, sink, stream));
 }
 
 extern "C" int rpa_probe_chain(int mode, int workgroups, unsigned long long* cycles, float* sink,

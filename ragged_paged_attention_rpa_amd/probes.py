@@ -1,7 +1,8 @@
 """Practical ceilings of one MI355X, measured with the probes of librpa.so
 (include/rpa_probe.h): HBM read bandwidth through the attention kernels' own
-LDS-DMA scheme, MFMA / LDS / exp issue rates per CU, and clocks per step of a
-dependent MFMA chain next to softmax-like VALU and LDS work.
+LDS-DMA scheme, MFMA / LDS / exp issue rates per CU, clocks per step of a
+dependent MFMA chain next to softmax-like VALU and LDS work, and the clocks a
+wave spends issuing 1 KB reads.
 
 Each function returns a dict ready for JSON; `python bench.py --probe` prints
 them. Rates per CU per clock are given at the nominal 2.4 GHz (wall-clock
@@ -34,6 +35,8 @@ def _lib():
         lib.rpa_probe_rate.restype = I32
         lib.rpa_probe_chain.argtypes = [I32, I32, P, P, P]
         lib.rpa_probe_chain.restype = I32
+        lib.rpa_probe_issue.argtypes = [I32, I32, I32, I32, P, SZ, P, P, P]
+        lib.rpa_probe_issue.restype = I32
         lib._probe_sigs = True
     return lib
 
@@ -113,6 +116,30 @@ def chain(torch, mode):
             "clocks_per_step": round(per_step, 1)}
 
 
+ISSUE_NAMES = {0: "global_load_lds_dwordx4", 1: "global_load_dwordx4"}
+
+
+def issue(torch, kind, waves, count=16, src_bytes=64 << 20):
+    """Shader clocks a wave spends issuing `count` 1 KB reads back to back
+    (median over one workgroup per CU of `waves` waves), and until they land."""
+    lib = _lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = cus * waves
+    src = torch.ones(src_bytes // 4, dtype=torch.float32, device="cuda")
+    ticks = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    sink = torch.empty(n * 64, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        _check(lib.rpa_probe_issue(kind, waves, count, cus, src.data_ptr(), src_bytes,
+                                   ticks.data_ptr(), sink.data_ptr(), st), "rpa_probe_issue")
+    torch.cuda.synchronize()
+    t = ticks.view(n, 2).double()
+    iss, tot = t[:, 0].median().item(), t[:, 1].median().item()
+    return {"probe": "issue_" + ISSUE_NAMES[kind], "waves_per_cu": waves, "reads_per_wave": count,
+            "clocks_to_issue": round(iss), "clocks_per_read": round(iss / count, 1),
+            "clocks_to_land": round(tot)}
+
+
 def run_all(torch):
     rows = [stream(torch, wg_per_cu=w, interleave=il) for il in (True, False) for w in (2, 1)]
     for kind in (0, 1, 2, 3):
@@ -120,4 +147,7 @@ def run_all(torch):
             rows.append(rate(torch, kind, w))
     for mode in sorted(CHAIN_NAMES):
         rows.append(chain(torch, mode))
+    for kind in (0, 1):
+        for w in (1, 4, 8):
+            rows.append(issue(torch, kind, w))
     return rows

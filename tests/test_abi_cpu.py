@@ -44,9 +44,9 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), f"{name} not exported by librpa.so"
 
 
-def test_probe_header_declares_the_three_probes():
-    assert _declared_functions(PROBE_HEADER) == ["rpa_probe_chain", "rpa_probe_rate",
-                                                 "rpa_probe_stream"]
+def test_probe_header_declares_the_four_probes():
+    assert _declared_functions(PROBE_HEADER) == ["rpa_probe_chain", "rpa_probe_issue",
+                                                 "rpa_probe_rate", "rpa_probe_stream"]
 
 
 def test_probes_reject_invalid_arguments(lib):
@@ -64,6 +64,15 @@ def test_probes_reject_invalid_arguments(lib):
         assert lib.rpa_probe_chain(mode, 256, fake, fake, st) == RPA_E_INVALID
     assert lib.rpa_probe_chain(0, 0, fake, fake, st) == RPA_E_INVALID
     assert lib.rpa_probe_chain(0, 256, None, fake, st) == RPA_E_INVALID
+    for kind, waves, count, wg, nbytes in [(2, 4, 16, 256, 1 << 20), (-1, 4, 16, 256, 1 << 20),
+                                           (0, 0, 16, 256, 1 << 20), (0, 9, 16, 256, 1 << 20),
+                                           (1, 4, 8, 256, 1 << 20), (1, 4, 16, 0, 1 << 20),
+                                           (0, 4, 16, 65537, 1 << 20), (0, 4, 16, 256, 16383)]:
+        assert lib.rpa_probe_issue(kind, waves, count, wg, fake, nbytes, fake, fake, st) == \
+            RPA_E_INVALID, (kind, waves, count, wg, nbytes)
+    assert lib.rpa_probe_issue(0, 4, 4, 256, None, 1 << 20, fake, fake, st) == RPA_E_INVALID
+    assert lib.rpa_probe_issue(0, 4, 4, 256, fake, 1 << 20, None, fake, st) == RPA_E_INVALID
+    assert lib.rpa_probe_issue(0, 4, 4, 256, fake, 1 << 20, fake, None, st) == RPA_E_INVALID
 
 
 def _meta(S=4, pps=8, T=16):
