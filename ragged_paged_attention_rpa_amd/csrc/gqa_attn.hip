@@ -514,7 +514,7 @@ __device__ __forceinline__ LogitConsts logit_consts(const GqaArgs& a) {
   k.c1 = CAP ? 2.f * kLog2e * a.score_scale / a.soft_cap : a.score_scale * kLog2e;
   k.c2 = a.soft_cap * kLog2e;
   k.c3 = 2.f * a.soft_cap * kLog2e;
-  k.cs = CAP ? cap_series(a.soft_cap, a.score_scale) : CapSeries{0.f, 0.f, 0.f, 0.f};
+  k.cs = CAP ? cap_series(a.soft_cap, a.score_scale) : CapSeries{0.f, 0.f, 0.f, 0.f, 0.f};
   return k;
 }
 
@@ -535,7 +535,12 @@ __device__ __forceinline__ void to_logits(floatx4* sv, const LogitConsts& k) {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) am = fmaxf(am, fabsf(sv[t][i]));
-    if (!wave_any(am > k.cs.smax)) {
+    if (!wave_any(am > k.cs.smax3)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[t][i] = cap_series3_eval(k.cs, sv[t][i], 0.f);
+    } else if (!wave_any(am > k.cs.smax)) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll

@@ -381,7 +381,12 @@ __device__ void prefill_tile(const GqaArgs& a, const Tile tile, PreSmem<KV_DT>& 
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(sv[tt][i]));
-      if (!wave_any(am > cs.smax)) {
+      if (!wave_any(am > cs.smax3)) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[tt][i] = cap_series3_eval(cs, sv[tt][i], -mref);
+      } else if (!wave_any(am > cs.smax)) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll

@@ -109,9 +109,11 @@ __device__ __forceinline__ float tanh_def(float x) {
 // first omitted one, 17/315 y^7, bounds the error: ymax is the largest |y|
 // (at most 1/2) at which that term times cap * log2(e) stays within 1e-4,
 // i.e. a relative error of the weight 2^logit below 1e-4, a twentieth of its
-// rounding to bf16. smax is the matching bound on the raw score |s|.
+// rounding to bf16. smax is the matching bound on the raw score |s|; smax3
+// the (smaller) one up to which the series may stop at y^3 (first omitted
+// term 2/15 y^5, same tolerance).
 struct CapSeries {
-  float a0, a1, a2, smax;
+  float a0, a1, a2, smax, smax3;
 };
 
 // (cap * tanh(x / cap) is even in cap: |cap| is used; the scale keeps its sign.)
@@ -122,12 +124,16 @@ __device__ __forceinline__ CapSeries cap_series(float cap, float scale) {
   // ymax = (kTol / (k * 17 / 315))^(1/7), by the hardware log2 and exp2.
   const float ymax =
       fminf(0.5f, fast_exp2(__builtin_amdgcn_logf(kTol / (k * (17.f / 315.f))) * (1.f / 7.f)));
+  // ymax3 = (kTol / (k * 2 / 15))^(1/5).
+  const float ymax3 =
+      fminf(0.5f, fast_exp2(__builtin_amdgcn_logf(kTol / (k * (2.f / 15.f))) * (1.f / 5.f)));
   const float c2 = c * c;
   CapSeries r;
   r.a0 = k * c;
   r.a1 = -r.a0 * c2 * (1.f / 3.f);
   r.a2 = r.a0 * c2 * c2 * (2.f / 15.f);
   r.smax = ymax / fabsf(c);
+  r.smax3 = ymax3 / fabsf(c);
   return r;
 }
 
@@ -135,6 +141,11 @@ __device__ __forceinline__ CapSeries cap_series(float cap, float scale) {
 __device__ __forceinline__ float cap_series_eval(const CapSeries& cs, float s, float shift) {
   const float s2 = s * s;
   return fmaf(s, fmaf(s2, fmaf(s2, cs.a2, cs.a1), cs.a0), shift);
+}
+
+// The same series stopped at y^3 (|s| <= smax3): one FMA less.
+__device__ __forceinline__ float cap_series3_eval(const CapSeries& cs, float s, float shift) {
+  return fmaf(s, fmaf(s * s, cs.a1, cs.a0), shift);
 }
 
 // D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16) on one wave.
