@@ -660,7 +660,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
                                               : (uint32_t)(((lane & 15) ^ kk) << 4);
         const int c = wave * kIPW + ii;  // 1 KB slot of the stage
         dma_b128_s(base, (uint32_t)sub * (uint32_t)token_bytes + col,
-                   __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024));
+                   __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024), keysplit);
       }
       return;
     }
@@ -679,7 +679,7 @@ __device__ void process_tile(const GqaArgs& a, const Tile& tile, TileSmem<KV_DT,
       const char* src = KV_DT == DT_BF16 ? base + (((lane & 31) ^ swz(kk)) << 4)
                                          : base + (((lane & 15) ^ kk) << 4);
       const int c = wave * kIPW + ii;  // 1 KB slot of the stage
-      dma_b128(src, __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024));
+      dma_b128(src, __builtin_amdgcn_readfirstlane(st + (uint32_t)c * 1024), keysplit);
     }
   };
 
@@ -1043,7 +1043,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
         const char* base = (const char*)(((uint64_t)h << 32) | l);
         const uint32_t voff = (uint32_t)sub * (uint32_t)token_bytes +
                               (uint32_t)(((lane & 15) ^ sw8(4 * ii + sub)) << 4);
-        dma_b128_s(base, voff, __builtin_amdgcn_readfirstlane(st + (uint32_t)ii * 1024));
+        dma_b128_s(base, voff, __builtin_amdgcn_readfirstlane(st + (uint32_t)ii * 1024), true);
       }
       return;
     }
@@ -1059,7 +1059,7 @@ __device__ void process_decode8(const GqaArgs& a, const Tile& tile, Dec8Smem& sm
       }
       const char* base = (const char*)(((uint64_t)hi << 32) | lo);
       dma_b128(base + (((lane & 15) ^ sw8(4 * ii + sub)) << 4),
-               __builtin_amdgcn_readfirstlane(st + (uint32_t)ii * 1024));
+               __builtin_amdgcn_readfirstlane(st + (uint32_t)ii * 1024), true);
     }
   };
 

@@ -21,10 +21,11 @@ constexpr int kStreamStage = 32 * 1024;  // bytes per stage: 8 DMA instructions 
 // stages per workgroup with global_load_lds_dwordx4 (1 KB per instruction),
 // keeping two stages in flight per wave, and computes nothing. Workgroup b
 // takes chunks b, b + grid, b + 2 grid, ... (INTERLEAVE) or its own
-// contiguous run of nchunks / grid chunks.
+// contiguous run of nchunks / grid chunks. nt: loads with the non-temporal
+// cache policy.
 template <bool INTERLEAVE>
 __global__ void __launch_bounds__(kProbeThreads) probe_stream_kernel(const char* buf,
-                                                                     int64_t nchunks) {
+                                                                     int64_t nchunks, int nt) {
   __shared__ __attribute__((aligned(1024))) char stage[2][kStreamStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -35,7 +36,7 @@ __global__ void __launch_bounds__(kProbeThreads) probe_stream_kernel(const char*
     const uint32_t dst = lds_addr(stage[i & 1]) + (uint32_t)wave * 8192;
     const char* src = buf + (first + i * step) * kStreamStage + wave * 8192 + lane * 16;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dma_b128(src + k * 1024, dst + (uint32_t)k * 1024);
+    for (int k = 0; k < 8; ++k) dma_b128(src + k * 1024, dst + (uint32_t)k * 1024, nt != 0);
     wait_vmcnt<8>();
   }
   wait_vmcnt<0>();
@@ -239,18 +240,20 @@ hipError_t probe_issue(int kind, int waves, int count, int grid, const void* src
   return hipErrorInvalidValue;
 }
 
-hipError_t probe_stream(const void* buf, size_t bytes, int grid, int interleave,
+hipError_t probe_stream(const void* buf, size_t bytes, int grid, int flags,
                         hipStream_t stream) {
+  const bool interleave = flags & 1;
+  const int nt = (flags >> 1) & 1;
   // Chunks read: per_wg = floor(bytes / 32 KB / grid) per workgroup, so every
   // chunk index, interleaved or contiguous, is below per_wg * grid.
   const int64_t nchunks = (int64_t)(bytes / kStreamStage) / grid * grid;
   if (nchunks <= 0) return hipErrorInvalidValue;
   if (interleave)
     hipLaunchKernelGGL(probe_stream_kernel<true>, dim3(grid), dim3(kProbeThreads), 0, stream,
-                       (const char*)buf, nchunks);
+                       (const char*)buf, nchunks, nt);
   else
     hipLaunchKernelGGL(probe_stream_kernel<false>, dim3(grid), dim3(kProbeThreads), 0, stream,
-                       (const char*)buf, nchunks);
+                       (const char*)buf, nchunks, nt);
   return hipGetLastError();
 }
 
@@ -298,12 +301,12 @@ constexpr int kMaxProbeGrid = 65536;
 int launched(hipError_t e) { return e == hipSuccess ? RPA_OK : RPA_E_HIP; }
 }  // namespace
 
-extern "C" int rpa_probe_stream(const void* buf, size_t bytes, int workgroups, int interleave,
+extern "C" int rpa_probe_stream(const void* buf, size_t bytes, int workgroups, int flags,
                                 rpa_stream_t stream) {
-  if (!buf || workgroups < 1 || workgroups > kMaxProbeGrid ||
+  if (!buf || workgroups < 1 || workgroups > kMaxProbeGrid || flags < 0 || flags > 3 ||
       bytes / (size_t)workgroups < (size_t)(32 * 1024))
     return RPA_E_INVALID;
-  return launched(rpa::probe_stream(buf, bytes, workgroups, interleave, stream));
+  return launched(rpa::probe_stream(buf, bytes, workgroups, flags, stream));
 }
 
 extern "C" int rpa_probe_rate(int kind, int workgroups, float* sink, rpa_stream_t stream) {

@@ -1,6 +1,6 @@
 """Practical ceilings of one MI355X, measured with the probes of librpa.so
 (include/rpa_probe.h): HBM read bandwidth through the attention kernels' own
-LDS-DMA scheme, MFMA / LDS / exp issue rates per CU, clocks per step of a
+LDS-DMA scheme (default and non-temporal cache policy), MFMA / LDS / exp issue rates per CU, clocks per step of a
 dependent MFMA chain next to softmax-like VALU and LDS work, and the clocks a
 wave spends issuing 1 KB reads.
 
@@ -61,8 +61,9 @@ def _timed(torch, launch, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def stream(torch, nbytes=4 << 30, wg_per_cu=2, interleave=True, reps=10):
-    """GB/s of a single read of `nbytes` with the LDS-DMA scheme."""
+def stream(torch, nbytes=4 << 30, wg_per_cu=2, interleave=True, nontemporal=False, reps=10):
+    """GB/s of a single read of `nbytes` with the LDS-DMA scheme (loads with the
+    default or the non-temporal cache policy)."""
     lib = _lib()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid = cus * wg_per_cu
@@ -70,11 +71,13 @@ def stream(torch, nbytes=4 << 30, wg_per_cu=2, interleave=True, reps=10):
     st = torch.cuda.current_stream().cuda_stream
     stage = 32 * 1024
     read = (nbytes // stage) // grid * grid * stage
-    ms = _timed(torch, lambda: _check(lib.rpa_probe_stream(buf.data_ptr(), nbytes, grid,
-                                                           int(interleave), st),
+    flags = int(interleave) | (2 if nontemporal else 0)
+    ms = _timed(torch, lambda: _check(lib.rpa_probe_stream(buf.data_ptr(), nbytes, grid, flags,
+                                                           st),
                                       "rpa_probe_stream"), reps)
     del buf
-    return {"probe": "stream_lds_dma", "bytes": read, "workgroups": grid,
+    return {"probe": "stream_lds_dma" + ("_nt" if nontemporal else ""), "bytes": read,
+            "workgroups": grid,
             "chunks": "interleaved" if interleave else "contiguous per workgroup",
             "stages": "2 x 32 KB per workgroup", "ms": round(ms, 4),
             "GB_per_s": round(read / (ms * 1e-3) / 1e9, 1),
@@ -141,7 +144,8 @@ def issue(torch, kind, waves, count=16, src_bytes=64 << 20):
 
 
 def run_all(torch):
-    rows = [stream(torch, wg_per_cu=w, interleave=il) for il in (True, False) for w in (2, 1)]
+    rows = [stream(torch, wg_per_cu=w, interleave=il, nontemporal=nt)
+            for nt in (False, True) for il in (True, False) for w in (2, 1)]
     for kind in (0, 1, 2, 3):
         for w in (1, 2):
             rows.append(rate(torch, kind, w))
