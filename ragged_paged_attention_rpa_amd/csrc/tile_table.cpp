@@ -29,13 +29,13 @@ struct TileRow {
 // `python -m ragged_paged_attention_rpa_amd.tune` (candidates interleaved call
 // by call, medians of 30 calls; run-to-run noise about 3%):
 //   decode 128 x 512..8192 keys, 32/8 heads: bf16 pool 1024 keys per split
-//     (0.440 ms; 512: 0.446, 2048: 0.446, 256: 0.465); fp8 pool 2048 (0.255 ms;
-//     1024: 0.258, 512: 0.288);
-//   decode 8 x 16k..32k, fp8: 2048 (0.104 ms; others 0.110..0.115);
-//   decode 256 x 128..2048, bf16: 1024 (0.238 ms; 256: 0.270);
+//     (0.406 ms; 512: 0.427, 2048: 0.409, 256: 0.464); fp8 pool 2048 (0.230 ms;
+//     1024: 0.236, 512: 0.272);
+//   decode 8 x 16k..32k, fp8: 2048 (0.106 ms; others 0.108..0.111);
+//   decode 256 x 128..2048, bf16: 1024 (0.222 ms; 256: 0.268);
 //   decode 32 x 2k..16k at 8/1 heads and 16 x 16k..64k at 16/2 heads (fp8):
 //     every split from 256 to 2048 within noise of the row's value, 4096 up to
-//     60% slower at one kv head;
+//     80% slower at one kv head;
 //   MLA shares: 128 keys on 8 x 1..4k (0.104 ms; 64: 0.111, 512: 0.117),
 //     2 x 2048 (0.064 ms; 64: 0.074, 1024: 0.114) and 4 x 512 with 4 query
 //     tokens each (64 and 128 equal); no effect on 64 x 4k..32k, where the
