@@ -38,9 +38,11 @@ extern "C" {
  * 32 KiB of `buf` once. flags bit 0 set: workgroup b reads chunks b,
  * b + workgroups, b + 2 workgroups, ...; clear: workgroup b reads its own
  * contiguous run of chunks. flags bit 1: the loads carry the non-temporal
- * cache policy (nt). Nothing is written to global memory. workgroups in
- * [1, 65536]; flags in [0, 3]; `bytes` must hold at least one chunk per
- * workgroup. Time the launch with events to get bytes per second.
+ * cache policy (nt). flags bit 2: plain loads into registers (one 8 KiB
+ * chunk share in flight per wave) instead of LDS-DMA. Nothing is written to
+ * global memory. workgroups in [1, 65536]; flags in [0, 7]; `bytes` must hold
+ * at least one chunk per workgroup. Time the launch with events to get bytes
+ * per second.
  */
 int rpa_probe_stream(const void* buf, size_t bytes, int workgroups, int flags,
                      rpa_stream_t stream);

@@ -22,16 +22,38 @@ constexpr int kStreamStage = 32 * 1024;  // bytes per stage: 8 DMA instructions 
 // keeping two stages in flight per wave, and computes nothing. Workgroup b
 // takes chunks b, b + grid, b + 2 grid, ... (INTERLEAVE) or its own
 // contiguous run of nchunks / grid chunks. nt: loads with the non-temporal
-// cache policy.
-template <bool INTERLEAVE>
+// cache policy. REGS: plain global_load_dwordx4 into registers instead of
+// LDS-DMA (one chunk in flight per wave, folded by XOR and kept live).
+template <bool INTERLEAVE, bool REGS, bool REGS_NT>
 __global__ void __launch_bounds__(kProbeThreads) probe_stream_kernel(const char* buf,
                                                                      int64_t nchunks, int nt) {
-  __shared__ __attribute__((aligned(1024))) char stage[2][kStreamStage];
+  __shared__ __attribute__((aligned(1024))) char stage[REGS ? 1 : 2][kStreamStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t per_wg = nchunks / gridDim.x;
   const int64_t first = INTERLEAVE ? blockIdx.x : blockIdx.x * per_wg;
   const int64_t step = INTERLEAVE ? gridDim.x : 1;
+  if constexpr (REGS) {
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t i = 0; i < per_wg; ++i) {
+      const char* src = buf + (first + i * step) * kStreamStage + wave * 8192 + lane * 16;
+      u32x4 r[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(src + k * 1024);
+        // (A compile-time choice: a run-time one lets the compiler merge the
+        // two loads and drop the hint.)
+        if constexpr (REGS_NT)
+          r[k] = __builtin_nontemporal_load(p);
+        else
+          r[k] = *p;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc ^= r[k];
+    }
+    asm volatile("" : : "v"(acc));
+    return;
+  }
   for (int64_t i = 0; i < per_wg; ++i) {
     const uint32_t dst = lds_addr(stage[i & 1]) + (uint32_t)wave * 8192;
     const char* src = buf + (first + i * step) * kStreamStage + wave * 8192 + lane * 16;
@@ -244,16 +266,29 @@ hipError_t probe_stream(const void* buf, size_t bytes, int grid, int flags,
                         hipStream_t stream) {
   const bool interleave = flags & 1;
   const int nt = (flags >> 1) & 1;
+  const bool regs = flags & 4;
   // Chunks read: per_wg = floor(bytes / 32 KB / grid) per workgroup, so every
   // chunk index, interleaved or contiguous, is below per_wg * grid.
   const int64_t nchunks = (int64_t)(bytes / kStreamStage) / grid * grid;
   if (nchunks <= 0) return hipErrorInvalidValue;
-  if (interleave)
-    hipLaunchKernelGGL(probe_stream_kernel<true>, dim3(grid), dim3(kProbeThreads), 0, stream,
-                       (const char*)buf, nchunks, nt);
-  else
-    hipLaunchKernelGGL(probe_stream_kernel<false>, dim3(grid), dim3(kProbeThreads), 0, stream,
-                       (const char*)buf, nchunks, nt);
+#define RPA_PROBE_STREAM(IL, RG, RNT)                                                   \
+  hipLaunchKernelGGL((probe_stream_kernel<IL, RG, RNT>), dim3(grid), dim3(kProbeThreads), 0, \
+                     stream, (const char*)buf, nchunks, nt)
+  if (regs) {
+    if (interleave && nt)
+      RPA_PROBE_STREAM(true, true, true);
+    else if (interleave)
+      RPA_PROBE_STREAM(true, true, false);
+    else if (nt)
+      RPA_PROBE_STREAM(false, true, true);
+    else
+      RPA_PROBE_STREAM(false, true, false);
+  } else if (interleave) {
+    RPA_PROBE_STREAM(true, false, false);
+  } else {
+    RPA_PROBE_STREAM(false, false, false);
+  }
+#undef RPA_PROBE_STREAM
   return hipGetLastError();
 }
 
@@ -303,7 +338,7 @@ int launched(hipError_t e) { return e == hipSuccess ? RPA_OK : RPA_E_HIP; }
 
 extern "C" int rpa_probe_stream(const void* buf, size_t bytes, int workgroups, int flags,
                                 rpa_stream_t stream) {
-  if (!buf || workgroups < 1 || workgroups > kMaxProbeGrid || flags < 0 || flags > 3 ||
+  if (!buf || workgroups < 1 || workgroups > kMaxProbeGrid || flags < 0 || flags > 7 ||
       bytes / (size_t)workgroups < (size_t)(32 * 1024))
     return RPA_E_INVALID;
   return launched(rpa::probe_stream(buf, bytes, workgroups, flags, stream));

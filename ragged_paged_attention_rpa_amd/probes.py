@@ -61,9 +61,11 @@ def _timed(torch, launch, reps):
     return e0.elapsed_time(e1) / reps
 
 
-def stream(torch, nbytes=4 << 30, wg_per_cu=2, interleave=True, nontemporal=False, reps=10):
-    """GB/s of a single read of `nbytes` with the LDS-DMA scheme (loads with the
-    default or the non-temporal cache policy)."""
+def stream(torch, nbytes=4 << 30, wg_per_cu=2, interleave=True, nontemporal=False, regs=False,
+           reps=10):
+    """GB/s of a single read of `nbytes` with the LDS-DMA scheme, or with plain
+    loads into registers (regs), with the default or the non-temporal cache
+    policy."""
     lib = _lib()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     grid = cus * wg_per_cu
@@ -71,15 +73,16 @@ def stream(torch, nbytes=4 << 30, wg_per_cu=2, interleave=True, nontemporal=Fals
     st = torch.cuda.current_stream().cuda_stream
     stage = 32 * 1024
     read = (nbytes // stage) // grid * grid * stage
-    flags = int(interleave) | (2 if nontemporal else 0)
+    flags = int(interleave) | (2 if nontemporal else 0) | (4 if regs else 0)
     ms = _timed(torch, lambda: _check(lib.rpa_probe_stream(buf.data_ptr(), nbytes, grid, flags,
                                                            st),
                                       "rpa_probe_stream"), reps)
     del buf
-    return {"probe": "stream_lds_dma" + ("_nt" if nontemporal else ""), "bytes": read,
-            "workgroups": grid,
+    return {"probe": ("stream_regs" if regs else "stream_lds_dma") + ("_nt" if nontemporal else ""),
+            "bytes": read, "workgroups": grid,
             "chunks": "interleaved" if interleave else "contiguous per workgroup",
-            "stages": "2 x 32 KB per workgroup", "ms": round(ms, 4),
+            "stages": "8 KB per wave in registers" if regs else "2 x 32 KB per workgroup",
+            "ms": round(ms, 4),
             "GB_per_s": round(read / (ms * 1e-3) / 1e9, 1),
             "frac_of_8TBps": round(read / (ms * 1e-3) / 8e12, 3)}
 
@@ -146,6 +149,8 @@ def issue(torch, kind, waves, count=16, src_bytes=64 << 20):
 def run_all(torch):
     rows = [stream(torch, wg_per_cu=w, interleave=il, nontemporal=nt)
             for nt in (False, True) for il in (True, False) for w in (2, 1)]
+    rows += [stream(torch, wg_per_cu=w, regs=True, nontemporal=nt)
+             for nt in (False, True) for w in (2, 1)]
     for kind in (0, 1, 2, 3):
         for w in (1, 2):
             rows.append(rate(torch, kind, w))

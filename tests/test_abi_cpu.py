@@ -57,7 +57,7 @@ def test_probes_reject_invalid_arguments(lib):
     assert lib.rpa_probe_stream(fake, 1 << 30, 0, 1, st) == RPA_E_INVALID
     assert lib.rpa_probe_stream(fake, 1 << 30, 65537, 0, st) == RPA_E_INVALID
     assert lib.rpa_probe_stream(fake, 32 * 1024 * 256 - 1, 256, 1, st) == RPA_E_INVALID
-    assert lib.rpa_probe_stream(fake, 1 << 30, 256, 4, st) == RPA_E_INVALID
+    assert lib.rpa_probe_stream(fake, 1 << 30, 256, 8, st) == RPA_E_INVALID
     assert lib.rpa_probe_stream(fake, 1 << 30, 256, -1, st) == RPA_E_INVALID
     assert lib.rpa_probe_rate(4, 256, fake, st) == RPA_E_INVALID
     assert lib.rpa_probe_rate(-1, 256, fake, st) == RPA_E_INVALID
