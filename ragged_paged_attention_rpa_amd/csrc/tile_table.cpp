@@ -36,10 +36,11 @@ struct TileRow {
 //   decode 32 x 2k..16k at 8/1 heads and 16 x 16k..64k at 16/2 heads (fp8):
 //     every split from 256 to 2048 within noise of the row's value, 4096 up to
 //     80% slower at one kv head;
-//   MLA shares: 128 keys on 8 x 1..4k (0.104 ms; 64: 0.111, 512: 0.117),
-//     2 x 2048 (0.064 ms; 64: 0.074, 1024: 0.114) and 4 x 512 with 4 query
-//     tokens each (64 and 128 equal); no effect on 64 x 4k..32k, where the
-//     equal shares are larger than any candidate.
+//   MLA shares: 128 keys on 8 x 1..4k (0.110 ms; 64: 0.118, 512: 0.117),
+//     2 x 2048 (0.063 ms; 64: 0.075, 1024: 0.104) and 4 x 512 with 4 query
+//     tokens each (0.077 ms; 64: 0.079, 256: 0.080); no effect on
+//     64 x 4k..32k (0.426..0.430 ms for every candidate), where the equal
+//     shares are larger than any candidate.
 constexpr TileRow kRows[] = {
     {kTileGqaDecode, DT_FP8, 128, 1 << 30, 0, 2048},
     {kTileGqaDecode, DT_BF16, 128, 1 << 30, 0, 1024},
