@@ -134,6 +134,9 @@ __device__ __forceinline__ CapSeries cap_series(float cap, float scale) {
   r.a2 = r.a0 * c2 * c2 * (2.f / 15.f);
   r.smax = ymax / fabsf(c);
   r.smax3 = ymax3 / fabsf(c);
+  // A cap so small that a coefficient overflows (below about 1e-11 at unit
+  // scale) would give 0 * inf for a zero score: such calls keep the exact form.
+  if (!(__builtin_isfinite(r.a1) && __builtin_isfinite(r.a2))) r.smax = r.smax3 = -1.f;
   return r;
 }
 

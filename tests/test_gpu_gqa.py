@@ -663,6 +663,27 @@ def test_fp8_scores_over_fp8_pool(variant):
     _check(c, got, want, "fp8")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_tiny_cap_with_zero_queries(kv):
+    """A soft cap of 1e-25 (the series coefficients overflow fp32, so 0 * inf
+    would follow for a zero score; the exact form must serve) over a batch
+    where one decode and one prefill chunk have all-zero queries (every score
+    exactly 0): uniform weights, no NaN."""
+    _say(f"tiny cap, zero queries ({kv})")
+    kvd = torch.bfloat16 if kv == "bf16" else torch.float8_e4m3fn
+    ks = None if kv == "bf16" else 0.5
+    c = wl.make_gqa([(1, 700), (1, 300), (300, 900), (200, 400), (1, 33)], num_q_heads=32,
+                    num_kv_heads=8, head_dim=128, page_size=16, q_dtype=torch.bfloat16,
+                    kv_dtype=kvd, seed=620, device="cuda", soft_cap=1e-25, k_scale=ks,
+                    v_scale=ks, name=f"tinycap-{kv}")
+    cu = c.cu_q_lens
+    for i in (1, 3):
+        c.q[int(cu[i]):int(cu[i + 1])].zero_()
+    got = _run_gpu(c)
+    assert torch.isfinite(got[: int(cu[-1])].float()).all()
+    _check(c, got, _run_oracle(c), "fp8" if kv == "fp8" else "bf16")
+
+
 FUSED_CASES = {
     # (seqs, Hq, Hkv, D, page size, pool dtype, window, cap, kernel path)
     "bf16-prefill-kernel": ([(1, 3000), (300, 1200), (1, 17), (64, 64), (1, 9000), (700, 2100)],
